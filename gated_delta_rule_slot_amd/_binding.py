@@ -1,0 +1,225 @@
+"""ctypes binding of libgdnslot.so (include/gdn_slot.h), argument marshalling only.
+
+Each function carries the C entry point's name and takes torch tensors that
+live on the current HIP device.  Nothing here computes: every step runs in the
+library's kernels.  PyTorch provides the device memory and the stream.  If the
+shared library is missing, importing this module raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdnslot.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+ALPHA_PER_HEAD, ALPHA_PER_CHANNEL = 0, 1
+L2NORM_K, L2NORM_Q, CONV_SILU = 1, 2, 4
+ERRW_BAD_SLOT, ERRW_BAD_TRACK_SLOT, ERRW_BAD_SEQLENS = 1, 2, 4
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"gdn status {status}: {message}")
+        self.status = status
+
+
+class PoolDesc(ct.Structure):
+    _fields_ = [
+        ("layers", ct.c_int32), ("slots", ct.c_int32), ("heads", ct.c_int32),
+        ("head_k", ct.c_int32), ("head_v", ct.c_int32), ("conv_kernel", ct.c_int32),
+        ("ssm_dtype", ct.c_int32), ("conv_dtype", ct.c_int32),
+        ("ssm_base", ct.c_void_p), ("conv_base", ct.c_void_p), ("err_word", ct.c_void_p),
+    ]
+
+
+class RestoreOp(ct.Structure):
+    _fields_ = [("linear_state_id", ct.c_int32), ("restore_requested", ct.c_int32),
+                ("restore_src_slot_id", ct.c_int32)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run gated_delta_rule_slot_amd/build.py")
+
+_lib = ct.CDLL(LIB_PATH)
+_vp, _i32, _u32, _f32, _sz = ct.c_void_p, ct.c_int32, ct.c_uint32, ct.c_float, ct.c_size_t
+_lib.state_pool_bytes.argtypes = [ct.POINTER(PoolDesc), ct.POINTER(_sz), ct.POINTER(_sz)]
+_lib.state_pool_create.argtypes = [ct.POINTER(PoolDesc), ct.POINTER(_vp)]
+_lib.state_pool_destroy.argtypes = [_vp]
+_lib.state_pool_destroy.restype = None
+_lib.gdn_last_error.restype = ct.c_char_p
+_lib.conv_gdn_prefill_chunked.argtypes = [
+    _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _u32,
+    _vp, _i32, _vp, _vp, _vp, _sz, _vp]
+_lib.gdn_prefill_workspace_bytes.argtypes = [_vp, _i32, _i32, ct.POINTER(_sz)]
+_lib.gdn_decode_step.argtypes = [
+    _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _u32, _vp, _vp, _i32, _vp, _vp, _vp]
+_lib.track_snapshot.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _vp]
+_lib.restore_slots.argtypes = [_vp, _i32, ct.POINTER(RestoreOp), ct.POINTER(ct.c_int64), _vp]
+for _f in ("state_pool_bytes", "state_pool_create", "conv_gdn_prefill_chunked",
+           "gdn_prefill_workspace_bytes", "gdn_decode_step", "track_snapshot", "restore_slots"):
+    getattr(_lib, _f).restype = ct.c_int
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise GdnError(status, _lib.gdn_last_error().decode(errors="replace"))
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _need(t, dtype, numel=None, name="tensor"):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def last_error() -> str:
+    return _lib.gdn_last_error().decode(errors="replace")
+
+
+def state_pool_bytes(layers, slots, heads, head_k, head_v, ssm_dtype):
+    d = PoolDesc(layers, slots, heads, head_k, head_v, 4, ssm_dtype, GDN_BF16, None, None, None)
+    s, c = _sz(), _sz()
+    _check(_lib.state_pool_bytes(ct.byref(d), ct.byref(s), ct.byref(c)))
+    return s.value, c.value
+
+
+class StatePool:
+    """Handle over caller-owned pool tensors (see state_pool_create)."""
+
+    def __init__(self, handle, ssm, conv, err_word, shape):
+        self.handle = handle
+        self.ssm, self.conv, self.err_word = ssm, conv, err_word
+        self.layers, self.slots, self.heads, self.head_k, self.head_v = shape
+
+    @property
+    def channels(self):
+        return self.heads * (2 * self.head_k + self.head_v)
+
+    def destroy(self):
+        if self.handle:
+            _lib.state_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def state_pool_create(ssm: torch.Tensor, conv: torch.Tensor, err_word: torch.Tensor | None = None):
+    """Wrap ``ssm`` [L,N,H,V,K] (float32|bfloat16) and ``conv`` [L,N,3,C] (bfloat16)."""
+    if ssm.dim() != 5 or conv.dim() != 4:
+        raise ValueError("ssm must be [L,N,H,V,K] and conv [L,N,3,C]")
+    L, N, H, V, K = ssm.shape
+    if ssm.dtype == torch.float32:
+        sd = GDN_F32
+    elif ssm.dtype == torch.bfloat16:
+        sd = GDN_BF16
+    else:
+        raise TypeError("ssm must be float32 or bfloat16")
+    if conv.dtype != torch.bfloat16 or tuple(conv.shape) != (L, N, 3, H * (2 * K + V)):
+        raise ValueError("conv must be bfloat16 [L, N, 3, H*(2K+V)]")
+    if err_word is not None:
+        _need(err_word, torch.int32, 1, "err_word")
+    d = PoolDesc(L, N, H, K, V, 4, sd, GDN_BF16, _ptr(ssm), _ptr(conv), _ptr(err_word))
+    h = _vp()
+    _check(_lib.state_pool_create(ct.byref(d), ct.byref(h)))
+    return StatePool(h, ssm, conv, err_word, (L, N, H, K, V))
+
+
+def gdn_prefill_workspace_bytes(pool: StatePool, batch: int, max_seqlen: int) -> int:
+    n = _sz()
+    _check(_lib.gdn_prefill_workspace_bytes(pool.handle, batch, max_seqlen, ct.byref(n)))
+    return n.value
+
+
+def conv_gdn_prefill_chunked(pool: StatePool, layer, cu_seqlens, slot_table, has_initial_state,
+                             x, conv_w, alpha, alpha_mode, beta, out, max_seqlen,
+                             start_len=None, scale=1.0, flags=L2NORM_K, snap_interval=0,
+                             track_slots=None, next_track_idx=None, workspace=None,
+                             stream=None):
+    B = slot_table.numel()
+    T = x.shape[0] if x is not None else 0
+    H, V, K = pool.heads, pool.head_v, pool.head_k
+    _need(cu_seqlens, torch.int32, B + 1, "cu_seqlens")
+    _need(slot_table, torch.int32, B, "slot_table")
+    _need(has_initial_state, torch.int32, B, "has_initial_state")
+    _need(start_len, torch.int32, B, "start_len")
+    _need(x, torch.bfloat16, T * pool.channels, "x")
+    _need(conv_w, torch.bfloat16, pool.channels * 4, "conv_w")
+    _need(alpha, torch.float32, T * H * (K if alpha_mode == ALPHA_PER_CHANNEL else 1), "alpha")
+    _need(beta, torch.float32, T * H, "beta")
+    _need(out, torch.bfloat16, T * H * V, "out")
+    _need(track_slots, torch.int32, 2 * B, "track_slots")
+    _need(next_track_idx, torch.int32, B, "next_track_idx")
+    if workspace is not None:
+        _need(workspace, torch.uint8, None, "workspace")
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(_lib.conv_gdn_prefill_chunked(
+        pool.handle, layer, B, T, int(max_seqlen), _ptr(cu_seqlens), _ptr(slot_table),
+        _ptr(has_initial_state), _ptr(start_len), _ptr(x), _ptr(conv_w), _ptr(alpha), alpha_mode,
+        _ptr(beta), float(scale), flags, _ptr(out), snap_interval, _ptr(track_slots),
+        _ptr(next_track_idx), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def gdn_decode_step(pool: StatePool, layer, slot_table, x, conv_w, alpha, alpha_mode, beta, out,
+                    scale=1.0, flags=L2NORM_K, seq_len_after=None, track_interval=0,
+                    track_slots=None, next_track_idx=None, stream=None):
+    B = slot_table.numel()
+    H, V, K = pool.heads, pool.head_v, pool.head_k
+    _need(slot_table, torch.int32, B, "slot_table")
+    _need(x, torch.bfloat16, B * pool.channels, "x")
+    _need(conv_w, torch.bfloat16, pool.channels * 4, "conv_w")
+    _need(alpha, torch.float32, B * H * (K if alpha_mode == ALPHA_PER_CHANNEL else 1), "alpha")
+    _need(beta, torch.float32, B * H, "beta")
+    _need(out, torch.bfloat16, B * H * V, "out")
+    _need(seq_len_after, torch.int32, B, "seq_len_after")
+    _need(track_slots, torch.int32, 2 * B, "track_slots")
+    _need(next_track_idx, torch.int32, B, "next_track_idx")
+    _check(_lib.gdn_decode_step(
+        pool.handle, layer, B, _ptr(slot_table), _ptr(x), _ptr(conv_w), _ptr(alpha), alpha_mode,
+        _ptr(beta), float(scale), flags, _ptr(out), _ptr(seq_len_after), track_interval,
+        _ptr(track_slots), _ptr(next_track_idx), _stream(stream)))
+
+
+def track_snapshot(pool: StatePool, layer_begin, layer_end, src_slots, dst_slots, stream=None):
+    n = src_slots.numel()
+    _need(src_slots, torch.int32, n, "src_slots")
+    _need(dst_slots, torch.int32, n, "dst_slots")
+    _check(_lib.track_snapshot(pool.handle, layer_begin, layer_end, n, _ptr(src_slots),
+                               _ptr(dst_slots), _stream(stream)))
+
+
+def restore_slots(pool: StatePool, ops, has_initial_state, stream=None):
+    """``ops``: sequence of (linear_state_id, restore_requested, restore_src_slot_id);
+    ``has_initial_state``: host int64 tensor or list, updated and returned as a list."""
+    n = len(ops)
+    arr = (RestoreOp * max(n, 1))(*[RestoreOp(*map(int, o)) for o in ops])
+    hi = (ct.c_int64 * max(n, 1))(*[int(v) for v in has_initial_state])
+    _check(_lib.restore_slots(pool.handle, n, arr, hi, _stream(stream)))
+    return [hi[i] for i in range(n)]

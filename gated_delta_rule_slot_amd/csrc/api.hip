@@ -1,0 +1,243 @@
+// api.hip -- the C ABI declared in include/gdn_slot.h: host-side validation,
+// error strings, and dispatch to the kernels.  No device memory is allocated
+// here; every buffer belongs to the caller.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <new>
+
+#include "common.hpp"
+
+#define GDN_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdn_status fail(gdn_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+gdn_status ok() {
+  g_err[0] = '\0';
+  return GDN_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+gdn_status check_shape(const gdn_pool_desc *d) {
+  if (!d) return fail(GDN_ERR_ARG, "descriptor is NULL");
+  if (d->layers <= 0 || d->slots < 2 || d->heads <= 0)
+    return fail(GDN_ERR_ARG, "need layers >= 1, slots >= 2 (slot 0 is reserved), heads >= 1");
+  if (d->conv_kernel != 4) return fail(GDN_ERR_UNSUPPORTED, "conv_kernel must be 4");
+  if (d->ssm_dtype != GDN_F32 && d->ssm_dtype != GDN_BF16)
+    return fail(GDN_ERR_ARG, "ssm_dtype must be GDN_F32 or GDN_BF16");
+  if (d->conv_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "conv_dtype must be GDN_BF16");
+  if (d->head_k != d->head_v)
+    return fail(GDN_ERR_UNSUPPORTED, "head_k must equal head_v (got %d, %d)", d->head_k, d->head_v);
+  if (d->head_k != 16 && d->head_k != 32 && d->head_k != 64 && d->head_k != 128)
+    return fail(GDN_ERR_UNSUPPORTED, "head dim %d not in {16, 32, 64, 128}", d->head_k);
+  if (d->heads > 65535) return fail(GDN_ERR_UNSUPPORTED, "heads > 65535");
+  return GDN_OK;
+}
+
+void sizes(const gdn_pool_desc *d, int64_t *C, int64_t *ssm_block, int64_t *conv_block) {
+  *C = int64_t(d->heads) * (2 * d->head_k + d->head_v);
+  *ssm_block = int64_t(d->heads) * d->head_v * d->head_k * (d->ssm_dtype == GDN_F32 ? 4 : 2);
+  *conv_block = int64_t(gdn::kConvRows) * (*C) * 2;
+}
+
+gdn_status check_pool(gdn_pool_t p, int layer) {
+  if (!p) return fail(GDN_ERR_ARG, "pool handle is NULL");
+  if (layer < 0 || layer >= p->d.layers)
+    return fail(GDN_ERR_RANGE, "layer %d outside [0, %d)", layer, p->d.layers);
+  return GDN_OK;
+}
+
+gdn_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+GDN_API gdn_status state_pool_bytes(const gdn_pool_desc *desc, size_t *ssm_bytes,
+                                    size_t *conv_bytes) {
+  gdn_status s = check_shape(desc);
+  if (s != GDN_OK) return s;
+  int64_t C, sb, cb;
+  sizes(desc, &C, &sb, &cb);
+  if (ssm_bytes) *ssm_bytes = size_t(sb) * desc->layers * desc->slots;
+  if (conv_bytes) *conv_bytes = size_t(cb) * desc->layers * desc->slots;
+  return ok();
+}
+
+GDN_API gdn_status state_pool_create(const gdn_pool_desc *desc, gdn_pool_t *out) {
+  if (!out) return fail(GDN_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  gdn_status s = check_shape(desc);
+  if (s != GDN_OK) return s;
+  if (!desc->ssm_base || !desc->conv_base) return fail(GDN_ERR_ARG, "pool base pointer is NULL");
+  if (!aligned(desc->ssm_base, 16) || !aligned(desc->conv_base, 16))
+    return fail(GDN_ERR_UNSUPPORTED, "pool base pointers must be 16-byte aligned");
+  if (desc->err_word && !aligned(desc->err_word, 4))
+    return fail(GDN_ERR_ARG, "err_word must be 4-byte aligned");
+  gdn_pool *p = new (std::nothrow) gdn_pool;
+  if (!p) return fail(GDN_ERR_ARG, "out of host memory");
+  p->d = *desc;
+  sizes(desc, &p->C, &p->ssm_block_bytes, &p->conv_block_bytes);
+  if ((p->ssm_block_bytes % 16) || (p->conv_block_bytes % 16)) {
+    delete p;
+    return fail(GDN_ERR_UNSUPPORTED, "state blocks must be multiples of 16 bytes");
+  }
+  *out = p;
+  return ok();
+}
+
+GDN_API void state_pool_destroy(gdn_pool_t pool) { delete pool; }
+
+GDN_API const char *gdn_last_error(void) { return g_err; }
+
+GDN_API gdn_status gdn_prefill_workspace_bytes(gdn_pool_t pool, int32_t batch,
+                                               int32_t max_seqlen, size_t *bytes) {
+  if (!pool || !bytes) return fail(GDN_ERR_ARG, "pool or bytes is NULL");
+  if (batch < 0 || max_seqlen < 0) return fail(GDN_ERR_RANGE, "batch or max_seqlen < 0");
+  const size_t chunks = (size_t(max_seqlen) + gdn::kChunk - 1) / gdn::kChunk;
+  *bytes = (chunks ? chunks : 1) * size_t(batch) * pool->d.heads * gdn::prefill_record_bytes(pool) +
+           gdn::prefill_carry_bytes(pool, batch);
+  return ok();
+}
+
+GDN_API gdn_status conv_gdn_prefill_chunked(
+    gdn_pool_t pool, int32_t layer, int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    const int32_t *cu_seqlens, const int32_t *slot_table, const int32_t *has_initial_state,
+    const int32_t *start_len, const uint16_t *x, const uint16_t *conv_w, const float *alpha,
+    int32_t alpha_mode, const float *beta, float scale, uint32_t flags, uint16_t *out,
+    int32_t snap_interval, const int32_t *track_slots, const int32_t *next_track_idx,
+    void *workspace, size_t workspace_bytes, void *stream) {
+  gdn_status s = check_pool(pool, layer);
+  if (s != GDN_OK) return s;
+  if (batch < 0 || batch > 65535) return fail(GDN_ERR_RANGE, "batch %d outside [0, 65535]", batch);
+  if (total_tokens < 0 || max_seqlen < 0) return fail(GDN_ERR_RANGE, "negative token count");
+  if (batch == 0) return ok();
+  if (!cu_seqlens || !slot_table || !has_initial_state || !conv_w || !alpha || !beta)
+    return fail(GDN_ERR_ARG, "a required pointer is NULL");
+  if (total_tokens > 0 && (!x || !out)) return fail(GDN_ERR_ARG, "x or out is NULL");
+  if (alpha_mode != GDN_ALPHA_PER_HEAD && alpha_mode != GDN_ALPHA_PER_CHANNEL)
+    return fail(GDN_ERR_ARG, "alpha_mode %d unknown", alpha_mode);
+  if (flags & ~uint32_t(GDN_F_L2NORM_K | GDN_F_L2NORM_Q | GDN_F_CONV_SILU))
+    return fail(GDN_ERR_ARG, "unknown flag bits 0x%x", flags);
+  if (snap_interval < 0 || (snap_interval % gdn::kChunk) != 0)
+    return fail(GDN_ERR_ARG, "snap_interval %d must be 0 or a positive multiple of 64",
+                snap_interval);
+  if (snap_interval > 0 && (!track_slots || !next_track_idx || !start_len))
+    return fail(GDN_ERR_ARG, "snapshots need track_slots, next_track_idx and start_len");
+  if (!aligned(conv_w, 8)) return fail(GDN_ERR_UNSUPPORTED, "conv_w must be 8-byte aligned");
+  if (x && !aligned(x, 16)) return fail(GDN_ERR_UNSUPPORTED, "x must be 16-byte aligned");
+  if (out && !aligned(out, 16)) return fail(GDN_ERR_UNSUPPORTED, "out must be 16-byte aligned");
+  if (!aligned(alpha, 16)) return fail(GDN_ERR_UNSUPPORTED, "alpha must be 16-byte aligned");
+  const size_t need_min = size_t(batch) * pool->d.heads * gdn::prefill_record_bytes(pool) +
+                          gdn::prefill_carry_bytes(pool, batch);
+  if (!workspace || workspace_bytes < need_min)
+    return fail(GDN_ERR_ARG, "workspace of %zu bytes is below the minimum %zu", workspace_bytes,
+                need_min);
+  if (!aligned(workspace, 256)) return fail(GDN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  gdn::PrefillArgs a{layer,       batch,          total_tokens,  max_seqlen, cu_seqlens,
+                     slot_table,  has_initial_state, start_len, x,          conv_w,
+                     alpha,       alpha_mode,     beta,          scale,      flags,
+                     out,         snap_interval,  track_slots,   next_track_idx,
+                     workspace,   workspace_bytes};
+  return launched(gdn::launch_prefill(pool, a, static_cast<hipStream_t>(stream)),
+                  "conv_gdn_prefill_chunked launch");
+}
+
+GDN_API gdn_status gdn_decode_step(gdn_pool_t pool, int32_t layer, int32_t batch,
+                                   const int32_t *slot_table, const uint16_t *x,
+                                   const uint16_t *conv_w, const float *alpha, int32_t alpha_mode,
+                                   const float *beta, float scale, uint32_t flags, uint16_t *out,
+                                   const int32_t *seq_len_after, int32_t track_interval,
+                                   const int32_t *track_slots, const int32_t *next_track_idx,
+                                   void *stream) {
+  gdn_status s = check_pool(pool, layer);
+  if (s != GDN_OK) return s;
+  if (batch < 0 || batch > 65535) return fail(GDN_ERR_RANGE, "batch %d outside [0, 65535]", batch);
+  if (batch == 0) return ok();
+  if (!slot_table || !x || !conv_w || !alpha || !beta || !out)
+    return fail(GDN_ERR_ARG, "a required pointer is NULL");
+  if (alpha_mode != GDN_ALPHA_PER_HEAD && alpha_mode != GDN_ALPHA_PER_CHANNEL)
+    return fail(GDN_ERR_ARG, "alpha_mode %d unknown", alpha_mode);
+  if (flags & ~uint32_t(GDN_F_L2NORM_K | GDN_F_L2NORM_Q | GDN_F_CONV_SILU))
+    return fail(GDN_ERR_ARG, "unknown flag bits 0x%x", flags);
+  if (track_interval < 0) return fail(GDN_ERR_ARG, "track_interval < 0");
+  if (track_interval > 0 && (!seq_len_after || !track_slots || !next_track_idx))
+    return fail(GDN_ERR_ARG, "tracking needs seq_len_after, track_slots and next_track_idx");
+  if (!aligned(conv_w, 8)) return fail(GDN_ERR_UNSUPPORTED, "conv_w must be 8-byte aligned");
+  if (!aligned(alpha, 16)) return fail(GDN_ERR_UNSUPPORTED, "alpha must be 16-byte aligned");
+  gdn::DecodeArgs a{layer,       batch,         slot_table,     x,           conv_w,
+                    alpha,       alpha_mode,    beta,           scale,       flags,
+                    out,         seq_len_after, track_interval, track_slots, next_track_idx};
+  return launched(gdn::launch_decode(pool, a, static_cast<hipStream_t>(stream)),
+                  "gdn_decode_step launch");
+}
+
+GDN_API gdn_status track_snapshot(gdn_pool_t pool, int32_t layer_begin, int32_t layer_end,
+                                  int32_t n, const int32_t *src_slots, const int32_t *dst_slots,
+                                  void *stream) {
+  if (!pool) return fail(GDN_ERR_ARG, "pool handle is NULL");
+  if (layer_begin < 0 || layer_end > pool->d.layers || layer_begin > layer_end)
+    return fail(GDN_ERR_RANGE, "layer range [%d, %d) outside [0, %d)", layer_begin, layer_end,
+                pool->d.layers);
+  if (n < 0) return fail(GDN_ERR_RANGE, "n < 0");
+  if (n == 0 || layer_begin == layer_end) return ok();
+  if (!src_slots || !dst_slots) return fail(GDN_ERR_ARG, "slot arrays are NULL");
+  return launched(gdn::launch_copy_device_pairs(pool, layer_begin, layer_end, n, src_slots,
+                                                dst_slots, static_cast<hipStream_t>(stream)),
+                  "track_snapshot launch");
+}
+
+GDN_API gdn_status restore_slots(gdn_pool_t pool, int32_t n_ops, const gdn_restore_op *ops,
+                                 int64_t *has_initial_state, void *stream) {
+  if (!pool) return fail(GDN_ERR_ARG, "pool handle is NULL");
+  if (n_ops < 0) return fail(GDN_ERR_RANGE, "n_ops < 0");
+  if (n_ops == 0) return ok();
+  if (!ops || !has_initial_state) return fail(GDN_ERR_ARG, "ops or has_initial_state is NULL");
+  int32_t *src = new (std::nothrow) int32_t[n_ops];
+  int32_t *dst = new (std::nothrow) int32_t[n_ops];
+  if (!src || !dst) {
+    delete[] src;
+    delete[] dst;
+    return fail(GDN_ERR_ARG, "out of host memory");
+  }
+  int n = 0;
+  const int slots = pool->d.slots;
+  for (int i = 0; i < n_ops; ++i) {
+    const gdn_restore_op &op = ops[i];
+    if (!op.restore_requested) continue;
+    const int s = op.restore_src_slot_id, d = op.linear_state_id;
+    if (s < 1 || s >= slots || d < 1 || d >= slots) {
+      has_initial_state[i] = 0;  // COLD_START
+      continue;
+    }
+    if (s != d) {
+      src[n] = s;
+      dst[n] = d;
+      ++n;
+    }
+    has_initial_state[i] = 1;  // RESTORED
+  }
+  hipError_t e = n ? gdn::launch_copy_host_pairs(pool, n, src, dst,
+                                                 static_cast<hipStream_t>(stream))
+                   : hipSuccess;
+  delete[] src;
+  delete[] dst;
+  if (e != hipSuccess) {
+    for (int i = 0; i < n_ops; ++i)
+      if (ops[i].restore_requested) has_initial_state[i] = 0;
+    return fail(GDN_ERR_HIP, "restore_slots launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}

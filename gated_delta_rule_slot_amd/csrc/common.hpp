@@ -1,0 +1,88 @@
+// common.hpp -- internal declarations shared by the library's translation units.
+// Not installed; the public interface is include/gdn_slot.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn_slot.h"
+
+struct gdn_pool {
+  gdn_pool_desc d;
+  int64_t C;                 // conv channels = heads * (2*head_k + head_v)
+  int64_t ssm_block_bytes;   // one (layer, slot) ssm block
+  int64_t conv_block_bytes;  // one (layer, slot) conv block (3 rows)
+};
+
+namespace gdn {
+
+constexpr int kConvRows = 3;
+constexpr int kChunk = 64;
+
+// ------------------------------------------------------------ bf16 helpers --
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round to nearest even (finite inputs; NaN maps to a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ------------------------------------------------------------- launchers --
+// Copy layers [layer_begin, layer_end) for n (src, dst) pairs read from device
+// arrays (dst <= 0 skipped).
+hipError_t launch_copy_device_pairs(const gdn_pool *p, int layer_begin, int layer_end, int n,
+                                    const int32_t *src, const int32_t *dst, hipStream_t s);
+// Copy all layers for n host-validated pairs (both in [1, slots), src != dst).
+hipError_t launch_copy_host_pairs(const gdn_pool *p, int n, const int32_t *src,
+                                  const int32_t *dst, hipStream_t s);
+
+struct DecodeArgs {
+  int layer, batch;
+  const int32_t *slot_table;
+  const uint16_t *x;
+  const uint16_t *conv_w;
+  const float *alpha;
+  int alpha_mode;
+  const float *beta;
+  float scale;
+  uint32_t flags;
+  uint16_t *out;
+  const int32_t *seq_len_after;
+  int track_interval;
+  const int32_t *track_slots;
+  const int32_t *next_track_idx;
+};
+hipError_t launch_decode(const gdn_pool *p, const DecodeArgs &a, hipStream_t s);
+
+struct PrefillArgs {
+  int layer, batch, total_tokens, max_seqlen;
+  const int32_t *cu_seqlens;
+  const int32_t *slot_table;
+  const int32_t *has_initial_state;
+  const int32_t *start_len;
+  const uint16_t *x;
+  const uint16_t *conv_w;
+  const float *alpha;
+  int alpha_mode;
+  const float *beta;
+  float scale;
+  uint32_t flags;
+  uint16_t *out;
+  int snap_interval;
+  const int32_t *track_slots;
+  const int32_t *next_track_idx;
+  void *workspace;
+  size_t workspace_bytes;
+};
+hipError_t launch_prefill(const gdn_pool *p, const PrefillArgs &a, hipStream_t s);
+// Workspace of the two-phase prefill: one record per (request, chunk, head) of
+// the chunks processed in one window, plus an fp32 state carry per (request, head).
+size_t prefill_record_bytes(const gdn_pool *p);
+size_t prefill_carry_bytes(const gdn_pool *p, int batch);
+
+}  // namespace gdn

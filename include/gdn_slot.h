@@ -1,0 +1,198 @@
+/*
+ * gdn_slot.h -- C ABI of the MI355X (gfx950) slot-indexed gated delta rule.
+ *
+ * What it computes.  Hybrid linear-attention models keep, per linear layer and
+ * per request, a fixed-size recurrent state in a pooled buffer: a conv window
+ * of the last three projected q/k/v rows and a temporal state S of shape
+ * [heads, head_v, head_k] (page "企业官网建设流程全解析", Kimi K3 notes,
+ * sections "Temporal/SSM state" and "Linear的kv cache大小具体计算逻辑"; page
+ * "SGLang之MambaRadixCache机制", section 1.3).  Every token of a request
+ * updates the slot that the request's slot-table entry names, in place (page
+ * "SGLang之MambaRadixCache机制", section 5.1; page "Qwen3.5 Linear-State Prefix
+ * Cache", section 2.1):
+ *
+ *   y      = causal conv, kernel 4, over [r0, r1, r2, x_t]   (r = conv rows)
+ *   q|k|v  = split of y, head-major;  k <- k / sqrt(sum k^2 + 1e-6)
+ *   S'     = S Diag(alpha_t)                       (alpha per head or per channel)
+ *   d      = beta_t (v - S' k)
+ *   S      = S' + d k^T
+ *   o_t    = scale * S q                           (bf16)
+ *
+ * (recurrence: page "企业官网建设流程全解析", section "Speculative decoding").
+ * Snapshots copy the live state into ping-pong track slots at chunk and
+ * track-interval boundaries (page "SGLang Mamba Radix Cache 深度解析：
+ * extra_buffer 模式的 Ping-Pong 缓冲机制", sections "Prefill 阶段" and "Decode
+ * 阶段"), and a prefix hit copies the deepest checkpoint slot into the live
+ * slot across all layers before a warm prefill (page "Qwen3.5 Linear-State
+ * Prefix Cache", sections 5.1, 6.1 and 6.4).
+ *
+ * Memory.  The caller owns every buffer (pool bytes, inputs, outputs, tables,
+ * the error word, the prefill workspace); the library allocates and frees no
+ * device memory.  All
+ * pointers marked "device" must be device-accessible on the current device.
+ *
+ *   ssm  pool  [layers][slots][heads][head_v][head_k]  fp32 or bf16, head_k fastest
+ *   conv pool  [layers][slots][3][C]                   bf16, C = heads*(2*head_k+head_v)
+ *   x          [tokens][C]     bf16, channel order q | k | v, each head-major
+ *   conv_w     [C][4]          bf16, tap 3 multiplies the current token
+ *   alpha      [tokens][heads] or [tokens][heads][head_k]   fp32, decay in (0, 1]
+ *   beta       [tokens][heads] fp32
+ *   out        [tokens][heads][head_v] bf16
+ *
+ * Slot ids.  Slot 0 is reserved (padding) and never written (page "Qwen3.5
+ * Linear-State Prefix Cache", section 2.3).  A slot-table entry <= 0 skips the
+ * request: nothing is read or written for it and its output rows are zeroed.
+ * An entry >= slots is skipped the same way and sets bit GDN_ERRW_BAD_SLOT in
+ * the pool's error word.  Live slots within one call must be distinct, and so
+ * must destination slots within one copy call.
+ *
+ * Streams and errors.  Every call is asynchronous on the given stream
+ * (a hipStream_t passed as void*, NULL = the default stream) with no internal
+ * synchronisation (page "Qwen3.5 Linear-State Prefix Cache", section 7.1).
+ * Arguments that the host can check are checked before any launch; a failure
+ * returns a negative gdn_status, launches nothing, and leaves a message for
+ * gdn_last_error() on the calling thread.  Calls that write the same slots must
+ * be ordered by the caller (same stream, or events).
+ */
+#ifndef GDN_SLOT_H
+#define GDN_SLOT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gdn_pool *gdn_pool_t;
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_ARG = -1,         /* null pointer, bad enum, inconsistent sizes */
+  GDN_ERR_RANGE = -2,       /* layer or count out of range */
+  GDN_ERR_UNSUPPORTED = -3, /* shape or alignment the kernels do not handle */
+  GDN_ERR_HIP = -4          /* a HIP call failed; see gdn_last_error() */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+enum { GDN_ALPHA_PER_HEAD = 0, GDN_ALPHA_PER_CHANNEL = 1 };
+
+/* flags */
+enum { GDN_F_L2NORM_K = 1u, GDN_F_L2NORM_Q = 2u, GDN_F_CONV_SILU = 4u };
+
+/* bits a kernel may set in the pool's error word (sticky; the caller clears it) */
+enum { GDN_ERRW_BAD_SLOT = 1, GDN_ERRW_BAD_TRACK_SLOT = 2, GDN_ERRW_BAD_SEQLENS = 4 };
+
+typedef struct {
+  int32_t layers, slots, heads, head_k, head_v;
+  int32_t conv_kernel;   /* must be 4 */
+  int32_t ssm_dtype;     /* GDN_F32 | GDN_BF16 */
+  int32_t conv_dtype;    /* GDN_BF16 */
+  void *ssm_base;        /* device, 16-byte aligned, state_pool_bytes() bytes */
+  void *conv_base;       /* device, 16-byte aligned */
+  int32_t *err_word;     /* device int32 or NULL */
+} gdn_pool_desc;
+
+/* Restore request, one per sequence (page "Qwen3.5 Linear-State Prefix Cache",
+ * section 6.1): copy restore_src_slot_id into linear_state_id. */
+typedef struct {
+  int32_t linear_state_id;
+  int32_t restore_requested;   /* 0 or 1 */
+  int32_t restore_src_slot_id; /* < 0: no source was found */
+} gdn_restore_op;
+
+/* Byte sizes of the two pool buffers for a descriptor's shape (pointers in the
+ * descriptor are ignored).  Pure host arithmetic. */
+gdn_status state_pool_bytes(const gdn_pool_desc *desc, size_t *ssm_bytes, size_t *conv_bytes);
+
+/* Validate a descriptor and wrap it in a handle (host memory only).  Supported:
+ * head_k == head_v in {16, 32, 64, 128}, conv_kernel 4, bf16 conv state, fp32 or
+ * bf16 ssm state, both bases 16-byte aligned.  The handle does not own the
+ * buffers.  Thread-safe; the handle is immutable. */
+gdn_status state_pool_create(const gdn_pool_desc *desc, gdn_pool_t *out);
+
+/* Free a handle (not the buffers).  NULL is ignored. */
+void state_pool_destroy(gdn_pool_t pool);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* Device workspace that conv_gdn_prefill_chunked needs to process a batch of
+ * `batch` requests, none longer than max_seqlen tokens, in a single pass.  Less
+ * is accepted (the call then works through the chunks in several windows) down
+ * to the minimum reported for max_seqlen = 64.  Pure host arithmetic. */
+gdn_status gdn_prefill_workspace_bytes(gdn_pool_t pool, int32_t batch, int32_t max_seqlen,
+                                       size_t *bytes);
+
+/* Chunked prefill of one layer for a batch of variable-length requests.
+ * cu_seqlens  device int32 [batch+1], non-decreasing, cu_seqlens[batch] <= total_tokens
+ * max_seqlen  host int: no request is longer (longer ones set GDN_ERRW_BAD_SEQLENS
+ *             and are skipped)
+ * slot_table  device int32 [batch]   live slot of each request
+ * has_initial_state device int32 [batch]: 1 = continue from the slot, 0 = start
+ *             from zero state and zero conv rows (page "Qwen3.5 Linear-State Prefix
+ *             Cache", section 6.4, warm/cold)
+ * start_len   device int32 [batch]   tokens already folded into the slot before
+ *             this call (only used to place snapshots; may be NULL if snap_interval == 0)
+ * snap_interval 0 (no snapshots) or a positive multiple of 64: after the token that
+ *             makes the request length n = start_len + i + 1 a multiple of it, the
+ *             j-th such boundary of the call is written to
+ *             track_slots[2b + ((next_track_idx[b] + j) & 1)] (device int32 [batch][2]
+ *             and [batch]); an entry <= 0 skips that snapshot.  Chunks are 64 tokens
+ *             (page "SGLang Mamba Radix Cache 深度解析", configuration:
+ *             mamba_cache_chunk_size defaults to 64).
+ * workspace   device scratch of workspace_bytes bytes, 256-byte aligned, owned by the
+ *             caller and not read across calls (see gdn_prefill_workspace_bytes)
+ * The live slot receives the state after the last token.  Requests of length 0
+ * leave a warm slot unchanged and zero a cold one. */
+gdn_status conv_gdn_prefill_chunked(gdn_pool_t pool, int32_t layer, int32_t batch,
+                                    int32_t total_tokens, int32_t max_seqlen,
+                                    const int32_t *cu_seqlens, const int32_t *slot_table,
+                                    const int32_t *has_initial_state, const int32_t *start_len,
+                                    const uint16_t *x, const uint16_t *conv_w, const float *alpha,
+                                    int32_t alpha_mode, const float *beta, float scale,
+                                    uint32_t flags, uint16_t *out, int32_t snap_interval,
+                                    const int32_t *track_slots, const int32_t *next_track_idx,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* One decode token per request for one layer (x [batch][C], alpha [batch][heads]
+ * or [batch][heads][head_k], beta [batch][heads], out [batch][heads][head_v]).
+ * The state is always read from the slot.  If track_interval > 0 and
+ * seq_len_after[b] % track_interval == 0 (tokens folded after this step), the
+ * updated conv + ssm state is also written to track_slots[2b + next_track_idx[b]]
+ * (page "企业官网建设流程全解析", section "--mamba-track-interval"; page
+ * "SGLang Mamba Radix Cache 深度解析", section "Decode 阶段").  The caller flips
+ * next_track_idx once per step, after the last layer. */
+gdn_status gdn_decode_step(gdn_pool_t pool, int32_t layer, int32_t batch,
+                           const int32_t *slot_table, const uint16_t *x, const uint16_t *conv_w,
+                           const float *alpha, int32_t alpha_mode, const float *beta, float scale,
+                           uint32_t flags, uint16_t *out, const int32_t *seq_len_after,
+                           int32_t track_interval, const int32_t *track_slots,
+                           const int32_t *next_track_idx, void *stream);
+
+/* Copy conv + ssm state of layers [layer_begin, layer_end) from src_slots[i] to
+ * dst_slots[i] for i < n (device int32 arrays).  dst <= 0 skips the entry; an id
+ * >= slots (or src <= 0 with dst > 0) skips it and sets GDN_ERRW_BAD_TRACK_SLOT.
+ * This is the masked track copy (page "企业官网建设流程全解析", section
+ * "--mamba-track-interval", the scatter into the track slot) and copy_from /
+ * fork (page "SGLang之MambaRadixCache机制", section 3.2).  Byte-exact. */
+gdn_status track_snapshot(gdn_pool_t pool, int32_t layer_begin, int32_t layer_end, int32_t n,
+                          const int32_t *src_slots, const int32_t *dst_slots, void *stream);
+
+/* restore_linear_state_slots (page "Qwen3.5 Linear-State Prefix Cache", sections
+ * 5.1 and 6.4).  ops and has_initial_state are HOST arrays of n_ops entries; the
+ * host decides each op's outcome before launching:
+ *   restore_requested == 0                       -> has_initial_state[i] unchanged
+ *   src < 1 or src >= slots or dst < 1 or dst >= slots -> 0 (COLD_START), no copy
+ *   src == dst                                   -> 1 (RESTORED), no copy
+ *   otherwise: copy conv + ssm of every layer    -> 1 (RESTORED)
+ * If a launch fails, every requested op of the call is set to 0 and GDN_ERR_HIP
+ * is returned.  The copies are queued on the stream (no synchronisation). */
+gdn_status restore_slots(gdn_pool_t pool, int32_t n_ops, const gdn_restore_op *ops,
+                         int64_t *has_initial_state, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_SLOT_H */

@@ -1,0 +1,77 @@
+"""Shared test utilities: comparisons and host<->device conversions.
+
+Only plumbing lives here (no arithmetic of the method): the oracle computes the
+expected values, the library computes the results, and these helpers move and
+compare bits.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+REL_L2_TOL = 2e-3   # floats: relative L2 per (request, head) unit, in the stored dtype
+
+
+def bf16_np(t: torch.Tensor) -> np.ndarray:
+    """Bits of a bf16 tensor (any device) as numpy uint16."""
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def widen(bits: np.ndarray) -> np.ndarray:
+    return oracle.bf16_widen(bits)
+
+
+def rel_l2(got: np.ndarray, want: np.ndarray) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    den = np.linalg.norm(want)
+    num = np.linalg.norm(got - want)
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(num / den)
+
+
+def worst_unit_rel_l2(got: np.ndarray, want: np.ndarray, unit_axes: int) -> float:
+    """Largest relative L2 over units formed by the leading ``unit_axes`` axes."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    lead = got.shape[:unit_axes]
+    g = got.reshape(int(np.prod(lead)), -1)
+    w = want.reshape(int(np.prod(lead)), -1)
+    worst = 0.0
+    for i in range(g.shape[0]):
+        if np.linalg.norm(w[i]) == 0.0 and np.linalg.norm(g[i]) == 0.0:
+            continue
+        worst = max(worst, rel_l2(g[i], w[i]))
+    return worst
+
+
+def pool_to_oracle(ssm: torch.Tensor, conv: torch.Tensor) -> oracle.Pool:
+    """Copy a device (or host) pool into an oracle host pool, byte for byte."""
+    L, N, H, V, K = ssm.shape
+    dt = oracle.SSM_F32 if ssm.dtype == torch.float32 else oracle.SSM_BF16
+    p = oracle.Pool(L, N, H, K, V, dt)
+    if dt == oracle.SSM_F32:
+        p.ssm()[:] = ssm.detach().cpu().numpy()
+    else:
+        p.ssm()[:] = bf16_np(ssm)
+    p.conv()[:] = bf16_np(conv)
+    return p
+
+
+def ssm_values(p: oracle.Pool) -> np.ndarray:
+    """Pool ssm as float64 values [L,N,H,V,K]."""
+    s = p.ssm()
+    return s.astype(np.float64) if p.ssm_dtype == oracle.SSM_F32 else widen(s)
+
+
+def device_ssm_values(ssm: torch.Tensor) -> np.ndarray:
+    return ssm.detach().cpu().to(torch.float64).numpy()
+
+
+def pool_bytes_equal(ssm: torch.Tensor, conv: torch.Tensor, p: oracle.Pool) -> bool:
+    a = ssm.detach().cpu().contiguous().view(torch.uint8).numpy().ravel()
+    b = conv.detach().cpu().contiguous().view(torch.uint8).numpy().ravel()
+    return np.array_equal(a, p.ssm_bytes) and np.array_equal(b, p.conv_bytes)

@@ -1,0 +1,132 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point the header declares, sizes pools like the oracle and the
+pages, and rejects bad arguments before launching anything."""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_slot_amd as gdn
+from gated_delta_rule_slot_amd import _binding as B
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "gdn_slot.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert {"state_pool_bytes", "state_pool_create", "state_pool_destroy", "gdn_last_error",
+            "conv_gdn_prefill_chunked", "gdn_prefill_workspace_bytes", "gdn_decode_step",
+            "track_snapshot", "restore_slots"} <= set(names)
+    lib = ct.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("shape", [
+    (69, 52, 12, 128, 128, 0), (69, 81, 12, 128, 128, 1), (1, 8, 2, 16, 16, 0),
+    (24, 81, 32, 128, 128, 0), (1, 512, 32, 128, 128, 0), (69, 1024, 12, 128, 128, 1)])
+def test_pool_bytes_match_oracle(shape):
+    L, N, H, K, V, dt = shape
+    assert gdn.state_pool_bytes(L, N, H, K, V, dt) == oracle.pool_bytes(L, N, H, K, V, dt)
+
+
+def _desc(**kw):
+    d = dict(layers=1, slots=8, heads=2, head_k=16, head_v=16, conv_kernel=4,
+             ssm_dtype=B.GDN_F32, conv_dtype=B.GDN_BF16, ssm_base=0x10000, conv_base=0x20000,
+             err_word=None)
+    d.update(kw)
+    return B.PoolDesc(*[d[f] for f, _ in B.PoolDesc._fields_])
+
+
+def _create(**kw):
+    h = ct.c_void_p()
+    st = B._lib.state_pool_create(ct.byref(_desc(**kw)), ct.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(conv_kernel=3), -3),
+    (dict(head_k=16, head_v=32), -3),
+    (dict(head_k=48, head_v=48), -3),
+    (dict(ssm_dtype=7), -1),
+    (dict(conv_dtype=B.GDN_F32), -3),
+    (dict(slots=1), -1),
+    (dict(ssm_base=0x10008), -3),
+    (dict(conv_base=None), -1),
+])
+def test_pool_create_validation(kw, status):
+    st, h = _create(**kw)
+    assert st == status, B.last_error()
+    if st == 0:
+        B._lib.state_pool_destroy(h)
+    else:
+        assert B.last_error()
+
+
+def test_calls_reject_bad_arguments_before_launch():
+    st, h = _create()
+    assert st == 0
+    try:
+        fake = ct.c_void_p(0x30000)
+        # bad layer
+        assert B._lib.gdn_decode_step(h, 1, 1, fake, fake, fake, fake, 0, fake, 1.0, 1, fake,
+                                      None, 0, None, None, None) == -2
+        # unknown alpha mode, unknown flag bits
+        assert B._lib.gdn_decode_step(h, 0, 1, fake, fake, fake, fake, 5, fake, 1.0, 1, fake,
+                                      None, 0, None, None, None) == -1
+        assert B._lib.gdn_decode_step(h, 0, 1, fake, fake, fake, fake, 0, fake, 1.0, 64, fake,
+                                      None, 0, None, None, None) == -1
+        # tracking without its tables
+        assert B._lib.gdn_decode_step(h, 0, 1, fake, fake, fake, fake, 0, fake, 1.0, 1, fake,
+                                      None, 256, None, None, None) == -1
+        # snapshot interval not a multiple of 64
+        assert B._lib.conv_gdn_prefill_chunked(
+            h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0, 1, fake,
+            32, fake, fake, fake, 1 << 30, None) == -1
+        # workspace below the minimum
+        assert B._lib.conv_gdn_prefill_chunked(
+            h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0, 1, fake,
+            0, None, None, fake, 16, None) == -1
+        assert "workspace" in B.last_error()
+        # layer range for copies
+        assert B._lib.track_snapshot(h, 0, 2, 1, fake, fake, None) == -2
+    finally:
+        B._lib.state_pool_destroy(h)
+
+
+def test_restore_rules_without_copies_are_host_only():
+    """Ops that need no copy are decided on the host (no GPU needed): not
+    requested -> unchanged, bad source or destination -> COLD_START (0),
+    src == dst -> RESTORED (1)."""
+    st, h = _create()
+    assert st == 0
+    try:
+        pool = B.StatePool(h, None, None, None, (1, 8, 2, 16, 16))
+        ops = [(3, 0, 2), (3, 1, -1), (3, 1, 8), (0, 1, 2), (4, 1, 4)]
+        got = B.restore_slots(pool, ops, [7, 7, 7, 7, 7], stream=type("S", (), {"cuda_stream": 0})())
+        assert got == [7, 0, 0, 0, 1]
+        pool.handle = None
+    finally:
+        B._lib.state_pool_destroy(h)
+
+
+def test_workspace_query():
+    st, h = _create()
+    assert st == 0
+    try:
+        n = ct.c_size_t()
+        assert B._lib.gdn_prefill_workspace_bytes(h, 2, 256, ct.byref(n)) == 0
+        m = ct.c_size_t()
+        assert B._lib.gdn_prefill_workspace_bytes(h, 2, 64, ct.byref(m)) == 0
+        assert n.value > m.value > 0
+    finally:
+        B._lib.state_pool_destroy(h)
