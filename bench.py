@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the slot-indexed gated delta rule on one MI355X.
+
+Headline (the JSON line's `value`): the GDN decode step of a Qwen3-Next-like
+linear layer: 32 heads, K = V = 128, conv width 12288, fp32 state pool of 512
+slots, batch 128, one token per request, scalar decay per head, decode tracking
+at interval 256.  A step is one gdn_decode_step over the batch (slot lookup,
+conv, key norm, recurrence, output, track snapshot when a request reaches a
+multiple of 256).  Steps rotate over three disjoint 128-slot batches so that
+consecutive steps do not find the previous step's state in the last-level
+cache.  Inputs are resident in HBM before timing starts.
+
+Secondary lines (in "extra"): the KDA chunked prefill (12 heads, one request of
+6144 tokens, snapshot every 64 tokens), the KDA decode with tracking over 69
+layers, and a prefix-hit restore across 24 layers followed by a warm prefill.
+
+Run on one GPU only: --gpus N with N > 1 exits with a message.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def event_pair():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+# ------------------------------------------------------------------ decode --
+def gdn_decode_setup(torch, gdn, wl, dev):
+    cfg = wl.GDN_DECODE
+    H, D, N, B = cfg.heads, cfg.head_k, cfg.slots, 128
+    C = H * 3 * D
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    ssm = 0.25 * torch.randn(1, N, H, D, D, device=dev, generator=g)
+    conv = torch.randn(1, N, 3, C, device=dev, generator=g).to(torch.bfloat16)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    pool = gdn.state_pool_create(ssm, conv, err)
+    gc = wl.generator(cfg.seed)
+    w = wl.conv_weights(gc, C).to(dev)
+    perm = torch.randperm(N - 1, generator=gc) + 1
+    tables = [perm[i * B:(i + 1) * B].to(torch.int32).to(dev) for i in range(3)]
+    spare = perm[3 * B:]
+    track = torch.stack([spare[(2 * torch.arange(B)) % spare.numel()],
+                         spare[(2 * torch.arange(B) + 1) % spare.numel()]], 1).to(torch.int32).to(dev)
+    inputs = [{k: v.to(dev) for k, v in wl.projected_inputs(gc, B, H, D, D, cfg.alpha_mode).items()}
+              for _ in range(3)]
+    base = (1 + 2 * torch.arange(B, dtype=torch.int32)).to(dev)   # distinct phases mod 256
+    nxt = torch.zeros(B, dtype=torch.int32, device=dev)
+    out = torch.empty(B, H, D, dtype=torch.bfloat16, device=dev)
+    return dict(cfg=cfg, pool=pool, w=w, tables=tables, track=track, inputs=inputs, base=base,
+                nxt=nxt, out=out, H=H, D=D, B=B, C=C)
+
+
+def gdn_decode_launch(gdn, st, step):
+    i = step % 3
+    inp = st["inputs"][i]
+    gdn.gdn_decode_step(st["pool"], 0, st["tables"][i], inp["x"], st["w"], inp["alpha"],
+                        st["cfg"].alpha_mode, inp["beta"], st["out"],
+                        seq_len_after=st["base"] + step, track_interval=256,
+                        track_slots=st["track"], next_track_idx=st["nxt"])
+
+
+def decode_bytes(B, H, D, C, state_bytes, alpha_per_channel, snapshots):
+    """Algorithmic HBM bytes of one decode launch (each byte the method must move once)."""
+    per_req = (2 * H * D * D * state_bytes      # state read + write
+               + 2 * 3 * C * 2                  # conv rows read + write
+               + C * 2                          # x
+               + H * (D if alpha_per_channel else 1) * 4 + H * 4  # alpha, beta
+               + H * D * 2                      # out
+               + 4)                             # slot id
+    snap = snapshots * (H * D * D * state_bytes + 3 * C * 2)
+    return B * per_req + C * 4 * 2 + snap
+
+
+def run_headline(torch, gdn, wl, dev, steps, warmup):
+    st = gdn_decode_setup(torch, gdn, wl, dev)
+    B, H, D, C = st["B"], st["H"], st["D"], st["C"]
+    for s in range(warmup):
+        gdn_decode_launch(gdn, st, s)
+    torch.cuda.synchronize()
+    evs = [event_pair() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        evs[k][0].record()
+        gdn_decode_launch(gdn, st, warmup + k)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    # snapshots taken in the timed steps (requests whose length hit a multiple of 256)
+    base = st["base"].cpu()
+    snaps = sum(int(((base + warmup + k) % 256 == 0).sum()) for k in range(steps))
+    total_bytes = sum(decode_bytes(B, H, D, C, 4, False, 0) for _ in range(steps)) + \
+        snaps * (H * D * D * 4 + 3 * C * 2)
+    avg_kernel_s = sum(kern_ms) / len(kern_ms) / 1e3
+    achieved = total_bytes / steps / avg_kernel_s / 1e9
+    assert int(st["pool"].err_word.item()) == 0
+    return dict(elapsed=elapsed, tokens=B * steps, avg_kernel_s=avg_kernel_s,
+                bytes_per_launch=total_bytes / steps, achieved_gbs=achieved, snapshots=snaps)
+
+
+# ----------------------------------------------------------------- prefill --
+def run_kda_prefill(torch, gdn, wl, dev, reps=5):
+    cfg = wl.KDA_PREFILL
+    H, D, T = cfg.heads, cfg.head_k, 6144
+    C = H * 3 * D
+    g = wl.generator(cfg.seed)
+    inp = {k: v.to(dev) for k, v in wl.projected_inputs(g, T, H, D, D, cfg.alpha_mode).items()}
+    w = wl.conv_weights(g, C).to(dev)
+    ssm = torch.zeros(1, cfg.slots, H, D, D, dtype=torch.bfloat16, device=dev)
+    conv = torch.zeros(1, cfg.slots, 3, C, dtype=torch.bfloat16, device=dev)
+    pool = gdn.state_pool_create(ssm, conv, torch.zeros(1, dtype=torch.int32, device=dev))
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    slot = torch.tensor([1], dtype=torch.int32, device=dev)
+    cold = torch.zeros(1, dtype=torch.int32, device=dev)
+    start = torch.zeros(1, dtype=torch.int32, device=dev)
+    track = torch.tensor([[2, 3]], dtype=torch.int32, device=dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(pool, 1, T), dtype=torch.uint8, device=dev)
+
+    def call():
+        gdn.conv_gdn_prefill_chunked(pool, 0, cu, slot, cold, inp["x"], w, inp["alpha"],
+                                     cfg.alpha_mode, inp["beta"], out, T, start_len=start,
+                                     snap_interval=64, track_slots=track, next_track_idx=nxt,
+                                     workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = event_pair()
+        a.record()
+        call()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    t = sorted(ms)[len(ms) // 2] / 1e3
+    flops = T * H * 140.6e3               # chunked-form algorithmic flops per (token, head)
+    io = T * (C * 2 + H * D * 4 + H * 4 + H * D * 2) + C * 8
+    snaps = (T // 64) * (H * D * D * 2 + 3 * C * 2)
+    byts = io + snaps + H * D * D * 2
+    return {"workload": "KDA chunked prefill: 12 heads, K=V=128, 1 x 6144 tokens, snapshot every 64",
+            "tokens_per_s": T / t, "ms": t * 1e3,
+            "mfma_util_vs_bf16_peak": flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": byts,
+            "algorithmic_flops": flops}
+
+
+# ----------------------------------------------------------------- restore --
+def run_restore(torch, gdn, wl, dev, reps=5):
+    cfg = wl.WARM_PREFILL
+    L, N, H, D = cfg.layers, cfg.slots, cfg.heads, cfg.head_k
+    C = H * 3 * D
+    ssm = torch.empty(L, N, H, D, D, dtype=torch.float32, device=dev)
+    conv = torch.empty(L, N, 3, C, dtype=torch.bfloat16, device=dev)
+    ssm.fill_(0.5)
+    conv.fill_(1.0)
+    pool = gdn.state_pool_create(ssm, conv)
+    # 35 restored requests (the expected count for the prefix mix): checkpoints 65..80 -> live 1..35
+    n = 35
+    ops = [(1 + i, 1, 65 + (i % 16)) for i in range(n)]
+    gdn.restore_slots(pool, ops, [0] * n)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = event_pair()
+        a.record()
+        gdn.restore_slots(pool, ops, [0] * n)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    t = sorted(ms)[len(ms) // 2] / 1e3
+    per_op = L * (H * D * D * 4 + 3 * C * 2)
+    byts = 2 * n * per_op
+    return {"workload": "prefix-hit restore: 35 requests x 24 layers, 32 heads, fp32 state",
+            "GB_per_s": byts / t / 1e9, "ms": t * 1e3, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS,
+            "bytes": byts}
+
+
+# ------------------------------------------------------------ cpu baseline --
+def cpu_baseline(wl, seconds=10.0):
+    import numpy as np
+    import oracle
+    cfg = wl.GDN_DECODE
+    H, D, B = cfg.heads, cfg.head_k, 128
+    g = wl.generator(cfg.seed)
+    pool = oracle.Pool(1, 2 * B + 1, H, D, D, oracle.SSM_F32)
+    pool.ssm()[:] = 0.25
+    w = wl.bf16_bits(wl.conv_weights(g, H * 3 * D))
+    inp = wl.projected_inputs(g, B, H, D, D, cfg.alpha_mode)
+    x, a, b = wl.bf16_bits(inp["x"]), inp["alpha"].numpy(), inp["beta"].numpy()
+    slots = np.arange(1, B + 1, dtype=np.int32)
+    steps = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        oracle.decode_step(pool, 0, slots, x, w, a, cfg.alpha_mode, b, precision="f32")
+        steps += 1
+    t = time.perf_counter() - t0
+    return {"value": B * steps / t, "unit": "tokens/s", "cores": oracle.num_threads("f32"),
+            "kind": "oracle",
+            "sample": f"{steps} GDN decode steps (128 requests x 32 heads, K=V=128, fp32) "
+                      f"of the fp32 oracle in {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the hot path has no cross-GPU step and this build "
+              "runs on a single MI355X; rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_slot_amd as gdn
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    log("headline: GDN decode")
+    r = run_headline(torch, gdn, wl, dev, args.steps, args.warmup)
+    value = r["tokens"] / r["elapsed"]
+    extra = {}
+    if not args.no_extra:
+        log("extra: KDA prefill")
+        extra["kda_prefill"] = run_kda_prefill(torch, gdn, wl, dev)
+        log("extra: restore")
+        extra["restore"] = run_restore(torch, gdn, wl, dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+    line = {
+        "metric": "gated-delta tokens/s (prefill, decode) + state-copy GB/s, % of HBM/MFMA peak",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["elapsed"] / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "GDN decode step: 32 heads, K=V=128, conv width 12288, fp32 pool "
+                               "of 512 slots, batch 128, 1 token/request, tracking every 256",
+                   "batch": 128, "heads": 32, "head_dim": 128, "pool_slots": 512},
+        "roofline": {"bound": "hbm", "achieved": r["achieved_gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": r["achieved_gbs"] / HBM_PEAK_GBS, "traffic": None},
+        "kernel_avg_us": r["avg_kernel_s"] * 1e6,
+        "bytes_per_launch": r["bytes_per_launch"],
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -136,7 +136,7 @@ GDN_API gdn_status conv_gdn_prefill_chunked(
                 snap_interval);
   if (snap_interval > 0 && (!track_slots || !next_track_idx || !start_len))
     return fail(GDN_ERR_ARG, "snapshots need track_slots, next_track_idx and start_len");
-  if (!aligned(conv_w, 8)) return fail(GDN_ERR_UNSUPPORTED, "conv_w must be 8-byte aligned");
+  if (!aligned(conv_w, 16)) return fail(GDN_ERR_UNSUPPORTED, "conv_w must be 16-byte aligned");
   if (x && !aligned(x, 16)) return fail(GDN_ERR_UNSUPPORTED, "x must be 16-byte aligned");
   if (out && !aligned(out, 16)) return fail(GDN_ERR_UNSUPPORTED, "out must be 16-byte aligned");
   if (!aligned(alpha, 16)) return fail(GDN_ERR_UNSUPPORTED, "alpha must be 16-byte aligned");

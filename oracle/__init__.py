@@ -61,6 +61,7 @@ def lib(precision: str = "f64"):
         _build.build()
     L = ct.CDLL(path)
     L.oracle_real_bytes.restype = ct.c_int
+    L.oracle_num_threads.restype = ct.c_int
     L.oracle_pool_bytes.argtypes = [ct.c_int32] * 6 + [ct.POINTER(ct.c_size_t)] * 2
     L.oracle_prefill.argtypes = [
         ct.POINTER(_Pool), ct.c_int32, ct.c_int32, _i32p, _i32p, _i32p, _i32p,
@@ -102,6 +103,10 @@ def _c(a, dtype):
             raise TypeError("bf16 data must be passed as uint16 bit patterns")
         a = a.astype(dtype)
     return np.ascontiguousarray(a)
+
+
+def num_threads(precision="f64") -> int:
+    return lib(precision).oracle_num_threads()
 
 
 def pool_bytes(layers, slots, heads, head_k, head_v, ssm_dtype, precision="f64"):

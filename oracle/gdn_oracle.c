@@ -25,6 +25,13 @@ typedef ORACLE_REAL real;
 
 int oracle_real_bytes(void) { return (int)sizeof(real); }
 
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif
+
 /* ---------------------------------------------------------------- bf16 ---- */
 
 double oracle_bf16_widen(uint16_t h) {

@@ -65,6 +65,9 @@ typedef struct {
 /* Size of the arithmetic type this build uses: 4 or 8. */
 int oracle_real_bytes(void);
 
+/* Threads the OpenMP loops use. */
+int oracle_num_threads(void);
+
 /* Bytes of the two pool buffers for the given shape. Returns 4 on bad shape. */
 int oracle_pool_bytes(int32_t layers, int32_t slots, int32_t heads, int32_t head_k,
                       int32_t head_v, int32_t ssm_dtype, size_t *ssm_bytes,

@@ -1,0 +1,228 @@
+"""GPU parity of conv_gdn_prefill_chunked against the oracle.
+
+Outputs: GPU bf16 against the oracle's bf16-rounded outputs; states: in the pool
+dtype; both as relative L2 per (request, head) unit, tolerance 2e-3.  Conv rows,
+snapshot placement and untouched slots: bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests.helpers import (REL_L2_TOL, bf16_np, device_ssm_values, pool_to_oracle, ssm_values,
+                           widen, worst_unit_rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+
+class Case:
+    def __init__(self, seed, H, D, lens, bf16=False, amode=1, slots=None, N=None, L=1,
+                 warm=None, start=None, flags=1, scale=1.0, snap=0):
+        g = wl.generator(seed)
+        B = len(lens)
+        self.H, self.D, self.lens, self.amode, self.flags, self.scale = H, D, lens, amode, flags, scale
+        self.L = L
+        self.layer = L - 1
+        self.N = N or (3 * B + 2)
+        self.ssm, self.conv = wl.warm_pool(g, L, self.N, H, D, D, bf16)
+        self.w = wl.conv_weights(g, 3 * H * D)
+        self.inp = wl.projected_inputs(g, max(sum(lens), 1), H, D, D, amode)
+        self.cu = wl.cu_seqlens(lens)
+        perm = torch.randperm(self.N - 1, generator=g) + 1
+        self.slots = (perm[:B] if slots is None else torch.tensor(slots)).to(torch.int32)
+        self.track = perm[B:3 * B].reshape(B, 2).to(torch.int32).contiguous()
+        self.nxt = torch.randint(0, 2, (B,), generator=g, dtype=torch.int32)
+        self.warm = torch.tensor(warm if warm is not None else [1] * B, dtype=torch.int32)
+        self.start = torch.tensor(start if start is not None else [0] * B, dtype=torch.int32)
+        self.snap = snap
+
+    def run_gpu(self, workspace_bytes=None):
+        import gated_delta_rule_slot_amd as gdn
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        pool = gdn.state_pool_create(self.ssm.cuda(), self.conv.cuda(), err)
+        T = int(self.cu[-1])
+        out = torch.full((max(T, 1), self.H, self.D), -7.0, dtype=torch.bfloat16, device="cuda")
+        maxlen = max(self.lens) if self.lens else 0
+        need = gdn.gdn_prefill_workspace_bytes(pool, len(self.lens), maxlen)
+        ws = torch.empty(workspace_bytes or need, dtype=torch.uint8, device="cuda")
+        gdn.conv_gdn_prefill_chunked(
+            pool, self.layer, self.cu.cuda(), self.slots.cuda(), self.warm.cuda(),
+            self.inp["x"].cuda(), self.w.cuda(), self.inp["alpha"].cuda(), self.amode,
+            self.inp["beta"].cuda(), out, maxlen, start_len=self.start.cuda(), scale=self.scale,
+            flags=self.flags, snap_interval=self.snap, track_slots=self.track.cuda(),
+            next_track_idx=self.nxt.cuda(), workspace=ws)
+        torch.cuda.synchronize()
+        return pool, out[:T]
+
+    def run_oracle(self):
+        ref = pool_to_oracle(self.ssm, self.conv)
+        o, e = oracle.prefill(
+            ref, self.layer, self.cu.numpy(), self.slots.numpy(), wl.bf16_bits(self.inp["x"]),
+            wl.bf16_bits(self.w), self.inp["alpha"].numpy(), self.amode, self.inp["beta"].numpy(),
+            has_initial_state=self.warm.numpy(), start_len=self.start.numpy(), scale=self.scale,
+            flags=self.flags, snap_interval=self.snap,
+            track_slots=self.track.numpy() if self.snap else None,
+            next_track_idx=self.nxt.numpy() if self.snap else None)
+        return ref, o, e
+
+    def written_slots(self):
+        s = [int(v) for v in self.slots if 0 < int(v) < self.N]
+        if self.snap:
+            for b, n in enumerate(self.lens):
+                if not (0 < int(self.slots[b]) < self.N):
+                    continue
+                st = int(self.start[b])
+                if any((st + i + 1) % self.snap == 0 for i in range(n)):
+                    s += [int(v) for v in self.track[b] if 0 < int(v) < self.N]
+        return sorted(set(s))
+
+
+def check(case, pool, out, ref, o_ref, tol=REL_L2_TOL):
+    T = int(case.cu[-1])
+    go = widen(bf16_np(out)).reshape(T, case.H, case.D)
+    wo = widen(o_ref).reshape(T, case.H, case.D)
+    eo = 0.0
+    for b in range(len(case.lens)):   # units: (request, head)
+        s0, s1 = int(case.cu[b]), int(case.cu[b + 1])
+        if s1 > s0:
+            eo = max(eo, worst_unit_rel_l2(go[s0:s1].transpose(1, 0, 2), wo[s0:s1].transpose(1, 0, 2), 1))
+    written = case.written_slots()
+    gs, ws = device_ssm_values(pool.ssm), ssm_values(ref)
+    es = worst_unit_rel_l2(gs[case.layer, written], ws[case.layer, written], 2) if written else 0.0
+    print(f"  worst unit rel-L2: out {eo:.2e}  state {es:.2e}", flush=True)
+    assert np.all(np.isfinite(widen(bf16_np(out))))
+    assert np.all(np.isfinite(gs[case.layer, written]))
+    assert eo <= tol, eo
+    assert es <= tol, es
+    assert np.array_equal(bf16_np(pool.conv), ref.conv()), "conv rows differ"
+    L, N = gs.shape[:2]
+    mask = np.ones((L, N), bool)
+    mask[case.layer, written] = False
+    a = pool.ssm.cpu().contiguous().view(torch.uint8).numpy().reshape(L, N, -1)
+    b = ref.ssm_bytes.reshape(L, N, -1)
+    assert np.array_equal(a[mask], b[mask]), "a slot that the call does not name changed"
+    return eo, es
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny D16 fp32 KDA, snapshots every 64", dict(seed=101, H=2, D=16, lens=[256, 256], snap=64,
+                                                   warm=[0, 0], N=8)),
+    ("D32 bf16 GDN ragged", dict(seed=3, H=3, D=32, lens=[1, 63, 64, 65, 130], bf16=True, amode=0)),
+    ("D64 fp32 KDA warm/cold", dict(seed=4, H=4, D=64, lens=[200, 7, 129], warm=[1, 0, 1],
+                                    scale=0.5)),
+    ("D128 bf16 KDA snapshots, unaligned start", dict(seed=5, H=4, D=128, lens=[300, 70, 2],
+                                                      bf16=True, snap=64, start=[64, 37, 126],
+                                                      warm=[1, 1, 1])),
+    ("D128 fp32 GDN silu + q norm", dict(seed=6, H=6, D=128, lens=[190, 64], amode=0, flags=7)),
+    ("D128 empty and bad slots", dict(seed=7, H=2, D=128, lens=[0, 40, 0, 33], slots=[3, 0, 4, 5],
+                                      warm=[1, 1, 0, 1], N=14)),
+])
+def test_prefill_parity(name, kw):
+    print(f"prefill parity: {name}", flush=True)
+    case = Case(**kw)
+    pool, out = case.run_gpu()
+    ref, o_ref, e = case.run_oracle()
+    check(case, pool, out, ref, o_ref)
+    assert int(pool.err_word.item()) == 0
+
+
+def test_prefill_small_workspace_windows_match_single_pass():
+    """A workspace that holds one chunk per request forces many windows; the
+    fp32 carry between windows makes the result identical bit for bit."""
+    print("prefill windows", flush=True)
+    import gated_delta_rule_slot_amd as gdn
+    case = Case(seed=8, H=3, D=64, lens=[333, 64, 129], amode=1, bf16=True, snap=128,
+                start=[0, 64, 128])
+    p1, o1 = case.run_gpu()
+    H, D, B = case.H, case.D, 3
+    minimum = gdn.gdn_prefill_workspace_bytes(p1, B, 64)
+    p2, o2 = case.run_gpu(workspace_bytes=minimum)
+    assert torch.equal(o1, o2)
+    assert torch.equal(p1.ssm, p2.ssm) and torch.equal(p1.conv, p2.conv)
+    ref, o_ref, e = case.run_oracle()
+    check(case, p2, o2, ref, o_ref)
+
+
+def test_prefill_full_kda_workload():
+    """12 heads, K=V=128, one request of 6144 tokens, per-channel decay, bf16
+    pool, snapshot at every 64-token boundary: checked in full."""
+    print("prefill parity: full KDA prefill workload", flush=True)
+    cfg = wl.KDA_PREFILL
+    case = Case(seed=cfg.seed, H=cfg.heads, D=cfg.head_k, lens=[6144], bf16=True, amode=1,
+                snap=64, warm=[0], N=cfg.slots)
+    pool, out = case.run_gpu()
+    ref, o_ref, e = case.run_oracle()
+    check(case, pool, out, ref, o_ref)
+
+
+def test_prefill_warm_gdn_subset():
+    """32 heads, K=V=128, scalar decay, fp32 pool, warm starts at a 6144
+    boundary followed by ragged remainders (a sample of the prefix-hit workload)."""
+    print("prefill parity: warm GDN sample", flush=True)
+    cfg = wl.WARM_PREFILL
+    case = Case(seed=cfg.seed, H=cfg.heads, D=cfg.head_k, lens=[1312, 700, 2048], amode=0,
+                start=[12288, 6144, 6144], warm=[1, 1, 1], N=12, snap=6144)
+    pool, out = case.run_gpu()
+    ref, o_ref, e = case.run_oracle()
+    check(case, pool, out, ref, o_ref)
+
+
+def test_prefill_extreme_decay():
+    """Channels with alpha = 1e-3 (and a head at 1e-20) stay finite and match."""
+    print("prefill extreme decay", flush=True)
+    case = Case(seed=9, H=3, D=128, lens=[150, 64], amode=1)
+    case.inp["alpha"][:, :, :16] = 1e-3
+    case.inp["alpha"][40:90, 1, :] = 1e-20
+    pool, out = case.run_gpu()
+    ref, o_ref, e = case.run_oracle()
+    check(case, pool, out, ref, o_ref)
+
+
+def test_prefill_then_restore_then_resume():
+    """Tiny workload end to end: prefill 256 tokens with a snapshot every 64,
+    restore each boundary's snapshot into a fresh slot, resume to 256, and land
+    on the uninterrupted state (GPU against the oracle at every step)."""
+    import gated_delta_rule_slot_amd as gdn
+    print("prefill + restore + resume", flush=True)
+    case = Case(seed=101, H=2, D=16, lens=[256, 256], snap=64, warm=[0, 0], N=8, slots=[1, 2])
+    case.track = torch.tensor([[3, 4], [5, 6]], dtype=torch.int32)
+    case.nxt = torch.zeros(2, dtype=torch.int32)
+    full_pool, full_out = case.run_gpu()
+    ref_full, o_full, _ = case.run_oracle()
+    check(case, full_pool, full_out, ref_full, o_full)
+    # prefill to 192 (snapshots at 64, 128, 192: the last lands in track[0])
+    part = Case(seed=101, H=2, D=16, lens=[256, 256], snap=64, warm=[0, 0], N=8, slots=[1, 2])
+    part.track, part.nxt = case.track, case.nxt
+    x, al, be = part.inp["x"], part.inp["alpha"], part.inp["beta"]
+    idx = torch.cat([torch.arange(0, 192), torch.arange(256, 448)])
+    part.inp = {"x": x[idx].contiguous(), "alpha": al[idx].contiguous(), "beta": be[idx].contiguous()}
+    part.lens, part.cu = [192, 192], wl.cu_seqlens([192, 192])
+    pool, _ = part.run_gpu()
+    ref, _, _ = part.run_oracle()
+    # preemption: live slots overwritten with garbage, then restore 192's snapshot into 7 and 1
+    pool.ssm[0, 1].fill_(float("nan"))
+    pool.ssm[0, 2].fill_(float("nan"))
+    ref.ssm()[0, 1] = np.nan
+    ref.ssm()[0, 2] = np.nan
+    ops = [(7, 1, 3), (1, 1, 5)]
+    hi = gdn.restore_slots(pool, ops, [0, 0])
+    hi_ref = oracle.restore_slots(ref, ops, np.zeros(2, dtype=np.int64))
+    assert hi == hi_ref.tolist() == [1, 1]
+    torch.cuda.synchronize()
+    # resume the last 64 tokens of each request from the restored slots
+    res = Case(seed=101, H=2, D=16, lens=[64, 64], N=8, slots=[7, 1], warm=[1, 1], start=[192, 192])
+    res.ssm = pool.ssm.cpu()
+    res.conv = pool.conv.cpu()
+    idx = torch.cat([torch.arange(192, 256), torch.arange(448, 512)])
+    res.inp = {"x": x[idx].contiguous(), "alpha": al[idx].contiguous(), "beta": be[idx].contiguous()}
+    rpool, rout = res.run_gpu()
+    rref, ro, _ = res.run_oracle()
+    check(res, rpool, rout, rref, ro)
+    # and the resumed state equals the uninterrupted run's, within tolerance
+    a = device_ssm_values(rpool.ssm)[0, [7, 1]]
+    b = device_ssm_values(full_pool.ssm)[0, [1, 2]]
+    assert worst_unit_rel_l2(a, b, 2) <= REL_L2_TOL
+    got_o = widen(bf16_np(rout)).reshape(2, 64, 2, 16)
+    want_o = widen(bf16_np(full_out)).reshape(2, 256, 2, 16)[:, 192:]
+    assert worst_unit_rel_l2(got_o.transpose(0, 2, 1, 3), want_o.transpose(0, 2, 1, 3), 2) <= REL_L2_TOL
