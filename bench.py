@@ -65,12 +65,12 @@ def gdn_decode_setup(torch, gdn, wl, dev):
                 nxt=nxt, out=out, H=H, D=D, B=B, C=C)
 
 
-def gdn_decode_launch(gdn, st, step):
+def gdn_decode_launch(gdn, st, step, seq_len_after):
     i = step % 3
     inp = st["inputs"][i]
     gdn.gdn_decode_step(st["pool"], 0, st["tables"][i], inp["x"], st["w"], inp["alpha"],
                         st["cfg"].alpha_mode, inp["beta"], st["out"],
-                        seq_len_after=st["base"] + step, track_interval=256,
+                        seq_len_after=seq_len_after, track_interval=256,
                         track_slots=st["track"], next_track_idx=st["nxt"])
 
 
@@ -89,29 +89,45 @@ def decode_bytes(B, H, D, C, state_bytes, alpha_per_channel, snapshots):
 def run_headline(torch, gdn, wl, dev, steps, warmup):
     st = gdn_decode_setup(torch, gdn, wl, dev)
     B, H, D, C = st["B"], st["H"], st["D"], st["C"]
+    # per-step lengths after the step, prepared before timing
+    seqs = [st["base"] + s for s in range(warmup + steps)]
     for s in range(warmup):
-        gdn_decode_launch(gdn, st, s)
+        gdn_decode_launch(gdn, st, s, seqs[s])
     torch.cuda.synchronize()
-    evs = [event_pair() for _ in range(steps)]
-    torch.cuda.synchronize()
+    start, end = event_pair()
     t0 = time.perf_counter()
+    start.record()
     for k in range(steps):
-        evs[k][0].record()
-        gdn_decode_launch(gdn, st, warmup + k)
-        evs[k][1].record()
+        gdn_decode_launch(gdn, st, warmup + k, seqs[warmup + k])
+    end.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
-    # snapshots taken in the timed steps (requests whose length hit a multiple of 256)
+    # the stream holds nothing but the decode launches between the two events
+    avg_kernel_s = start.elapsed_time(end) / steps / 1e3
     base = st["base"].cpu()
     snaps = sum(int(((base + warmup + k) % 256 == 0).sum()) for k in range(steps))
-    total_bytes = sum(decode_bytes(B, H, D, C, 4, False, 0) for _ in range(steps)) + \
+    total_bytes = steps * decode_bytes(B, H, D, C, 4, False, 0) + \
         snaps * (H * D * D * 4 + 3 * C * 2)
-    avg_kernel_s = sum(kern_ms) / len(kern_ms) / 1e3
     achieved = total_bytes / steps / avg_kernel_s / 1e9
     assert int(st["pool"].err_word.item()) == 0
     return dict(elapsed=elapsed, tokens=B * steps, avg_kernel_s=avg_kernel_s,
                 bytes_per_launch=total_bytes / steps, achieved_gbs=achieved, snapshots=snaps)
+
+
+def copy_calibration(torch, dev):
+    """Achieved bandwidth of a plain 1 GiB device-to-device copy (context for % of peak)."""
+    a = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    s, e = event_pair()
+    s.record()
+    for _ in range(10):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 10 / 1e3
+    return 2 * a.numel() * 4 / t / 1e9
 
 
 # ----------------------------------------------------------------- prefill --
@@ -239,7 +255,7 @@ def main():
     log("headline: GDN decode")
     r = run_headline(torch, gdn, wl, dev, args.steps, args.warmup)
     value = r["tokens"] / r["elapsed"]
-    extra = {}
+    extra = {"hbm_copy_calibration_GBps": copy_calibration(torch, dev)}
     if not args.no_extra:
         log("extra: KDA prefill")
         extra["kda_prefill"] = run_kda_prefill(torch, gdn, wl, dev)

@@ -106,7 +106,9 @@ GDN_API gdn_status gdn_prefill_workspace_bytes(gdn_pool_t pool, int32_t batch,
                                                int32_t max_seqlen, size_t *bytes) {
   if (!pool || !bytes) return fail(GDN_ERR_ARG, "pool or bytes is NULL");
   if (batch < 0 || max_seqlen < 0) return fail(GDN_ERR_RANGE, "batch or max_seqlen < 0");
-  const size_t chunks = (size_t(max_seqlen) + gdn::kChunk - 1) / gdn::kChunk;
+  // chunks are aligned to absolute positions, so a request may touch one more
+  // chunk than ceil(len / 64) when its start is not a multiple of 64
+  const size_t chunks = (size_t(max_seqlen) + 2 * gdn::kChunk - 2) / gdn::kChunk;
   *bytes = (chunks ? chunks : 1) * size_t(batch) * pool->d.heads * gdn::prefill_record_bytes(pool) +
            gdn::prefill_carry_bytes(pool, batch);
   return ok();
@@ -175,7 +177,8 @@ GDN_API gdn_status gdn_decode_step(gdn_pool_t pool, int32_t layer, int32_t batch
   if (track_interval < 0) return fail(GDN_ERR_ARG, "track_interval < 0");
   if (track_interval > 0 && (!seq_len_after || !track_slots || !next_track_idx))
     return fail(GDN_ERR_ARG, "tracking needs seq_len_after, track_slots and next_track_idx");
-  if (!aligned(conv_w, 8)) return fail(GDN_ERR_UNSUPPORTED, "conv_w must be 8-byte aligned");
+  if (!aligned(conv_w, 16)) return fail(GDN_ERR_UNSUPPORTED, "conv_w must be 16-byte aligned");
+  if (!aligned(x, 16)) return fail(GDN_ERR_UNSUPPORTED, "x must be 16-byte aligned");
   if (!aligned(alpha, 16)) return fail(GDN_ERR_UNSUPPORTED, "alpha must be 16-byte aligned");
   gdn::DecodeArgs a{layer,       batch,         slot_table,     x,           conv_w,
                     alpha,       alpha_mode,    beta,           scale,       flags,

@@ -1,4 +1,5 @@
-// decode.hip -- one decode token per request, one workgroup per (request, head).
+// decode.hip -- one decode token per request; per (request, head) one workgroup
+// whose waves each own a few state rows.
 //
 // Per token and head (page "企业官网建设流程全解析", Kimi K3 notes, section
 // "Speculative decoding" for the recurrence; section "Linear的kv cache大小具体
@@ -14,14 +15,12 @@
 // spread over D/VEC adjacent lanes: every load and store instruction of a wave
 // covers whole contiguous rows.  The per-row dot products S'k and S'q reduce
 // over those lanes with cross-lane shuffles.  All of a lane's state vectors are
-// loaded before the conv prologue runs, so the HBM reads overlap with it.
+// loaded before the conv prologue runs, so the HBM reads overlap with it; the
+// state is streamed with non-temporal loads and stores (it is not reused).
 #include "common.hpp"
 
 namespace gdn {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 
 template <typename TS>
 struct StateVec;
@@ -58,41 +57,56 @@ struct StateVec<uint16_t> {  // bf16
   }
 };
 
-__device__ __forceinline__ float block_sum(float v, float *scratch) {
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();  // scratch may still be read by a previous call
-  if (lane == 0) scratch[w] = v;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) t += scratch[i];
-  return t;
+  return v;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One workgroup per (request, head); each of its waves owns ROWS state rows.  The head's conv is split across the waves into shared memory;
+// after the single barrier every wave has what it needs, writes back its own
+// slice of the conv rows (all old rows were read before the barrier) and runs
+// its rows to completion on its own (norms are recomputed per wave).
+// Rows per wave: kIters 16-byte vectors per lane.  Measured on MI355X for this
+// in-place read-modify-write stream: 8 beat 4 (1024-thread workgroups) and 16.
+constexpr int kIters = 8;
+template <int D, typename TS>
+struct DecodeShape {
+  static constexpr int VEC = StateVec<TS>::N;
+  static constexpr int LPR = D / VEC;                         // lanes per row
+  static constexpr int RPI = 64 / LPR;                        // rows per load instruction
+  static constexpr int ROWS = RPI * kIters < D ? RPI * kIters : D;  // state rows per wave
+  static constexpr int THREADS = 64 * (D / ROWS);
+};
+
 template <int D, typename TS, int kAlphaMode>
-__global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
+__global__ __launch_bounds__((DecodeShape<D, TS>::THREADS)) void gdn_decode_kernel(
     TS *__restrict__ ssm, uint16_t *__restrict__ conv, int32_t *err, int slots, int heads,
     DecodeArgs a) {
   using SV = StateVec<TS>;
+  using SH = DecodeShape<D, TS>;
   constexpr int VEC = SV::N;
-  constexpr int LPR = D / VEC;          // lanes per row
-  constexpr int RPI = 64 / LPR;         // rows per wave instruction
-  constexpr int GROUPS = (D + RPI - 1) / RPI;  // row groups per head
-  constexpr int ITERS = (GROUPS + kWaves - 1) / kWaves;
+  constexpr int ROWS = SH::ROWS;          // state rows per wave
+  constexpr int LPR = SH::LPR;            // lanes per row
+  constexpr int RPI = SH::RPI;            // rows per load instruction
+  constexpr int ITERS = (ROWS + RPI - 1) / RPI;
+  static_assert(3 * D / 8 <= SH::THREADS, "one conv item per thread");
+  constexpr int ITEMS = 3 * D / 8;        // 8-channel conv items of the head
   static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "row layout");
 
   const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, part = threadIdx.x >> 6;
   const int H = heads;
   const int64_t C = int64_t(H) * 3 * D;
   const int slot = a.slot_table[b];
-  uint16_t *out = a.out + (int64_t(b) * H + h) * D;
+  const int r0 = part * ROWS;
+  uint16_t *out = a.out + (int64_t(b) * H + h) * D + r0;
 
   if (slot <= 0 || slot >= slots) {
-    if (tid < D) out[tid] = 0;
-    if (slot >= slots && err && tid == 0) atomicOr(err, GDN_ERRW_BAD_SLOT);
+    if (lane < ROWS) out[lane] = 0;
+    if (slot >= slots && err && threadIdx.x == 0) atomicOr(err, GDN_ERRW_BAD_SLOT);
     return;
   }
 
@@ -103,11 +117,10 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
   typename SV::raw sraw[ITERS];
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
-    const int g = wave + it * kWaves;
-    const int r = g * RPI + row_in_group;
-    if (g < GROUPS && r < D) {
-      sraw[it] = *reinterpret_cast<const typename SV::raw *>(Sblk + int64_t(r) * D + col0);
-    }
+    const int r = r0 + it * RPI + row_in_group;
+    if (r < r0 + ROWS)
+      sraw[it] = __builtin_nontemporal_load(
+          reinterpret_cast<const typename SV::raw *>(Sblk + int64_t(r) * D + col0));
   }
 
   // ---- snapshot target --------------------------------------------------
@@ -115,58 +128,76 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
   if (a.track_interval > 0 && a.track_slots && a.seq_len_after[b] % a.track_interval == 0) {
     track = a.track_slots[2 * b + (a.next_track_idx[b] & 1)];
     if (track >= slots) {
-      if (err && tid == 0) atomicOr(err, GDN_ERRW_BAD_TRACK_SLOT);
+      if (err && threadIdx.x == 0) atomicOr(err, GDN_ERRW_BAD_TRACK_SLOT);
       track = 0;
     }
   }
 
-  // ---- conv over the head's q, k, v channels -----------------------------
-  __shared__ float sq[D], sk[D], sv[D];
-  __shared__ float red[kWaves];
+  // ---- conv over the head's q, k, v channels, 8 channels per lane --------
+  __shared__ __attribute__((aligned(16))) float sy[3 * D];  // q | k | v of this head
   uint16_t *crow = conv + (int64_t(a.layer) * slots + slot) * kConvRows * C;
   uint16_t *trow = track > 0 ? conv + (int64_t(a.layer) * slots + track) * kConvRows * C : nullptr;
   const uint16_t *xb = a.x + int64_t(b) * C;
-  for (int i = tid; i < 3 * D; i += kThreads) {
-    const int part = i / D, j = i - part * D;
-    const int64_t ch = int64_t(part) * H * D + int64_t(h) * D + j;
-    const uint16_t r0 = crow[ch], r1 = crow[C + ch], r2 = crow[2 * C + ch], xv = xb[ch];
-    const uint2 wv = *reinterpret_cast<const uint2 *>(a.conv_w + ch * 4);
-    float y = __uint_as_float(wv.x << 16) * bf16_to_f32(r0);
-    y = fmaf(__uint_as_float(wv.x & 0xffff0000u), bf16_to_f32(r1), y);
-    y = fmaf(__uint_as_float(wv.y << 16), bf16_to_f32(r2), y);
-    y = fmaf(__uint_as_float(wv.y & 0xffff0000u), bf16_to_f32(xv), y);
-    if (a.flags & GDN_F_CONV_SILU) y = y / (1.f + __expf(-y));
-    (part == 0 ? sq : part == 1 ? sk : sv)[j] = y;
-    crow[ch] = r1;
-    crow[C + ch] = r2;
-    crow[2 * C + ch] = xv;
-    if (trow) {
-      trow[ch] = r1;
-      trow[C + ch] = r2;
-      trow[2 * C + ch] = xv;
+  const int item = threadIdx.x;  // one 8-channel item per thread (ITEMS <= threads)
+  const bool conv_lane = item < ITEMS;
+  const int pt = item / (D / 8), j8 = (item % (D / 8)) * 8;
+  const int64_t ch = int64_t(pt) * H * D + int64_t(h) * D + j8;
+  u32x4 r1v, r2v, xv;
+  if (conv_lane) {
+    const u32x4 r0v = *reinterpret_cast<const u32x4 *>(crow + ch);
+    r1v = *reinterpret_cast<const u32x4 *>(crow + C + ch);
+    r2v = *reinterpret_cast<const u32x4 *>(crow + 2 * C + ch);
+    xv = *reinterpret_cast<const u32x4 *>(xb + ch);
+    const u32x4 *wp = reinterpret_cast<const u32x4 *>(a.conv_w + ch * 4);
+    const u32x4 wv[4] = {wp[0], wp[1], wp[2], wp[3]};  // 4 taps of channels ch .. ch+7
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = (e & 1) ? 16 : 0;
+      auto pick = [&](const u32x4 &v) { return __uint_as_float(((v[e >> 1] >> sh) & 0xffffu) << 16); };
+      const u32x4 &w2 = wv[e >> 1];
+      const int wb = (e & 1) * 2;
+      float y = __uint_as_float(w2[wb] << 16) * pick(r0v);
+      y = fmaf(__uint_as_float(w2[wb] & 0xffff0000u), pick(r1v), y);
+      y = fmaf(__uint_as_float(w2[wb + 1] << 16), pick(r2v), y);
+      y = fmaf(__uint_as_float(w2[wb + 1] & 0xffff0000u), pick(xv), y);
+      if (a.flags & GDN_F_CONV_SILU) y = y / (1.f + __expf(-y));
+      sy[pt * D + j8 + e] = y;
     }
   }
-  __syncthreads();
+  __syncthreads();  // every old conv row has been read; sy is complete
+  if (conv_lane) {
+    *reinterpret_cast<u32x4 *>(crow + ch) = r1v;
+    *reinterpret_cast<u32x4 *>(crow + C + ch) = r2v;
+    *reinterpret_cast<u32x4 *>(crow + 2 * C + ch) = xv;
+    if (trow) {
+      *reinterpret_cast<u32x4 *>(trow + ch) = r1v;
+      *reinterpret_cast<u32x4 *>(trow + C + ch) = r2v;
+      *reinterpret_cast<u32x4 *>(trow + 2 * C + ch) = xv;
+    }
+  }
+  const float *sq = sy, *sk = sy + D, *sv = sy + 2 * D;
 
-  // ---- normalisation and k.q --------------------------------------------
+  // ---- normalisation and k.q (wave reductions) ---------------------------
+  float kinv = 1.f, qinv = 1.f;
   if (a.flags & GDN_F_L2NORM_K) {
-    const float ss = block_sum(tid < D ? sk[tid] * sk[tid] : 0.f, red);
-    const float inv = 1.f / sqrtf(ss + 1e-6f);
-    if (tid < D) sk[tid] *= inv;
+    float ss = 0.f;
+    for (int i = lane; i < D; i += 64) ss = fmaf(sk[i], sk[i], ss);
+    kinv = 1.f / sqrtf(wave_sum(ss) + 1e-6f);
   }
   if (a.flags & GDN_F_L2NORM_Q) {
-    const float ss = block_sum(tid < D ? sq[tid] * sq[tid] : 0.f, red);
-    const float inv = 1.f / sqrtf(ss + 1e-6f);
-    if (tid < D) sq[tid] *= inv;
+    float ss = 0.f;
+    for (int i = lane; i < D; i += 64) ss = fmaf(sq[i], sq[i], ss);
+    qinv = 1.f / sqrtf(wave_sum(ss) + 1e-6f);
   }
-  __syncthreads();
-  const float kq = block_sum(tid < D ? sk[tid] * sq[tid] : 0.f, red);
+  float kq = 0.f;
+  for (int i = lane; i < D; i += 64) kq = fmaf(sk[i] * kinv, sq[i] * qinv, kq);
+  kq = wave_sum(kq);
 
   float kk[VEC], qq[VEC], al[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    kk[e] = sk[col0 + e];
-    qq[e] = sq[col0 + e];
+    kk[e] = sk[col0 + e] * kinv;
+    qq[e] = sq[col0 + e] * qinv;
   }
   if (kAlphaMode == GDN_ALPHA_PER_CHANNEL) {
     const float *ap = a.alpha + (int64_t(b) * H + h) * D + col0;
@@ -183,44 +214,45 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
   // ---- the state stream --------------------------------------------------
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
-    const int g = wave + it * kWaves;
-    const int r = g * RPI + row_in_group;
-    if (g < GROUPS && r < D) {  // uniform over the LPR lanes of a row
-      float s[VEC];
-      SV::to_f32(sraw[it], s);
-      float pu = 0.f, pq = 0.f;
+    const int r = r0 + it * RPI + row_in_group;
+    const bool on = r < r0 + ROWS;  // uniform over the LPR lanes of a row
+    float s[VEC];
+    SV::to_f32(sraw[it], s);
+    float pu = 0.f, pq = 0.f;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        s[e] *= al[e];
-        pu = fmaf(s[e], kk[e], pu);
-        pq = fmaf(s[e], qq[e], pq);
-      }
+    for (int e = 0; e < VEC; ++e) {
+      s[e] *= al[e];
+      pu = fmaf(s[e], kk[e], pu);
+      pq = fmaf(s[e], qq[e], pq);
+    }
 #pragma unroll
-      for (int off = LPR / 2; off > 0; off >>= 1) {
-        pu += __shfl_xor(pu, off, 64);
-        pq += __shfl_xor(pq, off, 64);
-      }
+    for (int off = LPR / 2; off > 0; off >>= 1) {
+      pu += __shfl_xor(pu, off, 64);
+      pq += __shfl_xor(pq, off, 64);
+    }
+    if (on) {
       const float d = beta * (sv[r] - pu);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) s[e] = fmaf(d, kk[e], s[e]);
       const typename SV::raw w = SV::from_f32(s);
-      *reinterpret_cast<typename SV::raw *>(Sblk + int64_t(r) * D + col0) = w;
-      if (Tblk) *reinterpret_cast<typename SV::raw *>(Tblk + int64_t(r) * D + col0) = w;
-      if ((lane % LPR) == 0) out[r] = f32_to_bf16(a.scale * fmaf(d, kq, pq));
+      __builtin_nontemporal_store(w, reinterpret_cast<typename SV::raw *>(Sblk + int64_t(r) * D + col0));
+      if (Tblk)
+        __builtin_nontemporal_store(w, reinterpret_cast<typename SV::raw *>(Tblk + int64_t(r) * D + col0));
+      if ((lane % LPR) == 0) out[r - r0] = f32_to_bf16(a.scale * fmaf(d, kq, pq));
     }
   }
 }
 
 template <int D, typename TS>
 hipError_t launch_d(const gdn_pool *p, const DecodeArgs &a, hipStream_t s) {
+  constexpr int THREADS = DecodeShape<D, TS>::THREADS;
   dim3 grid(p->d.heads, a.batch);
   if (a.alpha_mode == GDN_ALPHA_PER_CHANNEL)
-    hipLaunchKernelGGL((gdn_decode_kernel<D, TS, GDN_ALPHA_PER_CHANNEL>), grid, dim3(kThreads), 0,
-                       s, static_cast<TS *>(p->d.ssm_base),
-                       static_cast<uint16_t *>(p->d.conv_base), p->d.err_word, p->d.slots,
-                       p->d.heads, a);
+    hipLaunchKernelGGL((gdn_decode_kernel<D, TS, GDN_ALPHA_PER_CHANNEL>), grid, dim3(THREADS), 0, s,
+                       static_cast<TS *>(p->d.ssm_base), static_cast<uint16_t *>(p->d.conv_base),
+                       p->d.err_word, p->d.slots, p->d.heads, a);
   else
-    hipLaunchKernelGGL((gdn_decode_kernel<D, TS, GDN_ALPHA_PER_HEAD>), grid, dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((gdn_decode_kernel<D, TS, GDN_ALPHA_PER_HEAD>), grid, dim3(THREADS), 0, s,
                        static_cast<TS *>(p->d.ssm_base), static_cast<uint16_t *>(p->d.conv_base),
                        p->d.err_word, p->d.slots, p->d.heads, a);
   return hipGetLastError();
