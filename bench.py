@@ -114,6 +114,22 @@ def run_headline(torch, gdn, wl, dev, steps, warmup):
                 bytes_per_launch=total_bytes / steps, achieved_gbs=achieved, snapshots=snaps)
 
 
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs, or None
+    if the decode kernel's sources changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gdn_decode_gdn32_b128_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except OSError:
+        return None
+    src = b"".join(open(os.path.join(ROOT, "gated_delta_rule_slot_amd", "csrc", f), "rb").read()
+                   for f in ("decode.hip", "common.hpp"))
+    if hashlib.sha256(src).hexdigest() != rec.get("sources_sha256"):
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def copy_calibration(torch, dev):
     """Achieved bandwidth of a plain 1 GiB device-to-device copy (context for % of peak)."""
     a = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
@@ -282,7 +298,8 @@ def main():
                                "of 512 slots, batch 128, 1 token/request, tracking every 256",
                    "batch": 128, "heads": 32, "head_dim": 128, "pool_slots": 512},
         "roofline": {"bound": "hbm", "achieved": r["achieved_gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": r["achieved_gbs"] / HBM_PEAK_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": r["achieved_gbs"] / HBM_PEAK_GBS,
+                     "traffic": measured_traffic()},
         "kernel_avg_us": r["avg_kernel_s"] * 1e6,
         "bytes_per_launch": r["bytes_per_launch"],
         "cpu_baseline": cpu,
