@@ -14,17 +14,21 @@
 // (a restatement checked against the sequential form by the oracle's tests).
 //
 // Two kernels per window of chunks:
-//   prep  (one workgroup per (request, chunk, head); all chunks in parallel):
-//         conv + key norm, log2 decays, A and M, T, and the chunk's operands
-//         W, U, g.Q, G(63,.)K, M, g_63 written to a workspace record.  Every
-//         contraction here runs on bf16 MFMA in a three-product hi/lo split, so
-//         it carries about 16 mantissa bits and fp32 range.
-//   scan  (one workgroup per (request, head, V-tile); serial over chunks):
-//         Dl = U - W S0^T, O = gQ S0^T + M Dl, S = S Diag(g) + Dl^T K~ with the
-//         same hi/lo bf16 split, the state held in fp32 registers across chunks;
-//         snapshots at boundaries; the live slot written at the end.  The
-//         record stores W, g.Q, K~ and M as pre-split bf16 planes, which the
-//         scan loads straight into MFMA operand registers.
+//   prep  (one 1024-thread workgroup per (request, chunk, head); all chunks in
+//         parallel): conv + norms, log2 decays, A and M, T, and the chunk's
+//         operands -W, U, g.Q, G(63,.)K, M, g_63 written to a workspace record.
+//         Every contraction runs on bf16 MFMA in a three-product hi/lo split,
+//         which carries about 16 mantissa bits and fp32 range.
+//   scan  (one workgroup per (request, head, 16 rows of V); serial over chunks):
+//         wave w keeps the state columns of channels [32w, 32w+32) in fp32
+//         registers, forms its share of W S0^T and (g.Q) S0^T, and one LDS
+//         exchange per chunk completes Dl; every wave then updates its own state
+//         columns and one 16-token block of outputs.  No operand is transposed
+//         on the way: the record is stored in MFMA operand order, with the
+//         32-wide k steps permuted the way two 16x16 accumulator tiles lie in a
+//         wave's registers (see pk below), so accumulators feed the next product
+//         directly, and the next chunk's operands are loaded while the current
+//         one is computed.
 //
 // Chunks are aligned to absolute positions: the first chunk of a request starts
 // at start_len rounded down to a multiple of 64 and is padded at the front
@@ -42,28 +46,43 @@ namespace gdn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
+constexpr int kPrepThreads = 1024;
 constexpr float kMidRange = 60.f;  // max |log2| of a factor on the diagonal fast path
 
+// An MFMA 16x16x32 operand gives lane l the k indices 8*(l/16) + e, e < 8.  Where
+// an operand is built from two 16x16 accumulator tiles (which give lane l the
+// rows 4*(l/16) + j, j < 4), its 32 k values are taken in the order
+//     pk(g, e) = 4g + e (e < 4, first tile),  16 + 4g + (e - 4) (e >= 4, second tile)
+// for g = l/16; both operands of a product use the same order, so the sum over k
+// is unchanged.
+__device__ __forceinline__ constexpr int pk(int g, int e) { return e < 4 ? 4 * g + e : 12 + 4 * g + e; }
+
 // ------------------------------------------------------------ record layout --
+// One record per (request, chunk, head).  A "fragment" is one bf16 plane (hi or
+// lo) of one MFMA operand: 64 lanes x 8 values, 1 KiB, lane-major.
 template <int D>
 struct Rec {
-  // bf16 hi/lo planes (x ~ hi + lo) of the scan's operands, then fp32 arrays
-  static constexpr size_t WH = 0;                          // [64][D]  W
-  static constexpr size_t WL = WH + size_t(64) * D * 2;
-  static constexpr size_t QH = WL + size_t(64) * D * 2;    // [64][D]  g_t q_t
-  static constexpr size_t QL = QH + size_t(64) * D * 2;
-  static constexpr size_t KH = QL + size_t(64) * D * 2;    // [D][64]  G(63,t) k_t, transposed
-  static constexpr size_t KL = KH + size_t(64) * D * 2;
-  static constexpr size_t MH = KL + size_t(64) * D * 2;    // [64][64] M
-  static constexpr size_t ML = MH + size_t(64) * 64 * 2;
-  static constexpr size_t U = ML + size_t(64) * 64 * 2;    // fp32 [64][D]
-  static constexpr size_t GC = U + size_t(64) * D * 4;     // fp32 [D]   g_63
+  static constexpr int KD = D < 32 ? 32 : D;  // channels padded to a k step
+  static constexpr int NKS = KD / 32;         // 32-channel k steps
+  static constexpr int NCB = D / 16;          // 16-wide tiles of channels (and of V)
+  static constexpr size_t FRAG = 1024;
+  // -W   [tb][ks][plane]: rows 16tb + l%16, channels 32ks + pk(l/16, e)
+  static constexpr size_t WF = 0;
+  // g.Q  [tb][ks][plane]: same order
+  static constexpr size_t QF = WF + size_t(4) * NKS * 2 * FRAG;
+  // M    [tb][ks'][plane]: rows 16tb + l%16, tokens 32ks' + pk(l/16, e)
+  static constexpr size_t MF = QF + size_t(4) * NKS * 2 * FRAG;
+  // G(63,t)k_t transposed [cb][ks'][plane]: channel 16cb + l%16, tokens 32ks' + pk(l/16, e)
+  static constexpr size_t KF = MF + size_t(4) * 2 * 2 * FRAG;
+  // U    fp32 [tb][vb][lane][4]: rows 16tb + 4(l/16) + j, column 16vb + l%16
+  static constexpr size_t UF = KF + size_t(NCB) * 2 * 2 * FRAG;
+  // g_63 fp32 [D]
+  static constexpr size_t GC = UF + size_t(4) * NCB * 64 * 16;
   static constexpr size_t BYTES = (GC + size_t(D) * 4 + 255) / 256 * 256;
 };
 
@@ -98,9 +117,6 @@ __device__ __forceinline__ ReqGeom req_geom(const PrefillArgs &a, int b) {
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_f16(const f16x8 &a, const f16x8 &b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
 
 struct Split {
   bf16x8 hi, lo;
@@ -115,6 +131,15 @@ __device__ __forceinline__ Split split8(const float *v) {
   }
   return s;
 }
+__device__ __forceinline__ Split split44(const f32x4 &x, const f32x4 &y) {
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = x[j];
+    v[4 + j] = y[j];
+  }
+  return split8(v);
+}
 // a*b ~ a_hi b_hi + a_hi b_lo + a_lo b_hi (the lo*lo term is ~2^-16 relative)
 __device__ __forceinline__ f32x4 mfma3(const Split &a, const Split &b, f32x4 c) {
   c = mfma_bf16(a.lo, b.hi, c);
@@ -123,59 +148,53 @@ __device__ __forceinline__ f32x4 mfma3(const Split &a, const Split &b, f32x4 c) 
   return c;
 }
 
-__device__ __forceinline__ void split1(float v, __bf16 &hi, __bf16 &lo) {
-  hi = static_cast<__bf16>(v);
-  lo = static_cast<__bf16>(v - static_cast<float>(hi));
-}
-__device__ __forceinline__ bf16x8 neg8(const bf16x8 &v) {
-  u32x4 u = __builtin_bit_cast(u32x4, v);
-  u ^= 0x80008000u;
-  return __builtin_bit_cast(bf16x8, u);
-}
-__device__ __forceinline__ Split load_split(const __bf16 *hi, const __bf16 *lo) {
-  Split s;
-  s.hi = *reinterpret_cast<const bf16x8 *>(hi);
-  s.lo = *reinterpret_cast<const bf16x8 *>(lo);
-  return s;
+__device__ __forceinline__ float bf16_elem(const u32x4 &v, int e) {
+  const uint32_t w = v[e >> 1];
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
-__device__ __forceinline__ void load_bf16x8(const uint16_t *p, float *f) {
-  const u32x4 r = *reinterpret_cast<const u32x4 *>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(r[i] << 16);
-    f[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
-  }
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ void st4(float *p, const f32x4 &v) { *reinterpret_cast<f32x4 *>(p) = v; }
+
+// a fragment pair (hi, lo) of a record
+__device__ __forceinline__ Split frag_load(const char *base, int idx, int lane) {
+  Split s;
+  s.hi = *reinterpret_cast<const bf16x8 *>(base + size_t(2 * idx) * 1024 + lane * 16);
+  s.lo = *reinterpret_cast<const bf16x8 *>(base + size_t(2 * idx + 1) * 1024 + lane * 16);
+  return s;
+}
+__device__ __forceinline__ void frag_store(char *base, int idx, int lane, const Split &s) {
+  *reinterpret_cast<bf16x8 *>(base + size_t(2 * idx) * 1024 + lane * 16) = s.hi;
+  *reinterpret_cast<bf16x8 *>(base + size_t(2 * idx + 1) * 1024 + lane * 16) = s.lo;
 }
 
 // =============================================================== prep kernel ==
 template <int D>
 struct PrepLds {
-  static constexpr int KD = D < 32 ? 32 : D;  // channel extent padded to an MFMA k-step
-  static constexpr int DP = KD + 4;           // fp32 pitch of [t][c] arrays
-  static constexpr int TP = 68;               // fp32 pitch of [c][t] and [t][i] arrays
-  static constexpr int RQ = (64 * DP > KD * TP ? 64 * DP : KD * TP);  // q, later (g.k)^T
-  static constexpr int RK = 64 * DP;                                  // k
-  static constexpr int RL = (64 * DP > 64 * TP ? 64 * DP : 64 * TP);  // log2 decays, later T
-  static constexpr int RV = KD * TP;                                  // v^T
+  static constexpr int KD = D < 32 ? 32 : D;
+  static constexpr int DP = KD + 4;  // fp32 pitch of [t][c] arrays
+  static constexpr int TP = 68;      // fp32 pitch of [v][t] and [t][i] arrays
+  static constexpr int RQ = (64 * DP > 64 * TP ? 64 * DP : 64 * TP);  // q, later T
+  static constexpr int RK = 64 * DP;                                  // k, later g.k
+  static constexpr int RL = 64 * DP;                                  // log2 decays
+  static constexpr int RV = D * TP;                                   // v^T
   static constexpr int RA = 64 * TP;                                  // Diag(b) A
-  static constexpr int RP = 4 * 16 * 17;                              // per-wave 16x16 scratch
-  static constexpr int RTOT = 4 * KD;                                 // block totals of log2 a
+  static constexpr int RP = 3 * 16 * 17;                              // 16x16 scratch per level block
   static constexpr int OQ = 0, OK = OQ + RQ, OL = OK + RK, OV = OL + RL, OA = OV + RV,
-                       OP = OA + RA, OTOT = OP + RP, OB = OTOT + RTOT, TOTAL = OB + 64 + 4;
+                       OP = OA + RA, OTOT = OP + RP, OB = OTOT + 4 * KD, OF = OB + 64, TOTAL = OF + 4;
 };
 
 template <int D, int AMODE>
-__global__ __launch_bounds__(kThreads) void prefill_prep_kernel(KArgs ka) {
+__global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
   using LY = PrepLds<D>;
+  using RC = Rec<D>;
   constexpr int KD = LY::KD, DP = LY::DP, TP = LY::TP;
-  constexpr int G = D / 8;  // 8-channel groups per head part
+  constexpr int NKS = RC::NKS, NCB = RC::NCB;
   __shared__ __attribute__((aligned(16))) float smem[LY::TOTAL];
   float *sQ = smem + LY::OQ, *sK = smem + LY::OK, *sL = smem + LY::OL, *sV = smem + LY::OV;
   float *sA = smem + LY::OA, *sP = smem + LY::OP, *sTot = smem + LY::OTOT, *sB = smem + LY::OB;
-  int *sFlag = reinterpret_cast<int *>(smem + LY::OB + 64);
-  float *sKG = sQ;  // (g . k)^T [KD][TP], after q is consumed
-  float *sT = sL;   // T [64][TP], after the decays are consumed
+  int *sWF = reinterpret_cast<int *>(smem + LY::OF);
+  float *sT = sQ;  // T [64][TP], once q has been consumed
 
   const PrefillArgs &a = ka.a;
   const int H = ka.heads;
@@ -188,263 +207,290 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(KArgs ka) {
   if (!rg.ok || slot <= 0 || slot >= ka.slots || c >= rg.nch) return;
   const bool warm = a.has_initial_state[b] != 0;
   const int64_t C = int64_t(H) * 3 * D;
-  char *rec = ka.ws + ka.carry_bytes + (size_t(b * ka.w + cl) * H + h) * Rec<D>::BYTES;
+  char *rec = ka.ws + ka.carry_bytes + (size_t(b * ka.w + cl) * H + h) * RC::BYTES;
   const int p0 = 64 * c - rg.off;  // request position of local token 0
 
-  // ---- phase 1: zero fills, beta, log2 decays ---------------------------------
-  for (int i = tid; i < 64 * TP; i += kThreads) sA[i] = 0.f;
-  for (int i = tid; i < 64 * DP; i += kThreads) {
-    sQ[i] = 0.f;
-    sK[i] = 0.f;
-  }
-  for (int i = tid; i < KD * TP; i += kThreads) sV[i] = 0.f;
-  if (tid == 0) *sFlag = 0;
-  if (tid >= 192) {
-    const int t = tid - 192;
-    const int pos = p0 + t;
-    sB[t] = (pos >= 0 && pos < rg.len) ? a.beta[int64_t(rg.bos + pos) * H + h] : 0.f;
-  }
-  __syncthreads();
-  if (tid < KD) {
-    const int ch = tid;
-    float acc = 0.f;
-#pragma unroll 4
-    for (int t = 0; t < 64; ++t) {
-      if ((t & 15) == 0) acc = 0.f;
-      const int pos = p0 + t;
-      float la = 0.f;
-      if (ch < D && pos >= 0 && pos < rg.len) {
-        const float av = AMODE == GDN_ALPHA_PER_CHANNEL
-                             ? a.alpha[(int64_t(rg.bos + pos) * H + h) * D + ch]
-                             : a.alpha[int64_t(rg.bos + pos) * H + h];
-        la = fmaxf(__log2f(av), -512.f);  // a == 0 behaves as a full decay
-      }
-      acc += la;
-      sL[t * DP + ch] = acc;  // cumulative inside the 16-token block
-      if ((t & 15) == 15) sTot[(t >> 4) * KD + ch] = acc;
+  // ---- phase 1: causal conv + norms (waves 0..11), log2 decays + beta (12..15) ----
+  if constexpr (KD != D) {  // channel padding of q and k
+    for (int i = tid; i < 64 * (KD - D); i += kPrepThreads) {
+      const int t = i / (KD - D), cc = D + i % (KD - D);
+      sQ[t * DP + cc] = 0.f;
+      sK[t * DP + cc] = 0.f;
     }
-    int flags = 0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float lr = sL[(16 * m + 7) * DP + ch];
-      const float up = sL[(16 * m) * DP + ch] - lr, dn = lr - sL[(16 * m + 15) * DP + ch];
-      if (fmaxf(up, dn) > kMidRange) flags |= 1 << m;
-    }
-    if (flags) atomicOr(sFlag, flags);
   }
-
-  // ---- phase 2: causal conv, key (and query) norm -----------------------------
-  {
+  constexpr int G = D / 8;                // 8-channel groups per head part
+  constexpr int R = G >= 8 ? G / 4 : 1;   // consecutive tokens per conv item
+  constexpr int NR = 64 / R;
+  constexpr int CONV_ITEMS = 3 * NR * G;  // 768, or 384 when D = 16
+  static_assert(CONV_ITEMS <= 768 && CONV_ITEMS % 64 == 0, "conv items must fill waves 0..11");
+  if (tid < CONV_ITEMS) {
+    const int g = tid % G, run = (tid / G) % NR, part = tid / (G * NR);
+    const int t0 = run * R;
+    const int64_t ch0 = int64_t(part) * H * D + int64_t(h) * D + 8 * g;
     const uint16_t *crow = ka.conv + (int64_t(a.layer) * ka.slots + slot) * kConvRows * C;
-    constexpr int ITEMS = 64 * G;
-    constexpr int ITERS = (ITEMS + kThreads - 1) / kThreads;
-#pragma unroll 1
-    for (int part = 0; part < 3; ++part) {
-#pragma unroll 1
-      for (int it = 0; it < ITERS; ++it) {
-        const int item = it * kThreads + tid;
-        const bool active = item < ITEMS;
-        const int t = active ? item / G : 0, g = active ? item % G : 0;
-        const int pos = p0 + t;
-        const bool valid = active && pos >= 0 && pos < rg.len;
-        const int64_t ch0 = int64_t(part) * H * D + int64_t(h) * D + 8 * g;
-        float y[8];
+    u32x4 wr[4], xr[R + 3];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = 0.f;
-        if (valid) {
-          float wv[8][4];
+    for (int i = 0; i < 4; ++i) wr[i] = *reinterpret_cast<const u32x4 *>(a.conv_w + (ch0 + 2 * i) * 4);
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            float tmp[8];
-            load_bf16x8(a.conv_w + (ch0 + e) * 4, tmp);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              wv[e][j] = tmp[j];
-              wv[e + 1][j] = tmp[4 + j];
-            }
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {  // tap j multiplies position pos - 3 + j
-            const int q = pos - 3 + j;
-            float xv[8];
-            if (q >= 0) {
-              load_bf16x8(a.x + int64_t(rg.bos + q) * C + ch0, xv);
-            } else if (warm) {
-              load_bf16x8(crow + int64_t(3 + q) * C + ch0, xv);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) xv[e] = 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = j == 0 ? wv[e][0] * xv[e] : fmaf(wv[e][j], xv[e], y[e]);
-          }
-          if (a.flags & GDN_F_CONV_SILU) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = y[e] / (1.f + __expf(-y[e]));
-          }
-        }
-        const bool norm = part == 1 ? (a.flags & GDN_F_L2NORM_K) : part == 0 ? (a.flags & GDN_F_L2NORM_Q) : false;
-        if (norm) {  // uniform branch: every lane takes part in the shuffles
-          float ss = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
-#pragma unroll
-          for (int off = G / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-          const float inv = 1.f / sqrtf(ss + 1e-6f);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] *= inv;
-        }
-        if (active) {
-          if (part == 2) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sV[(8 * g + e) * TP + t] = y[e];
-          } else {
-            float *dst = (part == 0 ? sQ : sK) + t * DP + 8 * g;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dst[e] = y[e];
-          }
-        }
-      }
+    for (int r = 0; r < R + 3; ++r) {  // positions p0 + t0 - 3 + r
+      const int q = p0 + t0 - 3 + r;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (q >= 0 && q < rg.len)
+        v = *reinterpret_cast<const u32x4 *>(a.x + int64_t(rg.bos + q) * C + ch0);
+      else if (q < 0 && q >= -3 && warm)
+        v = *reinterpret_cast<const u32x4 *>(crow + int64_t(3 + q) * C + ch0);
+      xr[r] = v;
     }
-  }
-  __syncthreads();
-
-  // ---- phase 3: A and M tiles ---------------------------------------------------
-  const int flags = *sFlag;
-  {
-    __bf16 *recMh = reinterpret_cast<__bf16 *>(rec + Rec<D>::MH);
-    __bf16 *recMl = reinterpret_cast<__bf16 *>(rec + Rec<D>::ML);
-#pragma unroll 1
-    for (int pi = wave; pi < 10; pi += 4) {
-      // pair index -> (m, n), n <= m, in the order (0,0) (1,0) (1,1) (2,0) ...
-      const int m = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
-      const int n = pi - m * (m + 1) / 2;
-      const bool diag = m == n;
-      const int t = 16 * m + r16;  // A-operand row
-      const int i = 16 * n + r16;  // B-operand column
-      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
-      if (!(diag && ((flags >> m) & 1))) {
-        const int r = 16 * m + 7;
-#pragma unroll 1
-        for (int ks = 0; ks < KD / 32; ++ks) {
-          const int c0 = ks * 32 + 8 * g4;
-          float rv[8], lk[8], lq[8];
+    const bool silu = (a.flags & GDN_F_CONV_SILU) != 0;
+    const bool norm = part == 0 ? (a.flags & GDN_F_L2NORM_Q) != 0 : part == 1 ? (a.flags & GDN_F_L2NORM_K) != 0 : false;
+    float y[R][8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int cc = c0 + e;
-            float rexp, lexp;
-            if (diag) {
-              const float lr = sL[r * DP + cc];
-              rexp = lr - sL[i * DP + cc];
-              lexp = sL[t * DP + cc] - lr;
-            } else {
-              float between = 0.f;
-              for (int kb = n + 1; kb < m; ++kb) between += sTot[kb * KD + cc];
-              rexp = sTot[n * KD + cc] - sL[i * DP + cc];
-              lexp = sL[t * DP + cc] + between;
-            }
-            rv[e] = sK[i * DP + cc] * exp2f(rexp);
-            const float f = exp2f(lexp);
-            lk[e] = sK[t * DP + cc] * f;
-            lq[e] = sQ[t * DP + cc] * f;
-          }
-          const Split R = split8(rv), LK = split8(lk), LQ = split8(lq);
-          accA = mfma3(LK, R, accA);
-          accM = mfma3(LQ, R, accM);
-        }
-      } else {
-        // exact per-pair evaluation for a diagonal block with extreme decays
-        const int ii = 16 * n + r16;
-#pragma unroll 1
-        for (int j = 0; j < 4; ++j) {
-          const int tt = 16 * m + 4 * g4 + j;
-          float sa = 0.f, sm = 0.f;
-          if (ii <= tt) {
-            for (int cc = 0; cc < KD; ++cc) {
-              const float f = exp2f(sL[tt * DP + cc] - sL[ii * DP + cc]) * sK[ii * DP + cc];
-              sa = fmaf(sK[tt * DP + cc], f, sa);
-              sm = fmaf(sQ[tt * DP + cc], f, sm);
-            }
-          }
-          accA[j] = sa;
-          accM[j] = sm;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tt = 16 * m + 4 * g4 + j, ii = 16 * n + r16;
-        const float av = (!diag || ii < tt) ? accA[j] : 0.f;
-        const float mv = (!diag || ii <= tt) ? accM[j] : 0.f;
-        sA[tt * TP + ii] = sB[tt] * av;  // Diag(b) A
-        split1(mv, recMh[tt * 64 + ii], recMl[tt * 64 + ii]);
-      }
-    }
-    // upper 16x16 tiles of M are zero
-    for (int ui = wave; ui < 6; ui += 4) {
-      // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-      const int um = ui < 3 ? 0 : ui < 5 ? 1 : 2;
-      const int un = ui < 3 ? ui + 1 : ui < 5 ? ui - 1 : 3;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int o = (16 * um + 4 * g4 + j) * 64 + 16 * un + r16;
-        recMh[o] = static_cast<__bf16>(0.f);
-        recMl[o] = static_cast<__bf16>(0.f);
-      }
-    }
-  }
-
-  // ---- phase 4: operands for the scan: g.Q, G(63,.)K (transposed), g_63 -------
-  {
-    __bf16 *recQh = reinterpret_cast<__bf16 *>(rec + Rec<D>::QH);
-    __bf16 *recQl = reinterpret_cast<__bf16 *>(rec + Rec<D>::QL);
-    __bf16 *recKh = reinterpret_cast<__bf16 *>(rec + Rec<D>::KH);
-    __bf16 *recKl = reinterpret_cast<__bf16 *>(rec + Rec<D>::KL);
-    float *recGC = reinterpret_cast<float *>(rec + Rec<D>::GC);
-    for (int it = tid; it < 64 * G; it += kThreads) {
-      const int t = it / G, cg = (it % G) * 8, m = t >> 4;
-      float v[8];
+    for (int r = 0; r < R; ++r) {
+      const int pos = p0 + t0 + r;
+      const bool valid = pos >= 0 && pos < rg.len;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float pre = 0.f;
-        for (int kb = 0; kb < m; ++kb) pre += sTot[kb * KD + cg + e];
-        v[e] = sQ[t * DP + cg + e] * exp2f(pre + sL[t * DP + cg + e]);
-      }
-      const Split sp = split8(v);
-      *reinterpret_cast<bf16x8 *>(recQh + t * D + cg) = sp.hi;
-      *reinterpret_cast<bf16x8 *>(recQl + t * D + cg) = sp.lo;
-    }
-    for (int it = tid; it < D * 8; it += kThreads) {
-      const int ch = it / 8, t0 = (it % 8) * 8, m = t0 >> 4;
-      float post = sTot[m * KD + ch];
-      for (int kb = m + 1; kb < 4; ++kb) post += sTot[kb * KD + ch];
-      float v[8];
+        // tap j multiplies position pos - 3 + j
+        float acc = bf16_elem(wr[e >> 1], 4 * (e & 1)) * bf16_elem(xr[r], e);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sK[(t0 + e) * DP + ch] * exp2f(post - sL[(t0 + e) * DP + ch]);
-      const Split sp = split8(v);
-      *reinterpret_cast<bf16x8 *>(recKh + ch * 64 + t0) = sp.hi;
-      *reinterpret_cast<bf16x8 *>(recKl + ch * 64 + t0) = sp.lo;
+        for (int j = 1; j < 4; ++j) acc = fmaf(bf16_elem(wr[e >> 1], 4 * (e & 1) + j), bf16_elem(xr[r + j], e), acc);
+        if (silu) acc = acc / (1.f + __expf(-acc));
+        y[r][e] = valid ? acc : 0.f;
+      }
+      if (norm) {  // wave-uniform: every lane takes part in the shuffles
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(y[r][e], y[r][e], ss);
+#pragma unroll
+        for (int off = G / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        const float inv = 1.f / sqrtf(ss + 1e-6f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[r][e] *= inv;
+      }
     }
-    for (int ch = tid; ch < D; ch += kThreads) {
-      float s = 0.f;
-      for (int kb = 0; kb < 4; ++kb) s += sTot[kb * KD + ch];
-      recGC[ch] = exp2f(s);
+    if (part == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float *dst = sV + (8 * g + e) * TP + t0;
+        if constexpr (R == 4) {
+          st4(dst, f32x4{y[0][e], y[1][e], y[2][e], y[3][e]});
+        } else {
+#pragma unroll
+          for (int r = 0; r < R; ++r) dst[r] = y[r][e];
+        }
+      }
+    } else {
+      float *base = part == 0 ? sQ : sK;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        st4(base + (t0 + r) * DP + 8 * g, f32x4{y[r][0], y[r][1], y[r][2], y[r][3]});
+        st4(base + (t0 + r) * DP + 8 * g + 4, f32x4{y[r][4], y[r][5], y[r][6], y[r][7]});
+      }
     }
-  }
-  __syncthreads();
-  // (g . k)^T into the q region
-  for (int it = tid; it < KD * 64; it += kThreads) {
-    const int ch = it / 64, t = it % 64, m = t >> 4;
-    float pre = 0.f;
-    for (int kb = 0; kb < m; ++kb) pre += sTot[kb * KD + ch];
-    sKG[ch * TP + t] = sK[t * DP + ch] * exp2f(pre + sL[t * DP + ch]);
+  } else if (wave >= 12) {
+    // wave 12 + m handles token block m; lane = (channel octet co, token quad tqb)
+    constexpr int NCO = KD / 8;
+    const int m = wave - 12, co = lane & 15, tqb = lane >> 4;
+    const bool act = co < NCO, chv = act && 8 * co < D;
+    if (wave == 12) {
+      const int pos = p0 + lane;
+      sB[lane] = (pos >= 0 && pos < rg.len) ? a.beta[int64_t(rg.bos + pos) * H + h] : 0.f;
+    }
+    float cum[4][8];
+#pragma unroll
+    for (int tok = 0; tok < 4; ++tok) {
+      const int pos = p0 + 16 * m + 4 * tqb + tok;
+      const bool valid = chv && pos >= 0 && pos < rg.len;
+      float av[8];
+      if (AMODE == GDN_ALPHA_PER_CHANNEL) {
+        f32x4 u0 = {1.f, 1.f, 1.f, 1.f}, u1 = u0;
+        if (valid) {
+          const float *ap = a.alpha + (int64_t(rg.bos + pos) * H + h) * D + 8 * co;
+          u0 = ld4(ap);
+          u1 = ld4(ap + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          av[j] = u0[j];
+          av[4 + j] = u1[j];
+        }
+      } else {
+        const float s = valid ? a.alpha[int64_t(rg.bos + pos) * H + h] : 1.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[e] = s;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float la = valid ? fmaxf(__log2f(av[e]), -512.f) : 0.f;  // a == 0: full decay
+        cum[tok][e] = tok == 0 ? la : cum[tok - 1][e] + la;
+      }
+    }
+    // cumulative inside the 16-token block: add the sums of the lower token quads
+    bool big = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float tot = cum[3][e];
+      const float v0 = __shfl(tot, co, 64), v1 = __shfl(tot, co + 16, 64), v2 = __shfl(tot, co + 32, 64);
+      const float off = tqb == 0 ? 0.f : tqb == 1 ? v0 : tqb == 2 ? v0 + v1 : (v0 + v1) + v2;
+#pragma unroll
+      for (int tok = 0; tok < 4; ++tok) cum[tok][e] += off;
+      const float l0 = __shfl(cum[0][e], co, 64), l7 = __shfl(cum[3][e], co + 16, 64),
+                  l15 = __shfl(cum[3][e], co + 48, 64);
+      big = big || (act && fmaxf(l0 - l7, l7 - l15) > kMidRange);
+    }
+    const bool any_big = __ballot(big) != 0;
+    if (lane == 0) sWF[m] = any_big ? 1 : 0;
+    if (act) {
+#pragma unroll
+      for (int tok = 0; tok < 4; ++tok) {
+        const int t = 16 * m + 4 * tqb + tok;
+        st4(sL + t * DP + 8 * co, f32x4{cum[tok][0], cum[tok][1], cum[tok][2], cum[tok][3]});
+        st4(sL + t * DP + 8 * co + 4, f32x4{cum[tok][4], cum[tok][5], cum[tok][6], cum[tok][7]});
+      }
+      if (tqb == 3) {
+        st4(sTot + m * KD + 8 * co, f32x4{cum[3][0], cum[3][1], cum[3][2], cum[3][3]});
+        st4(sTot + m * KD + 8 * co + 4, f32x4{cum[3][4], cum[3][5], cum[3][6], cum[3][7]});
+      }
+    }
   }
   __syncthreads();
 
-  // ---- phase 5: T = (I + Diag(b) A)^-1, blockwise -------------------------------
-  for (int i = tid; i < 64 * TP; i += kThreads) sT[i] = 0.f;
+  if (wave < 10) {
+    // ---- phase 2a: A^T and M^T tiles of pair (m, n), n <= m (waves 0..9) ----------
+    const int flags = sWF[0] | (sWF[1] << 1) | (sWF[2] << 2) | (sWF[3] << 3);
+    const int pi = wave;  // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
+    const int m = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
+    const int n = pi - m * (m + 1) / 2;
+    const bool diag = m == n;
+    const int i = 16 * n + r16;  // rows of the first operand (keys k_i)
+    const int t = 16 * m + r16;  // rows of the second operand (k_t, q_t)
+    f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+    if (!(diag && ((flags >> m) & 1))) {
+      const int r = 16 * m + 7;
+#pragma unroll 1
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int c0 = ks * 32 + 8 * g4;
+        float rv[8], lk[8], lq[8];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int cc = c0 + 4 * hf;
+          const f32x4 ki = ld4(sK + i * DP + cc), li = ld4(sL + i * DP + cc);
+          const f32x4 kt = ld4(sK + t * DP + cc), qt = ld4(sQ + t * DP + cc), lt = ld4(sL + t * DP + cc);
+          f32x4 rexp, lexp;
+          if (diag) {
+            const f32x4 lr = ld4(sL + r * DP + cc);
+            rexp = lr - li;
+            lexp = lt - lr;
+          } else {
+            f32x4 between = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = n + 1; kb < m; ++kb) between += ld4(sTot + kb * KD + cc);
+            rexp = ld4(sTot + n * KD + cc) - li;
+            lexp = lt + between;
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            rv[4 * hf + j] = ki[j] * exp2f(rexp[j]);
+            const float f = exp2f(lexp[j]);
+            lk[4 * hf + j] = kt[j] * f;
+            lq[4 * hf + j] = qt[j] * f;
+          }
+        }
+        const Split Rs = split8(rv), LK = split8(lk), LQ = split8(lq);
+        accA = mfma3(Rs, LK, accA);
+        accM = mfma3(Rs, LQ, accM);
+      }
+    } else {
+      // exact per-pair evaluation for a diagonal block with extreme decays
+#pragma unroll 1
+      for (int j = 0; j < 4; ++j) {
+        const int ii = 16 * n + 4 * g4 + j;
+        float sa = 0.f, sm = 0.f;
+        if (ii <= t) {
+          for (int cc = 0; cc < KD; ++cc) {
+            const float f = exp2f(sL[t * DP + cc] - sL[ii * DP + cc]) * sK[ii * DP + cc];
+            sa = fmaf(sK[t * DP + cc], f, sa);
+            sm = fmaf(sQ[t * DP + cc], f, sm);
+          }
+        }
+        accA[j] = sa;
+        accM[j] = sm;
+      }
+    }
+    // lane (t, g4) holds A[t][16n + 4g4 + j] and M[t][16n + 4g4 + j]
+    const float bt = sB[t];
+    f32x4 av;
+    float mv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ii = 16 * n + 4 * g4 + j;
+      av[j] = (!diag || ii < t) ? bt * accA[j] : 0.f;  // Diag(b) A
+      mv[j] = (!diag || ii <= t) ? accM[j] : 0.f;
+    }
+    st4(sA + t * TP + 16 * n + 4 * g4, av);
+    bf16x4 mh, ml;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const __bf16 hv = static_cast<__bf16>(mv[j]);
+      mh[j] = hv;
+      ml[j] = static_cast<__bf16>(mv[j] - static_cast<float>(hv));
+    }
+    char *mf = rec + RC::MF + size_t(2 * (2 * m + (n >> 1))) * 1024 + lane * 16 + (n & 1) * 8;
+    *reinterpret_cast<bf16x4 *>(mf) = mh;
+    *reinterpret_cast<bf16x4 *>(mf + 1024) = ml;
+    if (diag && !(m & 1)) {  // tile (m, m+1) above the diagonal is zero
+      const bf16x4 z = {static_cast<__bf16>(0.f), static_cast<__bf16>(0.f), static_cast<__bf16>(0.f),
+                        static_cast<__bf16>(0.f)};
+      *reinterpret_cast<bf16x4 *>(mf + 8) = z;
+      *reinterpret_cast<bf16x4 *>(mf + 1024 + 8) = z;
+    }
+  } else {
+    // ---- phase 2b: g.Q, G(63,.)K and g_63 to the record (waves 10..15) -----------
+    const int rel = tid - 640;
+    for (int it = rel; it < 4 * NKS * 64; it += 384) {
+      const int ln = it & 63, tb = (it >> 6) & 3, ks = it >> 8;
+      const int t = 16 * tb + (ln & 15), g = ln >> 4;
+      float v[8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int cc = 32 * ks + 16 * hf + 4 * g;  // channels 32ks + pk(g, 4hf + j)
+        f32x4 pre = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < tb; ++kb) pre += ld4(sTot + kb * KD + cc);
+        const f32x4 q4 = ld4(sQ + t * DP + cc), l4 = ld4(sL + t * DP + cc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * hf + j] = q4[j] * exp2f(pre[j] + l4[j]);
+      }
+      frag_store(rec + RC::QF, tb * NKS + ks, ln, split8(v));
+    }
+    for (int it = rel; it < NCB * 2 * 64; it += 384) {
+      const int ln = it & 63, ksp = (it >> 6) & 1, cb = it >> 7;
+      const int cc = 16 * cb + (ln & 15), g = ln >> 4;
+      float v[8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int tbk = 2 * ksp + hf;  // tokens 32ksp + pk(g, 4hf + j) lie in block tbk
+        float post = 0.f;
+        for (int kb = tbk; kb < 4; ++kb) post += sTot[kb * KD + cc];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tt = 16 * tbk + 4 * g + j;
+          v[4 * hf + j] = sK[tt * DP + cc] * exp2f(post - sL[tt * DP + cc]);
+        }
+      }
+      frag_store(rec + RC::KF, cb * 2 + ksp, ln, split8(v));
+    }
+    float *recGC = reinterpret_cast<float *>(rec + RC::GC);
+    for (int cc = rel; cc < D; cc += 384) {
+      float s = 0.f;
+      for (int kb = 0; kb < 4; ++kb) s += sTot[kb * KD + cc];
+      recGC[cc] = exp2f(s);
+    }
+  }
   __syncthreads();
-  if (lane < 16) {  // diagonal blocks: wave m inverts block m, lane j owns column j
-    const int m = wave, j = lane;
+
+  // ---- phase 3: diagonal blocks of T (wave 0) while the others form g.k in place ---
+  if (wave == 0) {
+    // lane (m, j): column j of the inverse of the unit lower-triangular block m
+    const int m = lane >> 4, j = lane & 15;
     float x[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -454,11 +500,28 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(KArgs ka) {
       x[t] = v;
       sT[(16 * m + t) * TP + 16 * m + j] = v;
     }
+  } else {
+    const int rel = tid - 64;
+    // upper tiles (0,1) and (2,3) of T are read by the U/W products: zero them
+    for (int i = rel; i < 512; i += kPrepThreads - 64) {
+      const int mb = 2 * (i >> 8), rr = (i >> 4) & 15, cc = i & 15;
+      sT[(16 * mb + rr) * TP + 16 * (mb + 1) + cc] = 0.f;
+    }
+    for (int i = rel; i < 64 * KD / 4; i += kPrepThreads - 64) {
+      const int t = i / (KD / 4), cc = 4 * (i % (KD / 4)), m = t >> 4;
+      f32x4 pre = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < m; ++kb) pre += ld4(sTot + kb * KD + cc);
+      f32x4 k4 = ld4(sK + t * DP + cc);
+      const f32x4 l4 = ld4(sL + t * DP + cc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k4[j] *= exp2f(pre[j] + l4[j]);
+      st4(sK + t * DP + cc, k4);
+    }
   }
   __syncthreads();
+  // off-diagonal blocks: T_mn = -T_mm sum_{k=n}^{m-1} (Diag(b)A)_mk T_kn, n = m - d
 #pragma unroll 1
   for (int d = 1; d < 4; ++d) {
-    // T_mn = -T_mm sum_{k=n}^{m-1} (Diag(b)A)_mk T_kn,  n = m - d, one wave per block
     const bool act = wave < 4 - d;
     const int m = wave + d, n = wave;
     const int rr = lane >> 2, cc = 4 * (lane & 3);
@@ -487,88 +550,113 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(KArgs ka) {
     __syncthreads();
   }
 
-  // ---- phase 6: U = T' V and W = T' (g.K), T' = T Diag(b) -----------------------
+  // ---- phase 4: U = T' V and -W^T = -(g.K)^T T'^T, T' = T Diag(b) ---------------
   {
-    float *recU = reinterpret_cast<float *>(rec + Rec<D>::U);
-    __bf16 *recWh = reinterpret_cast<__bf16 *>(rec + Rec<D>::WH);
-    __bf16 *recWl = reinterpret_cast<__bf16 *>(rec + Rec<D>::WL);
-    const int tb = wave;                 // 16-row block of tokens
-    const int nks = tb < 2 ? 1 : 2;      // T' is lower triangular
-    Split Af[2];
+    const int tb = wave & 3, qq = wave >> 2;
+    const int nks = tb < 2 ? 1 : 2;  // T' is lower triangular
+    const int t = 16 * tb + r16;
+    Split TF[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       if (ks < nks) {
         float v[8];
-        const int t = 16 * tb + r16, i0 = 32 * ks + 8 * g4;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = sT[t * TP + i0 + e] * sB[i0 + e];
-        Af[ks] = split8(v);
+        for (int hf = 0; hf < 2; ++hf) {
+          const int i0 = 32 * ks + 16 * hf + 4 * g4;  // tokens 32ks + pk(g4, 4hf + j)
+          const f32x4 tv = ld4(sT + t * TP + i0), bv = ld4(sB + i0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[4 * hf + j] = tv[j] * bv[j];
+        }
+        TF[ks] = split8(v);
       }
     }
 #pragma unroll 1
-    for (int which = 0; which < 2; ++which) {
-      const float *src = which == 0 ? sV : sKG;
+    for (int vb = qq; vb < NCB; vb += 4) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (ks < nks) {
+          float v[8];
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const f32x4 x4 = ld4(sV + (16 * vb + r16) * TP + 32 * ks + 16 * hf + 4 * g4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * hf + j] = x4[j];
+          }
+          acc = mfma3(TF[ks], split8(v), acc);
+        }
+      }
+      *reinterpret_cast<f32x4 *>(rec + RC::UF + size_t(tb * NCB + vb) * 1024 + lane * 16) = acc;
+    }
 #pragma unroll 1
-      for (int vb = 0; vb < D / 16; ++vb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ksc = qq; ksc < NKS; ksc += 4) {
+      f32x4 acc2[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int cc = 16 * (2 * ksc + hh) + r16;
+        acc2[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (ks < nks) {
             float v[8];
-            const int col = 16 * vb + r16, i0 = 32 * ks + 8 * g4;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = src[col * TP + i0 + e];
-            acc = mfma3(Af[ks], split8(v), acc);
+            for (int e = 0; e < 8; ++e) v[e] = sK[(32 * ks + pk(g4, e)) * DP + cc];
+            acc2[hh] = mfma3(split8(v), TF[ks], acc2[hh]);
           }
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = 16 * tb + 4 * g4 + j, col = 16 * vb + r16;
-          if (which == 0) recU[t * D + col] = acc[j];
-          else split1(acc[j], recWh[t * D + col], recWl[t * D + col]);
-        }
       }
+      // lane (t, g4) holds W[16tb + r16][32ksc + pk(g4, e)]; the record keeps -W
+      float w[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[j] = -acc2[0][j];
+        w[4 + j] = -acc2[1][j];
+      }
+      frag_store(rec + RC::WF, tb * NKS + ksc, lane, split8(w));
     }
   }
 }
 
 // =============================================================== scan kernel ==
-template <int D, int VTR>
-struct ScanLds {
-  static constexpr int KD = D < 32 ? 32 : D;
-  static constexpr int KP = KD + 8;  // bf16 pitch of [v][c] rows (16-byte rows, +4 banks)
-  static constexpr int TP = 72;      // bf16 pitch of [v][t] rows
-  static constexpr int OSH = 0, OSL = OSH + VTR * KP, ODH = OSL + VTR * KP, ODL = ODH + VTR * TP,
-                       TOTAL = ODL + VTR * TP;
-};
-
 template <typename TS>
-__device__ __forceinline__ float load_state(const TS *p);
+__device__ __forceinline__ f32x4 load_state4(const TS *p);
 template <>
-__device__ __forceinline__ float load_state<float>(const float *p) { return *p; }
+__device__ __forceinline__ f32x4 load_state4<float>(const float *p) { return ld4(p); }
 template <>
-__device__ __forceinline__ float load_state<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ f32x4 load_state4<uint16_t>(const uint16_t *p) {
+  const u32x2 u = *reinterpret_cast<const u32x2 *>(p);
+  return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+               __uint_as_float(u[1] & 0xffff0000u)};
+}
+__device__ __forceinline__ void store_state4(float *p, const f32x4 &v) { st4(p, v); }
+__device__ __forceinline__ void store_state4(uint16_t *p, const f32x4 &v) {
+  u32x2 u;
+  u[0] = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+  u[1] = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+  *reinterpret_cast<u32x2 *>(p) = u;
+}
 __device__ __forceinline__ void store_state(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_state(uint16_t *p, float v) { *p = f32_to_bf16(v); }
 
-template <int D, int VTR, typename TS>
-__global__ __launch_bounds__(kThreads) void prefill_scan_kernel(KArgs ka) {
-  using LY = ScanLds<D, VTR>;
-  constexpr int KD = LY::KD, KP = LY::KP, TP = LY::TP;
-  constexpr int NVB = VTR / 16, NCB = D / 16;
-  constexpr int NTS = NVB * NCB;                  // 16x16 state tiles of this V-tile
-  constexpr int MAXT = (NTS + 3) / 4;             // per wave
-  __shared__ __attribute__((aligned(16))) __bf16 smem[LY::TOTAL];
-  __bf16 *sSh = smem + LY::OSH, *sSl = smem + LY::OSL;  // S0 [v][c] hi/lo
-  __bf16 *sDh = smem + LY::ODH, *sDl = smem + LY::ODL;  // Dl^T [v][t] hi/lo
+template <int D, typename TS>
+__global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs ka) {
+  using RC = Rec<D>;
+  constexpr int NW = RC::NKS, NT = 64 * NW, NCB = RC::NCB;
+  constexpr int TBW = 4 / NW;  // 16-token output blocks per wave
+  // per-wave partial products over the wave's channels: [buffer][wave][tb][Dl | O][lane]
+  __shared__ f32x4 sPart[2][NW][4][2][64];
 
   const PrefillArgs &a = ka.a;
-  const int H = ka.heads;
-  const int VT = ka.vt_count;
-  const int b = blockIdx.x / VT, vt = blockIdx.x % VT, h = blockIdx.y;
+  const int H = ka.heads, VT = ka.vt_count;
+  // consecutive workgroups go to different XCDs; give each XCD a contiguous range
+  // of (request, head, V-tile) ids so that the V-tiles of one head share an L2
+  const int nblk = gridDim.x, lin = blockIdx.x;
+  const int qn = nblk / 8, rn = nblk % 8, xcd = lin % 8;
+  const int id = xcd * qn + min(xcd, rn) + lin / 8;
+  const int bh = id / VT, vt = id % VT, b = bh / H, h = bh % H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int v0 = vt * VTR;
+  const int v0 = 16 * vt;
 
   const ReqGeom rg = req_geom(a, b);
   if (!rg.ok) {
@@ -581,10 +669,9 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(KArgs ka) {
     if (slot >= ka.slots && ka.err && ka.c0 == 0 && vt == 0 && h == 0 && tid == 0)
       atomicOr(ka.err, GDN_ERRW_BAD_SLOT);
     for (int c = ka.c0; c < cend; ++c)
-      for (int i = tid; i < 64 * VTR; i += kThreads) {
-        const int pos = 64 * c - rg.off + i / VTR;
-        if (pos >= 0 && pos < rg.len)
-          a.out[(int64_t(rg.bos + pos) * H + h) * D + v0 + i % VTR] = 0;
+      for (int i = tid; i < 64 * 16; i += NT) {
+        const int pos = 64 * c - rg.off + i / 16;
+        if (pos >= 0 && pos < rg.len) a.out[(int64_t(rg.bos + pos) * H + h) * D + v0 + i % 16] = 0;
       }
     return;
   }
@@ -603,9 +690,9 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(KArgs ka) {
 
   if (rg.nch == 0) {  // empty request: a cold start still zeroes the slot
     if (ka.c0 == 0 && !warm) {
-      for (int i = tid; i < VTR * D; i += kThreads) store_state(Slive + int64_t(v0) * D + i, 0.f);
+      for (int i = tid; i < 16 * D; i += NT) store_state(Slive + int64_t(v0) * D + i, 0.f);
       if (vt == 0)
-        for (int i = tid; i < 3 * 3 * D; i += kThreads) {
+        for (int i = tid; i < 3 * 3 * D; i += NT) {
           const int row = i / (3 * D), k = i % (3 * D);
           const int64_t ch = int64_t(k / D) * H * D + int64_t(h) * D + k % D;
           conv_live[row * C + ch] = 0;
@@ -615,144 +702,120 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(KArgs ka) {
   }
   if (ka.c0 >= rg.nch) return;
 
-  // zero the channel padding of S0 once (only when D < 32)
-  if (KD != D)
-    for (int i = tid; i < VTR * KP; i += kThreads) {
-      sSh[i] = static_cast<__bf16>(0.f);
-      sSl[i] = static_cast<__bf16>(0.f);
-    }
-
-  // ---- state in registers: wave owns tiles tt = wave + 4k -----------------------
-  f32x4 S[MAXT];
+  // ---- state: lane (r16, g4) of wave w holds S[v0 + r16][16cb + 4g4 + j], cb = 2w + hh
+  f32x4 S[2];
 #pragma unroll
-  for (int k = 0; k < MAXT; ++k) {
-    const int tt = wave + 4 * k;
-    const int vb = tt / NCB, cb = tt % NCB;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v = 0.f;
-      if (tt < NTS) {
-        const int row = v0 + 16 * vb + 4 * g4 + j, col = 16 * cb + r16;
-        if (ka.c0 > 0) v = carry[int64_t(row) * D + col];
-        else if (warm) v = load_state<TS>(Slive + int64_t(row) * D + col);
-      }
-      S[k][j] = v;
+  for (int hh = 0; hh < 2; ++hh) {
+    const int cb = 2 * wave + hh;
+    S[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (cb < NCB) {
+      const int64_t o = int64_t(v0 + r16) * D + 16 * cb + 4 * g4;
+      if (ka.c0 > 0) S[hh] = ld4(carry + o);
+      else if (warm) S[hh] = load_state4<TS>(Slive + o);
     }
   }
 
-  const int nks2 = wave < 2 ? 1 : 2;  // M is lower triangular
+  auto rec_of = [&](int cc) -> const char * {
+    return ka.ws + ka.carry_bytes + (size_t(b * ka.w + (cc - ka.c0)) * H + h) * RC::BYTES;
+  };
+  Split Wn[4], Qn[4], Mn[TBW][2], Kn[2][2];
+  f32x4 Un[4], Gn[2];
+  auto load_wq = [&](const char *r) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      Wn[tb] = frag_load(r + RC::WF, tb * NW + wave, lane);
+      Qn[tb] = frag_load(r + RC::QF, tb * NW + wave, lane);
+    }
+  };
+  auto load_u = [&](const char *r) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) Un[tb] = *reinterpret_cast<const f32x4 *>(r + RC::UF + size_t(tb * NCB + vt) * 1024 + lane * 16);
+  };
+  auto load_kg = [&](const char *r) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int cb = 2 * wave + hh;
+      if (cb < NCB) {
+#pragma unroll
+        for (int ksp = 0; ksp < 2; ++ksp) Kn[hh][ksp] = frag_load(r + RC::KF, cb * 2 + ksp, lane);
+        Gn[hh] = ld4(reinterpret_cast<const float *>(r + RC::GC) + 16 * cb + 4 * g4);
+      }
+    }
+  };
+  auto load_m = [&](const char *r) {
+#pragma unroll
+    for (int u = 0; u < TBW; ++u) {
+      const int tbo = wave + NW * u;
+#pragma unroll
+      for (int ksp = 0; ksp < 2; ++ksp)
+        if (ksp <= (tbo >> 1)) Mn[u][ksp] = frag_load(r + RC::MF, tbo * 2 + ksp, lane);
+    }
+  };
+  {
+    const char *r0 = rec_of(ka.c0);
+    load_wq(r0);
+    load_u(r0);
+    load_kg(r0);
+    load_m(r0);
+  }
+
 #pragma unroll 1
   for (int c = ka.c0; c < cend; ++c) {
-    const char *rec = ka.ws + ka.carry_bytes + (size_t(b * ka.w + (c - ka.c0)) * H + h) * Rec<D>::BYTES;
-    const __bf16 *Wh = reinterpret_cast<const __bf16 *>(rec + Rec<D>::WH);
-    const __bf16 *Wl = reinterpret_cast<const __bf16 *>(rec + Rec<D>::WL);
-    const __bf16 *Qh = reinterpret_cast<const __bf16 *>(rec + Rec<D>::QH);
-    const __bf16 *Ql = reinterpret_cast<const __bf16 *>(rec + Rec<D>::QL);
-    const __bf16 *Kh = reinterpret_cast<const __bf16 *>(rec + Rec<D>::KH);
-    const __bf16 *Kl = reinterpret_cast<const __bf16 *>(rec + Rec<D>::KL);
-    const __bf16 *Mh = reinterpret_cast<const __bf16 *>(rec + Rec<D>::MH);
-    const __bf16 *Ml = reinterpret_cast<const __bf16 *>(rec + Rec<D>::ML);
-    const float *recU = reinterpret_cast<const float *>(rec + Rec<D>::U);
-    const float *recGC = reinterpret_cast<const float *>(rec + Rec<D>::GC);
+    const int buf = (c - ka.c0) & 1;
+    const char *rnext = rec_of(min(c + 1, cend - 1));  // operands of the next chunk
 
-    // the wave's rows of W (for Dl) and of g.Q and M (for O): direct operand loads
-    Split Wf[KD / 32], Qf[KD / 32], Mf[2];
+    // partial -W S0^T and (g.Q) S0^T over this wave's 32 channels
+    const Split Sb = split44(S[0], S[1]);
 #pragma unroll
-    for (int ks = 0; ks < KD / 32; ++ks) {
-      if (32 * ks + 8 * g4 < D) {
-        const int o = (16 * wave + r16) * D + 32 * ks + 8 * g4;
-        Wf[ks] = load_split(Wh + o, Wl + o);
-        Wf[ks].hi = neg8(Wf[ks].hi);
-        Wf[ks].lo = neg8(Wf[ks].lo);
-        Qf[ks] = load_split(Qh + o, Ql + o);
-      } else {  // channel padding (D < 32)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          Wf[ks].hi[e] = Wf[ks].lo[e] = Qf[ks].hi[e] = Qf[ks].lo[e] = static_cast<__bf16>(0.f);
-        }
-      }
+    for (int tb = 0; tb < 4; ++tb) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      sPart[buf][wave][tb][0][lane] = mfma3(Wn[tb], Sb, z);
+      sPart[buf][wave][tb][1][lane] = mfma3(Qn[tb], Sb, z);
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int o = (16 * wave + r16) * 64 + 32 * ks + 8 * g4;
-      Mf[ks] = load_split(Mh + o, Ml + o);
-    }
-
-    // the entry state as split operands
-#pragma unroll
-    for (int k = 0; k < MAXT; ++k) {
-      const int tt = wave + 4 * k;
-      if (tt < NTS) {
-        const int vb = tt / NCB, cb = tt % NCB;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int o = (16 * vb + 4 * g4 + j) * KP + 16 * cb + r16;
-          split1(S[k][j], sSh[o], sSl[o]);
-        }
-      }
-    }
+    load_wq(rnext);
     __syncthreads();
 
-    // Dl = U - W S0^T   (wave = 16-token block)
-#pragma unroll 1
-    for (int vb = 0; vb < NVB; ++vb) {
-      f32x4 acc;
+    // Dl = U - W S0^T, all 64 tokens of this wave's 16 V rows
+    f32x4 Dl[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = recU[(16 * wave + 4 * g4 + j) * D + v0 + 16 * vb + r16];
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4 d = Un[tb];
 #pragma unroll
-      for (int ks = 0; ks < KD / 32; ++ks) {
-        const int o = (16 * vb + r16) * KP + 32 * ks + 8 * g4;
-        acc = mfma3(Wf[ks], load_split(sSh + o, sSl + o), acc);
-      }
+      for (int w = 0; w < NW; ++w) d += sPart[buf][w][tb][0][lane];
+      Dl[tb] = d;
+    }
+    load_u(rnext);
+    const Split Db[2] = {split44(Dl[0], Dl[1]), split44(Dl[2], Dl[3])};
+
+    // S = S Diag(g_63) + Dl^T (G(63,.) K) on this wave's channels
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int o = (16 * vb + r16) * TP + 16 * wave + 4 * g4 + j;
-        split1(acc[j], sDh[o], sDl[o]);
+    for (int hh = 0; hh < 2; ++hh) {
+      if (2 * wave + hh < NCB) {
+        S[hh] *= Gn[hh];
+#pragma unroll
+        for (int ksp = 0; ksp < 2; ++ksp) S[hh] = mfma3(Kn[hh][ksp], Db[ksp], S[hh]);
       }
     }
-    __syncthreads();
+    load_kg(rnext);
 
-    // O = (g.Q) S0^T + M Dl
-#pragma unroll 1
-    for (int vb = 0; vb < NVB; ++vb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // O = (g.Q) S0^T + M Dl for this wave's token blocks
 #pragma unroll
-      for (int ks = 0; ks < KD / 32; ++ks) {
-        const int o = (16 * vb + r16) * KP + 32 * ks + 8 * g4;
-        acc = mfma3(Qf[ks], load_split(sSh + o, sSl + o), acc);
-      }
+    for (int u = 0; u < TBW; ++u) {
+      const int tbo = wave + NW * u;
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks < nks2) {
-          const int o = (16 * vb + r16) * TP + 32 * ks + 8 * g4;
-          acc = mfma3(Mf[ks], load_split(sDh + o, sDl + o), acc);
-        }
-      }
+      for (int w = 0; w < NW; ++w) o += sPart[buf][w][tbo][1][lane];
+#pragma unroll
+      for (int ksp = 0; ksp < 2; ++ksp)
+        if (ksp <= (tbo >> 1)) o = mfma3(Mn[u][ksp], Db[ksp], o);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int pos = 64 * c - rg.off + 16 * wave + 4 * g4 + j;
+        const int pos = 64 * c - rg.off + 16 * tbo + 4 * g4 + j;
         if (pos >= 0 && pos < rg.len)
-          a.out[(int64_t(rg.bos + pos) * H + h) * D + v0 + 16 * vb + r16] = f32_to_bf16(a.scale * acc[j]);
+          a.out[(int64_t(rg.bos + pos) * H + h) * D + v0 + r16] = f32_to_bf16(a.scale * o[j]);
       }
     }
-
-    // S = S Diag(g_63) + Dl^T (G(63,.) K)
-#pragma unroll
-    for (int k = 0; k < MAXT; ++k) {
-      const int tt = wave + 4 * k;
-      if (tt < NTS) {
-        const int vb = tt / NCB, cb = tt % NCB;
-        const float gc = recGC[16 * cb + r16];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[k][j] *= gc;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int od = (16 * vb + r16) * TP + 32 * ks + 8 * g4;
-          const int ok = (16 * cb + r16) * 64 + 32 * ks + 8 * g4;
-          S[k] = mfma3(load_split(sDh + od, sDl + od), load_split(Kh + ok, Kl + ok), S[k]);
-        }
-      }
-    }
+    load_m(rnext);
 
     // snapshot at a boundary that ends this chunk
     if (a.snap_interval > 0) {
@@ -767,18 +830,13 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(KArgs ka) {
         } else if (dst > 0) {
           TS *Sdst = ssm + ((int64_t(a.layer) * ka.slots + dst) * H + h) * int64_t(D) * D;
 #pragma unroll
-          for (int k = 0; k < MAXT; ++k) {
-            const int tt = wave + 4 * k;
-            if (tt < NTS) {
-              const int vb = tt / NCB, cb = tt % NCB;
-#pragma unroll
-              for (int jj = 0; jj < 4; ++jj)
-                store_state(Sdst + int64_t(v0 + 16 * vb + 4 * g4 + jj) * D + 16 * cb + r16, S[k][jj]);
-            }
+          for (int hh = 0; hh < 2; ++hh) {
+            const int cb = 2 * wave + hh;
+            if (cb < NCB) store_state4(Sdst + int64_t(v0 + r16) * D + 16 * cb + 4 * g4, S[hh]);
           }
           if (vt == 0) {
             uint16_t *conv_dst = ka.conv + (int64_t(a.layer) * ka.slots + dst) * kConvRows * C;
-            for (int i = tid; i < 3 * 3 * D; i += kThreads) {
+            for (int i = tid; i < 3 * 3 * D; i += NT) {
               const int row = i / (3 * D), k = i % (3 * D);
               const int64_t ch = int64_t(k / D) * H * D + int64_t(h) * D + k % D;
               conv_dst[row * C + ch] = conv_row_value(done - 3 + row, ch);
@@ -787,31 +845,26 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(KArgs ka) {
         }
       }
     }
-    __syncthreads();
   }
 
   // ---- end of the window: live slot (request done) or the carry ----------------
   const bool done_all = cend == rg.nch;
 #pragma unroll
-  for (int k = 0; k < MAXT; ++k) {
-    const int tt = wave + 4 * k;
-    if (tt < NTS) {
-      const int vb = tt / NCB, cb = tt % NCB;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t o = int64_t(v0 + 16 * vb + 4 * g4 + j) * D + 16 * cb + r16;
-        if (done_all) store_state(Slive + o, S[k][j]);
-        else carry[o] = S[k][j];
-      }
+  for (int hh = 0; hh < 2; ++hh) {
+    const int cb = 2 * wave + hh;
+    if (cb < NCB) {
+      const int64_t o = int64_t(v0 + r16) * D + 16 * cb + 4 * g4;
+      if (done_all) store_state4(Slive + o, S[hh]);
+      else st4(carry + o, S[hh]);
     }
   }
   if (done_all && vt == 0) {
     // read every new row before writing any: the old rows may be inputs
-    constexpr int NI = (9 * D + kThreads - 1) / kThreads;
+    constexpr int NI = (9 * D + NT - 1) / NT;
     uint16_t nv[NI];
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-      const int i = tid + u * kThreads;
+      const int i = tid + u * NT;
       if (i < 9 * D) {
         const int row = i / (3 * D), k = i % (3 * D);
         const int64_t ch = int64_t(k / D) * H * D + int64_t(h) * D + k % D;
@@ -821,7 +874,7 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(KArgs ka) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
-      const int i = tid + u * kThreads;
+      const int i = tid + u * NT;
       if (i < 9 * D) {
         const int row = i / (3 * D), k = i % (3 * D);
         const int64_t ch = int64_t(k / D) * H * D + int64_t(h) * D + k % D;
@@ -841,11 +894,9 @@ hipError_t launch_d(const gdn_pool *p, const PrefillArgs &a, hipStream_t s) {
   size_t avail = (a.workspace_bytes - carry) / (size_t(B) * H * rec);
   int w = int(avail < size_t(nch_max) ? avail : size_t(nch_max));
   if (w < 1) w = 1;
-  // V-tiles: enough workgroups to cover the chip when batch x heads is small
-  int vtr = D;
-  while (vtr > 16 && int64_t(B) * H * (D / vtr) < 512) vtr /= 2;
+  constexpr int VT = D / 16;  // one scan workgroup per 16 rows of V
   KArgs ka{a, p->d.ssm_base, static_cast<uint16_t *>(p->d.conv_base), p->d.err_word,
-           p->d.slots, H, 0, w, D / vtr, static_cast<char *>(a.workspace), carry};
+           p->d.slots, H, 0, w, VT, static_cast<char *>(a.workspace), carry};
   const bool bf = p->d.ssm_dtype == GDN_BF16;
   const int rounds = nch_max > 0 ? (nch_max + w - 1) / w : 1;
   for (int rnd = 0; rnd < rounds; ++rnd) {
@@ -853,23 +904,15 @@ hipError_t launch_d(const gdn_pool *p, const PrefillArgs &a, hipStream_t s) {
     if (nch_max > 0) {
       dim3 grid(B * w, H);
       if (a.alpha_mode == GDN_ALPHA_PER_CHANNEL)
-        hipLaunchKernelGGL((prefill_prep_kernel<D, GDN_ALPHA_PER_CHANNEL>), grid, dim3(kThreads), 0, s, ka);
+        hipLaunchKernelGGL((prefill_prep_kernel<D, GDN_ALPHA_PER_CHANNEL>), grid, dim3(kPrepThreads), 0, s, ka);
       else
-        hipLaunchKernelGGL((prefill_prep_kernel<D, GDN_ALPHA_PER_HEAD>), grid, dim3(kThreads), 0, s, ka);
+        hipLaunchKernelGGL((prefill_prep_kernel<D, GDN_ALPHA_PER_HEAD>), grid, dim3(kPrepThreads), 0, s, ka);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    dim3 grid(B * ka.vt_count, H);
-#define GDN_SCAN(VTR_)                                                                        \
-  if (vtr == VTR_) {                                                                          \
-    if (bf) hipLaunchKernelGGL((prefill_scan_kernel<D, VTR_, uint16_t>), grid, dim3(kThreads), 0, s, ka); \
-    else hipLaunchKernelGGL((prefill_scan_kernel<D, VTR_, float>), grid, dim3(kThreads), 0, s, ka);      \
-  }
-    if constexpr (D >= 16) { GDN_SCAN(16) }
-    if constexpr (D >= 32) { GDN_SCAN(32) }
-    if constexpr (D >= 64) { GDN_SCAN(64) }
-    if constexpr (D >= 128) { GDN_SCAN(128) }
-#undef GDN_SCAN
+    const dim3 grid(unsigned(B) * H * VT), block(64 * Rec<D>::NKS);
+    if (bf) hipLaunchKernelGGL((prefill_scan_kernel<D, uint16_t>), grid, block, 0, s, ka);
+    else hipLaunchKernelGGL((prefill_scan_kernel<D, float>), grid, block, 0, s, ka);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
