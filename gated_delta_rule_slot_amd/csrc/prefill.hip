@@ -478,6 +478,12 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
       }
       frag_store(rec + RC::KF, cb * 2 + ksp, ln, split8(v));
     }
+    // M fragments (tb 0 and 1, ks' 1) lie above the diagonal; the scan multiplies
+    // them anyway to keep its loop free of branches, so store zeros
+    for (int it = rel; it < 256; it += 384) {
+      const int idx = (it >> 7) ? 3 : 1, plane = (it >> 6) & 1, ln = it & 63;
+      *reinterpret_cast<u32x4 *>(rec + RC::MF + size_t(2 * idx + plane) * 1024 + ln * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
     float *recGC = reinterpret_cast<float *>(rec + RC::GC);
     for (int cc = rel; cc < D; cc += 384) {
       float s = 0.f;
@@ -643,6 +649,10 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
   using RC = Rec<D>;
   constexpr int NW = RC::NKS, NT = 64 * NW, NCB = RC::NCB;
   constexpr int TBW = 4 / NW;  // 16-token output blocks per wave
+  // every wave's two channel tiles exist unless D = 16 (then tile 1 is padding);
+  // keeping the guards compile-time leaves the chunk loop without branches, so
+  // the wait counts at its head cover only the operands actually needed
+  constexpr bool kAllCb = 2 * NW <= NCB;
   // per-wave partial products over the wave's channels: [buffer][wave][tb][Dl | O][lane]
   __shared__ f32x4 sPart[2][NW][4][2][64];
 
@@ -708,7 +718,7 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
   for (int hh = 0; hh < 2; ++hh) {
     const int cb = 2 * wave + hh;
     S[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (cb < NCB) {
+    if (kAllCb || cb < NCB) {
       const int64_t o = int64_t(v0 + r16) * D + 16 * cb + 4 * g4;
       if (ka.c0 > 0) S[hh] = ld4(carry + o);
       else if (warm) S[hh] = load_state4<TS>(Slive + o);
@@ -735,7 +745,7 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int cb = 2 * wave + hh;
-      if (cb < NCB) {
+      if (kAllCb || cb < NCB) {
 #pragma unroll
         for (int ksp = 0; ksp < 2; ++ksp) Kn[hh][ksp] = frag_load(r + RC::KF, cb * 2 + ksp, lane);
         Gn[hh] = ld4(reinterpret_cast<const float *>(r + RC::GC) + 16 * cb + 4 * g4);
@@ -747,16 +757,33 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
     for (int u = 0; u < TBW; ++u) {
       const int tbo = wave + NW * u;
 #pragma unroll
-      for (int ksp = 0; ksp < 2; ++ksp)
-        if (ksp <= (tbo >> 1)) Mn[u][ksp] = frag_load(r + RC::MF, tbo * 2 + ksp, lane);
+      for (int ksp = 0; ksp < 2; ++ksp) Mn[u][ksp] = frag_load(r + RC::MF, tbo * 2 + ksp, lane);
     }
   };
+  // snapshots: only the last boundary of each ping-pong parity in this call is
+  // stored (an earlier one is overwritten by a later boundary of the same call,
+  // so the pool afterwards is the same); per-request values are read once here
+  // so that no load inside the chunk loop waits behind the operand loads
+  int sl = 0, nxt = 0, trk0 = 0, trk1 = 0, snap_lo = 0x7fffffff;
+  if (a.snap_interval > 0) {
+    sl = a.start_len[b];
+    nxt = a.next_track_idx[b];
+    trk0 = a.track_slots[2 * b];
+    trk1 = a.track_slots[2 * b + 1];
+    snap_lo = (sl + rg.len) / a.snap_interval - sl / a.snap_interval - 2;
+  }
   {
+    // same issue order as inside the loop, so that the wait counts the compiler
+    // derives at the loop head do not force later groups to land early
     const char *r0 = rec_of(ka.c0);
     load_wq(r0);
+    __builtin_amdgcn_sched_barrier(0);
     load_u(r0);
+    __builtin_amdgcn_sched_barrier(0);
     load_kg(r0);
+    __builtin_amdgcn_sched_barrier(0);
     load_m(r0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
 #pragma unroll 1
@@ -787,10 +814,12 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
     load_u(rnext);
     const Split Db[2] = {split44(Dl[0], Dl[1]), split44(Dl[2], Dl[3])};
 
-    // S = S Diag(g_63) + Dl^T (G(63,.) K) on this wave's channels
+    // S = S Diag(g_63) + Dl^T (G(63,.) K) on this wave's channels (kept here: the
+    // g_63 operand is the latest load of the previous chunk)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      if (2 * wave + hh < NCB) {
+      if (kAllCb || 2 * wave + hh < NCB) {
         S[hh] *= Gn[hh];
 #pragma unroll
         for (int ksp = 0; ksp < 2; ++ksp) S[hh] = mfma3(Kn[hh][ksp], Db[ksp], S[hh]);
@@ -798,7 +827,12 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
     }
     load_kg(rnext);
 
-    // O = (g.Q) S0^T + M Dl for this wave's token blocks
+    // O = (g.Q) S0^T + M Dl for this wave's token blocks; the stores go through a
+    // buffer resource spanning this chunk's rows of the request, and a padding
+    // token's offset lies outside it, so the hardware drops that store
+    const int pbase = max(64 * c - rg.off, 0), pend = min(64 * c - rg.off + 64, rg.len);
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        a.out + (int64_t(rg.bos) + pbase) * H * D, 0, (pend - pbase) * H * D * 2, 0x00020000);
 #pragma unroll
     for (int u = 0; u < TBW; ++u) {
       const int tbo = wave + NW * u;
@@ -806,25 +840,23 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
 #pragma unroll
       for (int w = 0; w < NW; ++w) o += sPart[buf][w][tbo][1][lane];
 #pragma unroll
-      for (int ksp = 0; ksp < 2; ++ksp)
-        if (ksp <= (tbo >> 1)) o = mfma3(Mn[u][ksp], Db[ksp], o);
+      for (int ksp = 0; ksp < 2; ++ksp) o = mfma3(Mn[u][ksp], Db[ksp], o);  // zero above the diagonal
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int pos = 64 * c - rg.off + 16 * tbo + 4 * g4 + j;
-        if (pos >= 0 && pos < rg.len)
-          a.out[(int64_t(rg.bos + pos) * H + h) * D + v0 + r16] = f32_to_bf16(a.scale * o[j]);
+        const int offs = (pos >= pbase && pos < pend) ? (((pos - pbase) * H + h) * D + v0 + r16) * 2 : 0x7fffffff;
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(a.scale * o[j]), orsrc, offs, 0, 0);
       }
     }
     load_m(rnext);
 
     // snapshot at a boundary that ends this chunk
     if (a.snap_interval > 0) {
-      const int sl = a.start_len[b];
       const int done = min(64 * (c + 1) - rg.off, rg.len);
       const int n_end = sl + done;
-      if (n_end % a.snap_interval == 0) {
-        const int j = n_end / a.snap_interval - sl / a.snap_interval - 1;
-        const int dst = a.track_slots[2 * b + ((a.next_track_idx[b] + j) & 1)];
+      const int j = n_end / a.snap_interval - sl / a.snap_interval - 1;
+      if (n_end % a.snap_interval == 0 && j >= snap_lo) {
+        const int dst = ((nxt + j) & 1) ? trk1 : trk0;
         if (dst >= ka.slots) {
           if (ka.err && vt == 0 && tid == 0) atomicOr(ka.err, GDN_ERRW_BAD_TRACK_SLOT);
         } else if (dst > 0) {
@@ -832,7 +864,7 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int cb = 2 * wave + hh;
-            if (cb < NCB) store_state4(Sdst + int64_t(v0 + r16) * D + 16 * cb + 4 * g4, S[hh]);
+            if (kAllCb || cb < NCB) store_state4(Sdst + int64_t(v0 + r16) * D + 16 * cb + 4 * g4, S[hh]);
           }
           if (vt == 0) {
             uint16_t *conv_dst = ka.conv + (int64_t(a.layer) * ka.slots + dst) * kConvRows * C;
@@ -852,7 +884,7 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int cb = 2 * wave + hh;
-    if (cb < NCB) {
+    if (kAllCb || cb < NCB) {
       const int64_t o = int64_t(v0 + r16) * D + 16 * cb + 4 * g4;
       if (done_all) store_state4(Slive + o, S[hh]);
       else st4(carry + o, S[hh]);
