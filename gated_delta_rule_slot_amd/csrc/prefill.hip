@@ -157,12 +157,6 @@ __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<
 __device__ __forceinline__ void st4(float *p, const f32x4 &v) { *reinterpret_cast<f32x4 *>(p) = v; }
 
 // a fragment pair (hi, lo) of a record
-__device__ __forceinline__ Split frag_load(const char *base, int idx, int lane) {
-  Split s;
-  s.hi = *reinterpret_cast<const bf16x8 *>(base + size_t(2 * idx) * 1024 + lane * 16);
-  s.lo = *reinterpret_cast<const bf16x8 *>(base + size_t(2 * idx + 1) * 1024 + lane * 16);
-  return s;
-}
 __device__ __forceinline__ void frag_store(char *base, int idx, int lane, const Split &s) {
   *reinterpret_cast<bf16x8 *>(base + size_t(2 * idx) * 1024 + lane * 16) = s.hi;
   *reinterpret_cast<bf16x8 *>(base + size_t(2 * idx + 1) * 1024 + lane * 16) = s.lo;
@@ -199,7 +193,8 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
   const PrefillArgs &a = ka.a;
   const int H = ka.heads;
   const int b = blockIdx.x / ka.w, cl = blockIdx.x % ka.w, c = ka.c0 + cl, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
 
   const ReqGeom rg = req_geom(a, b);
@@ -644,17 +639,39 @@ __device__ __forceinline__ void store_state4(uint16_t *p, const f32x4 &v) {
 __device__ __forceinline__ void store_state(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_state(uint16_t *p, float v) { *p = f32_to_bf16(v); }
 
+// One fragment pair (hi, lo) of the record held by buffer resource r; byte_off is
+// wave-uniform, so the address needs no per-lane arithmetic.
+__device__ __forceinline__ Split frag_buf(__amdgpu_buffer_rsrc_t r, int voff, int byte_off) {
+  Split s;
+  s.hi = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, byte_off, 0));
+  s.lo = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, byte_off + 1024, 0));
+  return s;
+}
+__device__ __forceinline__ f32x4 f4_buf(__amdgpu_buffer_rsrc_t r, int voff, int byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, byte_off, 0));
+}
+__device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const __bf16 h = static_cast<__bf16>(v[j]);
+    hi[j] = h;
+    lo[j] = static_cast<__bf16>(v[j] - static_cast<float>(h));
+  }
+}
+
 template <int D, typename TS>
 __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs ka) {
   using RC = Rec<D>;
   constexpr int NW = RC::NKS, NT = 64 * NW, NCB = RC::NCB;
-  constexpr int TBW = 4 / NW;  // 16-token output blocks per wave
+  constexpr int TBW = 4 / NW;  // 16-token blocks per wave
   // every wave's two channel tiles exist unless D = 16 (then tile 1 is padding);
   // keeping the guards compile-time leaves the chunk loop without branches, so
   // the wait counts at its head cover only the operands actually needed
   constexpr bool kAllCb = 2 * NW <= NCB;
-  // per-wave partial products over the wave's channels: [buffer][wave][tb][Dl | O][lane]
-  __shared__ f32x4 sPart[2][NW][4][2][64];
+  // entry-state operand fragments of each 32-channel slice, and Dl operand
+  // fragments of each 32-token step (two 16-token halves of 4 values per lane)
+  __shared__ bf16x8 sS[NW][2][64];
+  __shared__ bf16x4 sD[2][2][64][2];
 
   const PrefillArgs &a = ka.a;
   const int H = ka.heads, VT = ka.vt_count;
@@ -664,7 +681,8 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
   const int qn = nblk / 8, rn = nblk % 8, xcd = lin % 8;
   const int id = xcd * qn + min(xcd, rn) + lin / 8;
   const int bh = id / VT, vt = id % VT, b = bh / H, h = bh % H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
   const int v0 = 16 * vt;
 
@@ -725,41 +743,6 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
     }
   }
 
-  auto rec_of = [&](int cc) -> const char * {
-    return ka.ws + ka.carry_bytes + (size_t(b * ka.w + (cc - ka.c0)) * H + h) * RC::BYTES;
-  };
-  Split Wn[4], Qn[4], Mn[TBW][2], Kn[2][2];
-  f32x4 Un[4], Gn[2];
-  auto load_wq = [&](const char *r) {
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      Wn[tb] = frag_load(r + RC::WF, tb * NW + wave, lane);
-      Qn[tb] = frag_load(r + RC::QF, tb * NW + wave, lane);
-    }
-  };
-  auto load_u = [&](const char *r) {
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) Un[tb] = *reinterpret_cast<const f32x4 *>(r + RC::UF + size_t(tb * NCB + vt) * 1024 + lane * 16);
-  };
-  auto load_kg = [&](const char *r) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int cb = 2 * wave + hh;
-      if (kAllCb || cb < NCB) {
-#pragma unroll
-        for (int ksp = 0; ksp < 2; ++ksp) Kn[hh][ksp] = frag_load(r + RC::KF, cb * 2 + ksp, lane);
-        Gn[hh] = ld4(reinterpret_cast<const float *>(r + RC::GC) + 16 * cb + 4 * g4);
-      }
-    }
-  };
-  auto load_m = [&](const char *r) {
-#pragma unroll
-    for (int u = 0; u < TBW; ++u) {
-      const int tbo = wave + NW * u;
-#pragma unroll
-      for (int ksp = 0; ksp < 2; ++ksp) Mn[u][ksp] = frag_load(r + RC::MF, tbo * 2 + ksp, lane);
-    }
-  };
   // snapshots: only the last boundary of each ping-pong parity in this call is
   // stored (an earlier one is overwritten by a later boundary of the same call,
   // so the pool afterwards is the same); per-request values are read once here
@@ -772,13 +755,60 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
     trk1 = a.track_slots[2 * b + 1];
     snap_lo = (sl + rg.len) / a.snap_interval - sl / a.snap_interval - 2;
   }
+
+  // operands of one chunk for this wave: its token blocks (W, g.Q, M, U) and its
+  // channel tiles (G(63,.)K, g_63)
+  auto rec_rsrc = [&](int cc) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        ka.ws + ka.carry_bytes + (size_t(b * ka.w + (cc - ka.c0)) * H + h) * RC::BYTES, 0, int(RC::BYTES),
+        0x00020000);
+  };
+  const int voff = lane * 16;
+  Split Wn[TBW][NW], Qn[TBW][NW], Mn[TBW][2], Kn[2][2];
+  f32x4 Un[TBW], Gn[2];
+  auto load_wu = [&](__amdgpu_buffer_rsrc_t r) {
+#pragma unroll
+    for (int u = 0; u < TBW; ++u) {
+      const int tb = wave + NW * u;
+#pragma unroll
+      for (int ks = 0; ks < NW; ++ks) Wn[u][ks] = frag_buf(r, voff, int(RC::WF) + (tb * NW + ks) * 2048);
+      Un[u] = f4_buf(r, voff, int(RC::UF) + (tb * NCB + vt) * 1024);
+    }
+  };
+  auto load_q = [&](__amdgpu_buffer_rsrc_t r) {
+#pragma unroll
+    for (int u = 0; u < TBW; ++u) {
+      const int tb = wave + NW * u;
+#pragma unroll
+      for (int ks = 0; ks < NW; ++ks) Qn[u][ks] = frag_buf(r, voff, int(RC::QF) + (tb * NW + ks) * 2048);
+    }
+  };
+  auto load_kg = [&](__amdgpu_buffer_rsrc_t r) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int cb = 2 * wave + hh;
+      if (kAllCb || cb < NCB) {
+#pragma unroll
+        for (int ksp = 0; ksp < 2; ++ksp) Kn[hh][ksp] = frag_buf(r, voff, int(RC::KF) + (cb * 2 + ksp) * 2048);
+        Gn[hh] = f4_buf(r, g4 * 16, int(RC::GC) + cb * 64);
+      }
+    }
+  };
+  auto load_m = [&](__amdgpu_buffer_rsrc_t r) {
+#pragma unroll
+    for (int u = 0; u < TBW; ++u) {
+      const int tb = wave + NW * u;
+#pragma unroll
+      for (int ksp = 0; ksp < 2; ++ksp) Mn[u][ksp] = frag_buf(r, voff, int(RC::MF) + (tb * 2 + ksp) * 2048);
+    }
+  };
   {
     // same issue order as inside the loop, so that the wait counts the compiler
     // derives at the loop head do not force later groups to land early
-    const char *r0 = rec_of(ka.c0);
-    load_wq(r0);
+    const __amdgpu_buffer_rsrc_t r0 = rec_rsrc(ka.c0);
+    load_wu(r0);
     __builtin_amdgcn_sched_barrier(0);
-    load_u(r0);
+    load_q(r0);
     __builtin_amdgcn_sched_barrier(0);
     load_kg(r0);
     __builtin_amdgcn_sched_barrier(0);
@@ -788,34 +818,54 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
 
 #pragma unroll 1
   for (int c = ka.c0; c < cend; ++c) {
-    const int buf = (c - ka.c0) & 1;
-    const char *rnext = rec_of(min(c + 1, cend - 1));  // operands of the next chunk
+    const __amdgpu_buffer_rsrc_t rnext = rec_rsrc(min(c + 1, cend - 1));  // next chunk's operands
 
-    // partial -W S0^T and (g.Q) S0^T over this wave's 32 channels
-    const Split Sb = split44(S[0], S[1]);
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      sPart[buf][wave][tb][0][lane] = mfma3(Wn[tb], Sb, z);
-      sPart[buf][wave][tb][1][lane] = mfma3(Qn[tb], Sb, z);
+    // this wave's channel slice of the entry state, as an operand, to every wave
+    {
+      const Split sb = split44(S[0], S[1]);
+      sS[wave][0][lane] = sb.hi;
+      sS[wave][1][lane] = sb.lo;
     }
-    load_wq(rnext);
     __syncthreads();
-
-    // Dl = U - W S0^T, all 64 tokens of this wave's 16 V rows
-    f32x4 Dl[4];
+    Split Sf[NW];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      f32x4 d = Un[tb];
-#pragma unroll
-      for (int w = 0; w < NW; ++w) d += sPart[buf][w][tb][0][lane];
-      Dl[tb] = d;
+    for (int ks = 0; ks < NW; ++ks) {
+      Sf[ks].hi = sS[ks][0][lane];
+      Sf[ks].lo = sS[ks][1][lane];
     }
-    load_u(rnext);
-    const Split Db[2] = {split44(Dl[0], Dl[1]), split44(Dl[2], Dl[3])};
+
+    // Dl = U - W S0^T for this wave's token blocks (the record keeps -W)
+#pragma unroll
+    for (int u = 0; u < TBW; ++u) {
+      const int tb = wave + NW * u;
+      f32x4 d = Un[u];
+#pragma unroll
+      for (int ks = 0; ks < NW; ++ks) d = mfma3(Wn[u][ks], Sf[ks], d);
+      bf16x4 dh, dl;
+      split4(d, dh, dl);
+      sD[tb >> 1][0][lane][tb & 1] = dh;
+      sD[tb >> 1][1][lane][tb & 1] = dl;
+    }
+    load_wu(rnext);
+    // (g.Q) S0^T for the same blocks
+    f32x4 Oq[TBW];
+#pragma unroll
+    for (int u = 0; u < TBW; ++u) {
+      Oq[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NW; ++ks) Oq[u] = mfma3(Qn[u][ks], Sf[ks], Oq[u]);
+    }
+    load_q(rnext);
+    __syncthreads();
+    Split Db[2];
+#pragma unroll
+    for (int ksp = 0; ksp < 2; ++ksp) {
+      Db[ksp].hi = *reinterpret_cast<const bf16x8 *>(&sD[ksp][0][lane][0]);
+      Db[ksp].lo = *reinterpret_cast<const bf16x8 *>(&sD[ksp][1][lane][0]);
+    }
 
     // S = S Diag(g_63) + Dl^T (G(63,.) K) on this wave's channels (kept here: the
-    // g_63 operand is the latest load of the previous chunk)
+    // g_63 operand is among the latest loads of the previous chunk)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -827,23 +877,21 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
     }
     load_kg(rnext);
 
-    // O = (g.Q) S0^T + M Dl for this wave's token blocks; the stores go through a
-    // buffer resource spanning this chunk's rows of the request, and a padding
-    // token's offset lies outside it, so the hardware drops that store
+    // O = (g.Q) S0^T + M Dl; the stores go through a buffer resource spanning this
+    // chunk's rows of the request, and a padding token's offset lies outside it,
+    // so the hardware drops that store
     const int pbase = max(64 * c - rg.off, 0), pend = min(64 * c - rg.off + 64, rg.len);
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         a.out + (int64_t(rg.bos) + pbase) * H * D, 0, (pend - pbase) * H * D * 2, 0x00020000);
 #pragma unroll
     for (int u = 0; u < TBW; ++u) {
-      const int tbo = wave + NW * u;
-      f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < NW; ++w) o += sPart[buf][w][tbo][1][lane];
+      const int tb = wave + NW * u;
+      f32x4 o = Oq[u];
 #pragma unroll
       for (int ksp = 0; ksp < 2; ++ksp) o = mfma3(Mn[u][ksp], Db[ksp], o);  // zero above the diagonal
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int pos = 64 * c - rg.off + 16 * tbo + 4 * g4 + j;
+        const int pos = 64 * c - rg.off + 16 * tb + 4 * g4 + j;
         const int offs = (pos >= pbase && pos < pend) ? (((pos - pbase) * H + h) * D + v0 + r16) * 2 : 0x7fffffff;
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(a.scale * o[j]), orsrc, offs, 0, 0);
       }
