@@ -153,6 +153,10 @@ __device__ __forceinline__ float bf16_elem(const u32x4 &v, int e) {
   return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
+// 2^x on the hardware unit; a result below 2^-126 comes out as zero, which only
+// drops decay products that are negligible next to the unit-scale terms they join
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ void st4(float *p, const f32x4 &v) { *reinterpret_cast<f32x4 *>(p) = v; }
 
@@ -384,8 +388,8 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            rv[4 * hf + j] = ki[j] * exp2f(rexp[j]);
-            const float f = exp2f(lexp[j]);
+            rv[4 * hf + j] = ki[j] * fexp2(rexp[j]);
+            const float f = fexp2(lexp[j]);
             lk[4 * hf + j] = kt[j] * f;
             lq[4 * hf + j] = qt[j] * f;
           }
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
         float sa = 0.f, sm = 0.f;
         if (ii <= t) {
           for (int cc = 0; cc < KD; ++cc) {
-            const float f = exp2f(sL[t * DP + cc] - sL[ii * DP + cc]) * sK[ii * DP + cc];
+            const float f = fexp2(sL[t * DP + cc] - sL[ii * DP + cc]) * sK[ii * DP + cc];
             sa = fmaf(sK[t * DP + cc], f, sa);
             sm = fmaf(sQ[t * DP + cc], f, sm);
           }
@@ -452,7 +456,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
         for (int kb = 0; kb < tb; ++kb) pre += ld4(sTot + kb * KD + cc);
         const f32x4 q4 = ld4(sQ + t * DP + cc), l4 = ld4(sL + t * DP + cc);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[4 * hf + j] = q4[j] * exp2f(pre[j] + l4[j]);
+        for (int j = 0; j < 4; ++j) v[4 * hf + j] = q4[j] * fexp2(pre[j] + l4[j]);
       }
       frag_store(rec + RC::QF, tb * NKS + ks, ln, split8(v));
     }
@@ -468,7 +472,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int tt = 16 * tbk + 4 * g + j;
-          v[4 * hf + j] = sK[tt * DP + cc] * exp2f(post - sL[tt * DP + cc]);
+          v[4 * hf + j] = sK[tt * DP + cc] * fexp2(post - sL[tt * DP + cc]);
         }
       }
       frag_store(rec + RC::KF, cb * 2 + ksp, ln, split8(v));
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
     for (int cc = rel; cc < D; cc += 384) {
       float s = 0.f;
       for (int kb = 0; kb < 4; ++kb) s += sTot[kb * KD + cc];
-      recGC[cc] = exp2f(s);
+      recGC[cc] = fexp2(s);
     }
   }
   __syncthreads();
@@ -515,24 +519,24 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
       f32x4 k4 = ld4(sK + t * DP + cc);
       const f32x4 l4 = ld4(sL + t * DP + cc);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) k4[j] *= exp2f(pre[j] + l4[j]);
+      for (int j = 0; j < 4; ++j) k4[j] *= fexp2(pre[j] + l4[j]);
       st4(sK + t * DP + cc, k4);
     }
   }
   __syncthreads();
   // off-diagonal blocks: T_mn = -T_mm sum_{k=n}^{m-1} (Diag(b)A)_mk T_kn, n = m - d
-#pragma unroll 1
+#pragma unroll
   for (int d = 1; d < 4; ++d) {
     const bool act = wave < 4 - d;
     const int m = wave + d, n = wave;
     const int rr = lane >> 2, cc = 4 * (lane & 3);
     float *P = sP + wave * 16 * 17;
     if (act) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int k = 16 * n; k < 16 * m; ++k) {
-        const float l = sA[(16 * m + rr) * TP + k];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaf(l, sT[k * TP + 16 * n + cc + e], acc[e]);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+      for (int kk = 0; kk < 16 * d; ++kk) {
+        const int k = 16 * n + kk;
+        acc += sA[(16 * m + rr) * TP + k] * ld4(sT + k * TP + 16 * n + cc);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) P[rr * 17 + cc + e] = acc[e];
@@ -540,6 +544,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
     __syncthreads();
     if (act) {
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
       for (int q = 0; q < 16; ++q) {
         const float tv = sT[(16 * m + rr) * TP + 16 * m + q];
 #pragma unroll
