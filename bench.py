@@ -193,6 +193,143 @@ def run_kda_prefill(torch, gdn, wl, dev, reps=5):
             "algorithmic_flops": flops}
 
 
+# ------------------------------------------------- KDA decode with tracking --
+def run_kda_decode_tracking(torch, gdn, wl, dev, steps=16, warmup=2):
+    """69 KDA layers per step, batch 256, bf16 pool of 1024 slots, per-channel decay,
+    snapshot every 256 tokens into ping-pong track slots; the caller flips
+    next_track_idx after the last layer.  Initial lengths ~ U[256, 8192), so the
+    snapshots are spread over the steps.  The same steps are also timed without
+    tracking to give the snapshot overhead."""
+    cfg = wl.KDA_DECODE
+    L, N, H, D, B = cfg.layers, cfg.slots, cfg.heads, cfg.head_k, 256
+    C = H * 3 * D
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    ssm = torch.empty(L, N, H, D, D, dtype=torch.bfloat16, device=dev)
+    conv = torch.empty(L, N, 3, C, dtype=torch.bfloat16, device=dev)
+    for l in range(L):
+        ssm[l].normal_(0.0, 0.25, generator=g)
+        conv[l].normal_(0.0, 1.0, generator=g)
+    pool = gdn.state_pool_create(ssm, conv, torch.zeros(1, dtype=torch.int32, device=dev))
+    gc = wl.generator(cfg.seed)
+    perm = (torch.randperm(N - 1, generator=gc) + 1).to(torch.int32)
+    slots = perm[:B].to(dev)
+    track = perm[B:3 * B].view(B, 2).contiguous().to(dev)
+    len0 = torch.randint(256, 8192, (B,), generator=gc, dtype=torch.int32)
+    w = wl.conv_weights(gc, C).to(dev)
+    inputs = [{k: v.to(dev) for k, v in wl.projected_inputs(gc, B, H, D, D, cfg.alpha_mode).items()}
+              for _ in range(3)]
+    out = torch.empty(B, H, D, dtype=torch.bfloat16, device=dev)
+    nxt = torch.zeros(B, dtype=torch.int32, device=dev)
+    seqs = [(len0 + s + 1).to(dev) for s in range(warmup + steps)]
+    flips = [(sq % 256 == 0).to(torch.int32) for sq in seqs]
+
+    def step(s, interval):
+        sq = seqs[s]
+        for l in range(L):
+            inp = inputs[l % 3]
+            gdn.gdn_decode_step(pool, l, slots, inp["x"], w, inp["alpha"], cfg.alpha_mode, inp["beta"], out,
+                                seq_len_after=sq, track_interval=interval, track_slots=track,
+                                next_track_idx=nxt)
+        if interval:
+            nxt.bitwise_xor_(flips[s])
+
+    res = {}
+    for interval in (256, 0):
+        for s in range(warmup):
+            step(s, interval)
+        torch.cuda.synchronize()
+        a, b = event_pair()
+        a.record()
+        for s in range(warmup, warmup + steps):
+            step(s, interval)
+        b.record()
+        torch.cuda.synchronize()
+        res[interval] = a.elapsed_time(b) / 1e3
+    assert int(pool.err_word.item()) == 0
+    snaps = sum(int(f.sum()) for f in flips[warmup:])
+    t = res[256]
+    byts = steps * L * decode_bytes(B, H, D, C, 2, True, 0) + snaps * L * (H * D * D * 2 + 3 * C * 2)
+    del pool, ssm, conv
+    torch.cuda.empty_cache()
+    return {"workload": "KDA decode with tracking: 12 heads, K=V=128, 69 layers, batch 256, "
+                        "bf16 pool of 1024 slots, snapshot every 256 tokens",
+            "steps": steps, "tokens_per_s": B * steps / t, "ms_per_step": t / steps * 1e3,
+            "GB_per_s": byts / t / 1e9, "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS,
+            "snapshots": snaps, "snapshot_overhead_frac": res[256] / res[0] - 1.0}
+
+
+# ------------------------------------------------ prefix hit + warm prefill --
+def run_warm_prefill(torch, gdn, wl, dev, ws_cap=8 << 30):
+    """64 requests of 13600 tokens in 8 prefix groups over 24 GDN layers (32 heads,
+    fp32 pool of 81 slots: 64 live + 8 groups x 2 checkpoints).  A request whose
+    shared prefix P reaches c = 6144 * min(2, P // 6144) > 0 restores the group's
+    checkpoint at c into its live slot across all layers, then every request is
+    prefilled from c to 13600 (cold when c = 0).  Checkpoint contents are random
+    (they stand for the seed runs); one x buffer serves every layer."""
+    cfg = wl.WARM_PREFILL
+    L, N, H, D, B, T_full = cfg.layers, cfg.slots, cfg.heads, cfg.head_k, 64, 13600
+    C = H * 3 * D
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    ssm = torch.empty(L, N, H, D, D, dtype=torch.float32, device=dev)
+    conv = torch.empty(L, N, 3, C, dtype=torch.bfloat16, device=dev)
+    for l in range(L):
+        ssm[l].normal_(0.0, 0.25, generator=g)
+        conv[l].normal_(0.0, 1.0, generator=g)
+    pool = gdn.state_pool_create(ssm, conv, torch.zeros(1, dtype=torch.int32, device=dev))
+    gc = wl.generator(cfg.seed)
+    group = torch.randint(0, 8, (B,), generator=gc).tolist()
+    prefix = torch.randint(0, T_full, (B,), generator=gc).tolist()
+    depth = [6144 * min(2, p // 6144) for p in prefix]
+    ops = [(1 + i, 1 if depth[i] > 0 else 0, 65 + 2 * group[i] + (depth[i] // 6144 - 1))
+           for i in range(B)]
+    lens = [T_full - c for c in depth]
+    T = sum(lens)
+    cu = wl.cu_seqlens(lens).to(dev)
+    x = torch.randn(T, C, generator=g, device=dev, dtype=torch.bfloat16)
+    alpha = torch.sigmoid(torch.randn(T, H, generator=g, device=dev) + 3.0)
+    beta = torch.sigmoid(torch.randn(T, H, generator=g, device=dev))
+    w = wl.conv_weights(gc, C).to(dev)
+    out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+    slots = torch.arange(1, B + 1, dtype=torch.int32, device=dev)
+    start = torch.tensor(depth, dtype=torch.int32, device=dev)
+    ws = torch.empty(min(gdn.gdn_prefill_workspace_bytes(pool, B, max(lens)), ws_cap),
+                     dtype=torch.uint8, device=dev)
+
+    # warm up on one layer, then time the whole pass (restore + 24 layers)
+    gdn.conv_gdn_prefill_chunked(pool, 0, cu, slots, torch.ones(B, dtype=torch.int32, device=dev), x, w,
+                                 alpha, cfg.alpha_mode, beta, out, max(lens), start_len=start, workspace=ws)
+    torch.cuda.synchronize()
+    a, m, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), \
+        torch.cuda.Event(enable_timing=True)
+    a.record()
+    hist = gdn.restore_slots(pool, ops, [0] * B)
+    m.record()
+    has = torch.tensor(hist, dtype=torch.int32, device=dev)
+    for l in range(L):
+        gdn.conv_gdn_prefill_chunked(pool, l, cu, slots, has, x, w, alpha, cfg.alpha_mode, beta, out,
+                                     max(lens), start_len=start, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    assert int(pool.err_word.item()) == 0
+    t_restore = a.elapsed_time(m) / 1e3
+    t_prefill = m.elapsed_time(b) / 1e3
+    n_restored = sum(1 for o in ops if o[1])
+    restore_bytes = 2 * n_restored * L * (H * D * D * 4 + 3 * C * 2)
+    flops = T * L * H * 140.6e3
+    del pool, ssm, conv, x, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": "prefix-hit restore + warm prefill: 64 requests x 13600 tokens, 8 prefix groups, "
+                        "24 GDN layers, 32 heads, K=V=128, fp32 pool of 81 slots",
+            "restored_requests": n_restored, "restore_ms": t_restore * 1e3,
+            "restore_GB_per_s": restore_bytes / t_restore / 1e9,
+            "prefill_tokens": T, "prefill_ms": t_prefill * 1e3,
+            "prefill_tokens_per_s": T / t_prefill,
+            "prefill_mfma_util_vs_bf16_peak": flops / t_prefill / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "workspace_bytes": ws_cap}
+
+
 # ----------------------------------------------------------------- restore --
 def run_restore(torch, gdn, wl, dev, reps=5):
     cfg = wl.WARM_PREFILL
@@ -277,6 +414,10 @@ def main():
         extra["kda_prefill"] = run_kda_prefill(torch, gdn, wl, dev)
         log("extra: restore")
         extra["restore"] = run_restore(torch, gdn, wl, dev)
+        log("extra: KDA decode with tracking (69 layers)")
+        extra["kda_decode_tracking"] = run_kda_decode_tracking(torch, gdn, wl, dev)
+        log("extra: prefix-hit restore + warm prefill (24 layers)")
+        extra["warm_prefill"] = run_warm_prefill(torch, gdn, wl, dev)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
