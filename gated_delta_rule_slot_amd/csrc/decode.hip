@@ -57,13 +57,56 @@ struct StateVec<uint16_t> {  // bf16
   }
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+// Sum over each aligned group of N lanes, left in every lane of the group.  The
+// first four steps are DPP lane permutes inside the VALU (swap neighbours, swap
+// pairs, mirror within 8, mirror within 16); wider groups use the gfx950 row swaps
+// (lane ^ 16, lane ^ 32).  Each step adds the same two partial sums in every lane
+// of a group, so all lanes end with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "group of 2^k lanes");
+  const int lane = threadIdx.x & 63;
+  if constexpr (N >= 2) v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror
+  if constexpr (N >= 16) v += dpp_mov<0x140>(v); // row_mirror
+  if constexpr (N >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v += __uint_as_float((lane & 16) ? r[0] : r[1]);
+  }
+  if constexpr (N >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v += __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
   return v;
 }
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// CW consecutive bf16 conv values (a row slice) as one load / store
+template <int CW>
+struct ConvVec;
+template <>
+struct ConvVec<2> {
+  typedef uint32_t raw;
+  static __device__ __forceinline__ uint32_t word(const raw &v, int) { return v; }
+};
+template <>
+struct ConvVec<4> {
+  typedef u32x2 raw;
+  static __device__ __forceinline__ uint32_t word(const raw &v, int i) { return v[i]; }
+};
+template <>
+struct ConvVec<8> {
+  typedef u32x4 raw;
+  static __device__ __forceinline__ uint32_t word(const raw &v, int i) { return v[i]; }
+};
 
 // One workgroup per (request, head); each of its waves owns ROWS state rows.  The head's conv is split across the waves into shared memory;
 // after the single barrier every wave has what it needs, writes back its own
@@ -79,10 +122,14 @@ struct DecodeShape {
   static constexpr int RPI = 64 / LPR;                        // rows per load instruction
   static constexpr int ROWS = RPI * kIters < D ? RPI * kIters : D;  // state rows per wave
   static constexpr int THREADS = 64 * (D / ROWS);
+  // fp32 state: 8-wave workgroups; capping registers at 6 waves per SIMD (80 VGPRs,
+  // no spills) fits a third workgroup per CU, i.e. more state loads in flight
+  static constexpr int WAVES_PER_EU = sizeof(TS) == 4 ? 6 : 1;
 };
 
 template <int D, typename TS, int kAlphaMode>
-__global__ __launch_bounds__((DecodeShape<D, TS>::THREADS)) void gdn_decode_kernel(
+__global__ __launch_bounds__((DecodeShape<D, TS>::THREADS))
+__attribute__((amdgpu_waves_per_eu(DecodeShape<D, TS>::WAVES_PER_EU))) void gdn_decode_kernel(
     TS *__restrict__ ssm, uint16_t *__restrict__ conv, int32_t *err, int slots, int heads,
     DecodeArgs a) {
   using SV = StateVec<TS>;
@@ -92,8 +139,13 @@ __global__ __launch_bounds__((DecodeShape<D, TS>::THREADS)) void gdn_decode_kern
   constexpr int LPR = SH::LPR;            // lanes per row
   constexpr int RPI = SH::RPI;            // rows per load instruction
   constexpr int ITERS = (ROWS + RPI - 1) / RPI;
-  static_assert(3 * D / 8 <= SH::THREADS, "one conv item per thread");
-  constexpr int ITEMS = 3 * D / 8;        // 8-channel conv items of the head
+  // conv items of CW channels: the narrowest width that still gives every item its
+  // own thread, which keeps the conv's registers (live while the state loads are in
+  // flight) few enough for more workgroups per CU
+  constexpr int CW = 3 * D / 2 <= SH::THREADS ? 2 : 3 * D / 4 <= SH::THREADS ? 4 : 8;
+  static_assert(3 * D / CW <= SH::THREADS, "one conv item per thread");
+  constexpr int ITEMS = 3 * D / CW;       // CW-channel conv items of the head
+  using CV = ConvVec<CW>;
   static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "row layout");
 
   const int h = blockIdx.x, b = blockIdx.y;
@@ -123,6 +175,39 @@ __global__ __launch_bounds__((DecodeShape<D, TS>::THREADS)) void gdn_decode_kern
           reinterpret_cast<const typename SV::raw *>(Sblk + int64_t(r) * D + col0));
   }
 
+  // ---- conv over the head's q, k, v channels, CW channels per lane -------
+  __shared__ __attribute__((aligned(16))) float sy[3 * D];  // q | k | v of this head
+  uint16_t *crow = conv + (int64_t(a.layer) * slots + slot) * kConvRows * C;
+  const uint16_t *xb = a.x + int64_t(b) * C;
+  const int item = threadIdx.x;  // one CW-channel item per thread (ITEMS <= threads)
+  const bool conv_lane = item < ITEMS;
+  const int pt = item / (D / CW), jc = (item % (D / CW)) * CW;
+  const int64_t ch = int64_t(pt) * H * D + int64_t(h) * D + jc;
+  typename CV::raw r0v, r1v, r2v, xv;
+  u32x4 wv[CW / 2];  // weights [C][4]: the 4 taps of channels 2i and 2i+1 make up wv[i]
+  if (conv_lane) {  // issued right behind the state loads, before anything waits
+    r0v = *reinterpret_cast<const typename CV::raw *>(crow + ch);
+    r1v = *reinterpret_cast<const typename CV::raw *>(crow + C + ch);
+    r2v = *reinterpret_cast<const typename CV::raw *>(crow + 2 * C + ch);
+    xv = *reinterpret_cast<const typename CV::raw *>(xb + ch);
+    const u32x4 *wp = reinterpret_cast<const u32x4 *>(a.conv_w + ch * 4);
+#pragma unroll
+    for (int i = 0; i < CW / 2; ++i) wv[i] = wp[i];
+  }
+
+  // decay of this lane's columns and beta: loaded here, not behind the barrier
+  float al[VEC];
+  if (kAlphaMode == GDN_ALPHA_PER_CHANNEL) {
+    const float *ap = a.alpha + (int64_t(b) * H + h) * D + col0;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) al[e] = ap[e];
+  } else {
+    const float av = a.alpha[int64_t(b) * H + h];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) al[e] = av;
+  }
+  const float beta = a.beta[int64_t(b) * H + h];
+
   // ---- snapshot target --------------------------------------------------
   int track = 0;
   if (a.track_interval > 0 && a.track_slots && a.seq_len_after[b] % a.track_interval == 0) {
@@ -132,28 +217,15 @@ __global__ __launch_bounds__((DecodeShape<D, TS>::THREADS)) void gdn_decode_kern
       track = 0;
     }
   }
-
-  // ---- conv over the head's q, k, v channels, 8 channels per lane --------
-  __shared__ __attribute__((aligned(16))) float sy[3 * D];  // q | k | v of this head
-  uint16_t *crow = conv + (int64_t(a.layer) * slots + slot) * kConvRows * C;
   uint16_t *trow = track > 0 ? conv + (int64_t(a.layer) * slots + track) * kConvRows * C : nullptr;
-  const uint16_t *xb = a.x + int64_t(b) * C;
-  const int item = threadIdx.x;  // one 8-channel item per thread (ITEMS <= threads)
-  const bool conv_lane = item < ITEMS;
-  const int pt = item / (D / 8), j8 = (item % (D / 8)) * 8;
-  const int64_t ch = int64_t(pt) * H * D + int64_t(h) * D + j8;
-  u32x4 r1v, r2v, xv;
+
   if (conv_lane) {
-    const u32x4 r0v = *reinterpret_cast<const u32x4 *>(crow + ch);
-    r1v = *reinterpret_cast<const u32x4 *>(crow + C + ch);
-    r2v = *reinterpret_cast<const u32x4 *>(crow + 2 * C + ch);
-    xv = *reinterpret_cast<const u32x4 *>(xb + ch);
-    const u32x4 *wp = reinterpret_cast<const u32x4 *>(a.conv_w + ch * 4);
-    const u32x4 wv[4] = {wp[0], wp[1], wp[2], wp[3]};  // 4 taps of channels ch .. ch+7
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < CW; ++e) {
       const int sh = (e & 1) ? 16 : 0;
-      auto pick = [&](const u32x4 &v) { return __uint_as_float(((v[e >> 1] >> sh) & 0xffffu) << 16); };
+      auto pick = [&](const typename CV::raw &v) {
+        return __uint_as_float(((CV::word(v, e >> 1) >> sh) & 0xffffu) << 16);
+      };
       const u32x4 &w2 = wv[e >> 1];
       const int wb = (e & 1) * 2;
       float y = __uint_as_float(w2[wb] << 16) * pick(r0v);
@@ -161,18 +233,19 @@ __global__ __launch_bounds__((DecodeShape<D, TS>::THREADS)) void gdn_decode_kern
       y = fmaf(__uint_as_float(w2[wb + 1] << 16), pick(r2v), y);
       y = fmaf(__uint_as_float(w2[wb + 1] & 0xffff0000u), pick(xv), y);
       if (a.flags & GDN_F_CONV_SILU) y = y / (1.f + __expf(-y));
-      sy[pt * D + j8 + e] = y;
+      sy[pt * D + jc + e] = y;
     }
   }
   __syncthreads();  // every old conv row has been read; sy is complete
   if (conv_lane) {
-    *reinterpret_cast<u32x4 *>(crow + ch) = r1v;
-    *reinterpret_cast<u32x4 *>(crow + C + ch) = r2v;
-    *reinterpret_cast<u32x4 *>(crow + 2 * C + ch) = xv;
+    typedef typename CV::raw R;
+    *reinterpret_cast<R *>(crow + ch) = r1v;
+    *reinterpret_cast<R *>(crow + C + ch) = r2v;
+    *reinterpret_cast<R *>(crow + 2 * C + ch) = xv;
     if (trow) {
-      *reinterpret_cast<u32x4 *>(trow + ch) = r1v;
-      *reinterpret_cast<u32x4 *>(trow + C + ch) = r2v;
-      *reinterpret_cast<u32x4 *>(trow + 2 * C + ch) = xv;
+      *reinterpret_cast<R *>(trow + ch) = r1v;
+      *reinterpret_cast<R *>(trow + C + ch) = r2v;
+      *reinterpret_cast<R *>(trow + 2 * C + ch) = xv;
     }
   }
   const float *sq = sy, *sk = sy + D, *sv = sy + 2 * D;
@@ -193,22 +266,12 @@ __global__ __launch_bounds__((DecodeShape<D, TS>::THREADS)) void gdn_decode_kern
   for (int i = lane; i < D; i += 64) kq = fmaf(sk[i] * kinv, sq[i] * qinv, kq);
   kq = wave_sum(kq);
 
-  float kk[VEC], qq[VEC], al[VEC];
+  float kk[VEC], qq[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     kk[e] = sk[col0 + e] * kinv;
     qq[e] = sq[col0 + e] * qinv;
   }
-  if (kAlphaMode == GDN_ALPHA_PER_CHANNEL) {
-    const float *ap = a.alpha + (int64_t(b) * H + h) * D + col0;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) al[e] = ap[e];
-  } else {
-    const float av = a.alpha[int64_t(b) * H + h];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) al[e] = av;
-  }
-  const float beta = a.beta[int64_t(b) * H + h];
   TS *Tblk = track > 0 ? ssm + ((int64_t(a.layer) * slots + track) * H + h) * int64_t(D) * D : nullptr;
 
   // ---- the state stream --------------------------------------------------
@@ -225,11 +288,8 @@ __global__ __launch_bounds__((DecodeShape<D, TS>::THREADS)) void gdn_decode_kern
       pu = fmaf(s[e], kk[e], pu);
       pq = fmaf(s[e], qq[e], pq);
     }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) {
-      pu += __shfl_xor(pu, off, 64);
-      pq += __shfl_xor(pq, off, 64);
-    }
+    pu = group_sum<LPR>(pu);
+    pq = group_sum<LPR>(pq);
     if (on) {
       const float d = beta * (sv[r] - pu);
 #pragma unroll
