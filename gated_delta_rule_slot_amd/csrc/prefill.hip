@@ -53,6 +53,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPrepThreads = 1024;
 constexpr float kMidRange = 60.f;  // max |log2| of a factor on the diagonal fast path
+// A chunk takes the chunk-reference path when no 16-token block decays any channel
+// by more than 2^-kBlockSpan, so that e^{+-L} stays within 2^(+-4 kBlockSpan).
+constexpr float kBlockSpan = 24.f;
 
 // An MFMA 16x16x32 operand gives lane l the k indices 8*(l/16) + e, e < 8.  Where
 // an operand is built from two 16x16 accumulator tiles (which give lane l the
@@ -167,19 +170,37 @@ __device__ __forceinline__ void frag_store(char *base, int idx, int lane, const 
 }
 
 // =============================================================== prep kernel ==
+// Two layouts share one LDS array (fp32 words); the log2 decays, block totals, beta
+// and block flags sit in a common tail that both use.
 template <int D>
 struct PrepLds {
   static constexpr int KD = D < 32 ? 32 : D;
   static constexpr int DP = KD + 4;  // fp32 pitch of [t][c] arrays
   static constexpr int TP = 68;      // fp32 pitch of [v][t] and [t][i] arrays
+  // blockwise path: q, k, v^T, Diag(b) A, T and scratch in fp32
   static constexpr int RQ = (64 * DP > 64 * TP ? 64 * DP : 64 * TP);  // q, later T
   static constexpr int RK = 64 * DP;                                  // k, later g.k
-  static constexpr int RL = 64 * DP;                                  // log2 decays
   static constexpr int RV = D * TP;                                   // v^T
   static constexpr int RA = 64 * TP;                                  // Diag(b) A
   static constexpr int RP = 3 * 16 * 17;                              // 16x16 scratch per level block
-  static constexpr int OQ = 0, OK = OQ + RQ, OL = OK + RK, OV = OL + RL, OA = OV + RV,
-                       OP = OA + RA, OTOT = OP + RP, OB = OTOT + 4 * KD, OF = OB + 64, TOTAL = OF + 4;
+  static constexpr int OQ = 0, OK = OQ + RQ, OV = OK + RK, OA = OV + RV, OP = OA + RA,
+                       SLOW_END = OP + RP;
+  // chunk-reference path: bf16 hi/lo planes [64][KP] of P = k e^L, R = k e^-L and
+  // Q = q e^L; Diag(b) A and the diagonal inverses reuse the R planes (or follow
+  // the planes when those are too small), W reuses the Q planes, V the decays
+  static constexpr int KP = KD + 8;          // bf16 pitch of a plane row (16-byte rows)
+  static constexpr int PS = 64 * KP / 2;     // one plane in fp32 words
+  static constexpr int DPITCH = 20;          // fp32 pitch of a diagonal inverse row
+  static constexpr int RD = 4 * 16 * DPITCH;
+  static constexpr bool A_IN_R = 2 * PS >= 64 * TP + RD;
+  static constexpr int FPH = 0, FPL = PS, FRH = 2 * PS, FRL = 3 * PS, FQH = 4 * PS, FQL = 5 * PS;
+  static constexpr int FA = A_IN_R ? FRH : 6 * PS, FD = FA + 64 * TP, FW = FQH;
+  static constexpr int FAST_END = A_IN_R ? 6 * PS : FD + RD;
+  static_assert(64 * DP <= 2 * PS, "W fits the Q planes");
+  // common tail
+  static constexpr int RL = 64 * DP;                                  // log2 decays, later V (fast path)
+  static constexpr int OL = SLOW_END > FAST_END ? SLOW_END : FAST_END;
+  static constexpr int OTOT = OL + RL, OB = OTOT + 4 * KD, OF = OB + 64, TOTAL = OF + 4;
 };
 
 template <int D, int AMODE>
@@ -210,21 +231,18 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
   const int p0 = 64 * c - rg.off;  // request position of local token 0
 
   // ---- phase 1: causal conv + norms (waves 0..11), log2 decays + beta (12..15) ----
-  if constexpr (KD != D) {  // channel padding of q and k
-    for (int i = tid; i < 64 * (KD - D); i += kPrepThreads) {
-      const int t = i / (KD - D), cc = D + i % (KD - D);
-      sQ[t * DP + cc] = 0.f;
-      sK[t * DP + cc] = 0.f;
-    }
-  }
+  // The conv results stay in registers until the decays decide which path runs.
   constexpr int G = D / 8;                // 8-channel groups per head part
   constexpr int R = G >= 8 ? G / 4 : 1;   // consecutive tokens per conv item
   constexpr int NR = 64 / R;
   constexpr int CONV_ITEMS = 3 * NR * G;  // 768, or 384 when D = 16
   static_assert(CONV_ITEMS <= 768 && CONV_ITEMS % 64 == 0, "conv items must fill waves 0..11");
-  if (tid < CONV_ITEMS) {
-    const int g = tid % G, run = (tid / G) % NR, part = tid / (G * NR);
-    const int t0 = run * R;
+  const bool conv_thread = tid < CONV_ITEMS;
+  const int cg = tid % G, cpart = tid / (G * NR);
+  const int ct0 = ((tid / G) % NR) * R;
+  float y[R][8];
+  if (conv_thread) {
+    const int g = cg, part = cpart, t0 = ct0;
     const int64_t ch0 = int64_t(part) * H * D + int64_t(h) * D + 8 * g;
     const uint16_t *crow = ka.conv + (int64_t(a.layer) * ka.slots + slot) * kConvRows * C;
     u32x4 wr[4], xr[R + 3];
@@ -242,7 +260,6 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
     }
     const bool silu = (a.flags & GDN_F_CONV_SILU) != 0;
     const bool norm = part == 0 ? (a.flags & GDN_F_L2NORM_Q) != 0 : part == 1 ? (a.flags & GDN_F_L2NORM_K) != 0 : false;
-    float y[R][8];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int pos = p0 + t0 + r;
@@ -265,25 +282,6 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
         const float inv = 1.f / sqrtf(ss + 1e-6f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[r][e] *= inv;
-      }
-    }
-    if (part == 2) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float *dst = sV + (8 * g + e) * TP + t0;
-        if constexpr (R == 4) {
-          st4(dst, f32x4{y[0][e], y[1][e], y[2][e], y[3][e]});
-        } else {
-#pragma unroll
-          for (int r = 0; r < R; ++r) dst[r] = y[r][e];
-        }
-      }
-    } else {
-      float *base = part == 0 ? sQ : sK;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        st4(base + (t0 + r) * DP + 8 * g, f32x4{y[r][0], y[r][1], y[r][2], y[r][3]});
-        st4(base + (t0 + r) * DP + 8 * g + 4, f32x4{y[r][4], y[r][5], y[r][6], y[r][7]});
       }
     }
   } else if (wave >= 12) {
@@ -325,7 +323,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
       }
     }
     // cumulative inside the 16-token block: add the sums of the lower token quads
-    bool big = false;
+    bool big = false, wide = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float tot = cum[3][e];
@@ -336,9 +334,12 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
       const float l0 = __shfl(cum[0][e], co, 64), l7 = __shfl(cum[3][e], co + 16, 64),
                   l15 = __shfl(cum[3][e], co + 48, 64);
       big = big || (act && fmaxf(l0 - l7, l7 - l15) > kMidRange);
+      wide = wide || (act && -l15 > kBlockSpan);
     }
-    const bool any_big = __ballot(big) != 0;
-    if (lane == 0) sWF[m] = any_big ? 1 : 0;
+    const bool any_big = __ballot(big) != 0, any_wide = __ballot(wide) != 0;
+    // bit 0: the blockwise path evaluates this diagonal block exactly;
+    // bit 1: the block rules out the chunk-reference path
+    if (lane == 0) sWF[m] = (any_big ? 1 : 0) | (any_wide ? 2 : 0);
     if (act) {
 #pragma unroll
       for (int tok = 0; tok < 4; ++tok) {
@@ -354,9 +355,282 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
   }
   __syncthreads();
 
+  if (((sWF[0] | sWF[1] | sWF[2] | sWF[3]) & 2) == 0) {
+    // ====== chunk-reference path ================================================
+    // With L_t the log2 decay cumulated from the chunk start, G(t,i) = e^{L_t - L_i}
+    // factors exactly into P = k e^L and R = k e^-L, so A = P R^T, M = Q R^T with
+    // Q = q e^L, and g.K = P, g.Q = Q, G(63,.)K = R e^{L_63}.  The operands are
+    // rounded to hi/lo bf16 planes once, here, and every product reads them as is.
+    constexpr int KP = LY::KP;
+    __bf16 *pPh = reinterpret_cast<__bf16 *>(smem + LY::FPH), *pPl = reinterpret_cast<__bf16 *>(smem + LY::FPL);
+    __bf16 *pRh = reinterpret_cast<__bf16 *>(smem + LY::FRH), *pRl = reinterpret_cast<__bf16 *>(smem + LY::FRL);
+    __bf16 *pQh = reinterpret_cast<__bf16 *>(smem + LY::FQH), *pQl = reinterpret_cast<__bf16 *>(smem + LY::FQL);
+    float *fA = smem + LY::FA, *fD = smem + LY::FD, *fW = smem + LY::FW;
+    float *fV = sL;  // V over the decays once the planes are built
+    constexpr int DPT = LY::DPITCH;
+
+    // ---- F1: planes from the conv outputs ----------------------------------
+    if constexpr (KD != D) {  // channel padding of P, R, Q
+      for (int i = tid; i < 64 * (KD - D); i += kPrepThreads) {
+        const int t = i / (KD - D), cc = D + i % (KD - D);
+        const __bf16 z = static_cast<__bf16>(0.f);
+        pPh[t * KP + cc] = z;
+        pPl[t * KP + cc] = z;
+        pRh[t * KP + cc] = z;
+        pRl[t * KP + cc] = z;
+        pQh[t * KP + cc] = z;
+        pQl[t * KP + cc] = z;
+      }
+    }
+    if (conv_thread && cpart < 2) {
+      const int m = ct0 >> 4;  // the item's tokens share one 16-token block
+      f32x4 pre0 = {0.f, 0.f, 0.f, 0.f}, pre1 = pre0;
+      for (int kb = 0; kb < m; ++kb) {
+        pre0 += ld4(sTot + kb * KD + 8 * cg);
+        pre1 += ld4(sTot + kb * KD + 8 * cg + 4);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int t = ct0 + r;
+        const f32x4 l0 = pre0 + ld4(sL + t * DP + 8 * cg), l1 = pre1 + ld4(sL + t * DP + 8 * cg + 4);
+        float lam[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lam[j] = l0[j];
+          lam[4 + j] = l1[j];
+        }
+        float u[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = y[r][e] * fexp2(lam[e]);
+        const Split su = split8(u);
+        const int o = t * KP + 8 * cg;
+        if (cpart == 0) {
+          *reinterpret_cast<bf16x8 *>(pQh + o) = su.hi;
+          *reinterpret_cast<bf16x8 *>(pQl + o) = su.lo;
+        } else {
+          *reinterpret_cast<bf16x8 *>(pPh + o) = su.hi;
+          *reinterpret_cast<bf16x8 *>(pPl + o) = su.lo;
+          float w[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] = y[r][e] * fexp2(-lam[e]);
+          const Split sw = split8(w);
+          *reinterpret_cast<bf16x8 *>(pRh + o) = sw.hi;
+          *reinterpret_cast<bf16x8 *>(pRl + o) = sw.lo;
+        }
+      }
+    }
+    __syncthreads();
+    if (conv_thread && cpart == 2) {  // V over the decays, which are no longer read
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        st4(fV + (ct0 + r) * DP + 8 * cg, f32x4{y[r][0], y[r][1], y[r][2], y[r][3]});
+        st4(fV + (ct0 + r) * DP + 8 * cg + 4, f32x4{y[r][4], y[r][5], y[r][6], y[r][7]});
+      }
+    }
+
+    // ---- F2: A^T, M^T tiles (waves 0..9); g.Q, G(63,.)K, g_63 records (10..15) ----
+    f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+    const int pi = wave;  // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
+    const int pm = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
+    const int pn = pi - pm * (pm + 1) / 2;
+    if (wave < 10) {
+      const int i = 16 * pn + r16, t = 16 * pm + r16;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int c0 = 32 * ks + 8 * g4;
+        Split Ra, Pb, Qb;
+        Ra.hi = *reinterpret_cast<const bf16x8 *>(pRh + i * KP + c0);
+        Ra.lo = *reinterpret_cast<const bf16x8 *>(pRl + i * KP + c0);
+        Pb.hi = *reinterpret_cast<const bf16x8 *>(pPh + t * KP + c0);
+        Pb.lo = *reinterpret_cast<const bf16x8 *>(pPl + t * KP + c0);
+        Qb.hi = *reinterpret_cast<const bf16x8 *>(pQh + t * KP + c0);
+        Qb.lo = *reinterpret_cast<const bf16x8 *>(pQl + t * KP + c0);
+        accA = mfma3(Ra, Pb, accA);
+        accM = mfma3(Ra, Qb, accM);
+      }
+    } else {
+      const int rel = tid - 640;
+      for (int it = rel; it < 4 * NKS * 64; it += 384) {  // g.Q: the Q planes in fragment order
+        const int ln = it & 63, tb = (it >> 6) & 3, ks = it >> 8;
+        const int o = (16 * tb + (ln & 15)) * KP + 32 * ks + 4 * (ln >> 4);  // channels o, o+16
+        Split sp;
+        sp.hi = __builtin_shufflevector(*reinterpret_cast<const bf16x4 *>(pQh + o),
+                                        *reinterpret_cast<const bf16x4 *>(pQh + o + 16), 0, 1, 2, 3, 4, 5, 6, 7);
+        sp.lo = __builtin_shufflevector(*reinterpret_cast<const bf16x4 *>(pQl + o),
+                                        *reinterpret_cast<const bf16x4 *>(pQl + o + 16), 0, 1, 2, 3, 4, 5, 6, 7);
+        frag_store(rec + RC::QF, tb * NKS + ks, ln, sp);
+      }
+      for (int it = rel; it < NCB * 2 * 64; it += 384) {  // G(63,.)K = R e^{L_63}, tokens along k
+        const int ln = it & 63, ksp = (it >> 6) & 1, cb = it >> 7;
+        const int cc = 16 * cb + (ln & 15), g = ln >> 4;
+        float tot = 0.f;
+        for (int kb = 0; kb < 4; ++kb) tot += sTot[kb * KD + cc];
+        const float g63 = fexp2(tot);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int o = (32 * ksp + pk(g, e)) * KP + cc;
+          v[e] = (static_cast<float>(pRh[o]) + static_cast<float>(pRl[o])) * g63;
+        }
+        frag_store(rec + RC::KF, cb * 2 + ksp, ln, split8(v));
+      }
+      // M fragments (tb 0 and 1, ks' 1) lie above the diagonal; the scan multiplies
+      // them anyway to keep its loop free of branches, so store zeros
+      for (int it = rel; it < 256; it += 384) {
+        const int idx = (it >> 7) ? 3 : 1, plane = (it >> 6) & 1, ln = it & 63;
+        *reinterpret_cast<u32x4 *>(rec + RC::MF + size_t(2 * idx + plane) * 1024 + ln * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+      float *recGC = reinterpret_cast<float *>(rec + RC::GC);
+      for (int cc = rel; cc < D; cc += 384) {
+        float tot = 0.f;
+        for (int kb = 0; kb < 4; ++kb) tot += sTot[kb * KD + cc];
+        recGC[cc] = fexp2(tot);
+      }
+    }
+    __syncthreads();  // the R and Q planes are free from here on
+    if (wave < 10) {
+      // lane (t, g4) holds A[t][16n + 4g4 + j] and M[t][16n + 4g4 + j]
+      const bool diag = pm == pn;
+      const int t = 16 * pm + r16;
+      const float bt = sB[t];
+      f32x4 av;
+      float mv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ii = 16 * pn + 4 * g4 + j;
+        av[j] = (!diag || ii < t) ? bt * accA[j] : 0.f;  // Diag(b) A
+        mv[j] = (!diag || ii <= t) ? accM[j] : 0.f;
+      }
+      st4(fA + t * TP + 16 * pn + 4 * g4, av);
+      bf16x4 mh, ml;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const __bf16 hv = static_cast<__bf16>(mv[j]);
+        mh[j] = hv;
+        ml[j] = static_cast<__bf16>(mv[j] - static_cast<float>(hv));
+      }
+      char *mf = rec + RC::MF + size_t(2 * (2 * pm + (pn >> 1))) * 1024 + lane * 16 + (pn & 1) * 8;
+      *reinterpret_cast<bf16x4 *>(mf) = mh;
+      *reinterpret_cast<bf16x4 *>(mf + 1024) = ml;
+      if (diag && !(pm & 1)) {  // tile (m, m+1) above the diagonal is zero
+        const bf16x4 z = {static_cast<__bf16>(0.f), static_cast<__bf16>(0.f), static_cast<__bf16>(0.f),
+                          static_cast<__bf16>(0.f)};
+        *reinterpret_cast<bf16x4 *>(mf + 8) = z;
+        *reinterpret_cast<bf16x4 *>(mf + 1024 + 8) = z;
+      }
+    }
+    __syncthreads();
+
+    // ---- F3: inverses D_m of the unit lower-triangular diagonal blocks --------
+    if (wave == 0) {
+      const int m = lane >> 4, j = lane & 15;  // lane: column j of block m
+      float x[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        float v = (t == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 0; i < t; ++i) v = fmaf(-fA[(16 * m + t) * TP + 16 * m + i], x[i], v);
+        x[t] = v;
+        fD[(16 * m + t) * DPT + j] = v;
+      }
+    } else {
+      if constexpr (KD != D) {  // W's channel padding (the solve writes channels < D)
+        for (int i = tid - 64; i < 64 * (KD - D); i += kPrepThreads - 64) {
+          const int t = i / (KD - D), cc = D + i % (KD - D);
+          fW[t * DP + cc] = 0.f;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- F4: (I + Diag(b) A) X = Diag(b) [V | g.K] by block forward substitution,
+    //      X_m = D_m (Y_m - sum_{k<m} N_mk X_k).  Wave w owns one 16-column tile: V
+    //      tiles give U, g.K tiles give W.  The 16-row blocks of X stay in the wave's
+    //      accumulators and enter the next products as operands whose first four k
+    //      values are the block (the rest zero), in the order of the pk mapping.
+    if (wave < 2 * NCB) {
+      const bool isw = wave >= NCB;
+      const int tile = isw ? wave - NCB : wave;
+      const int col = 16 * tile + r16;
+      auto pad4 = [](const f32x4 &x) {
+        float v[8] = {x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f};
+        return split8(v);
+      };
+      f32x4 X[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4 acc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * m + 4 * g4 + j;
+          const float yv = isw ? static_cast<float>(pPh[t * KP + col]) + static_cast<float>(pPl[t * KP + col])
+                               : fV[t * DP + col];
+          acc[j] = sB[t] * yv;
+        }
+#pragma unroll
+        for (int k = 0; k < m; ++k)
+          acc = mfma3(pad4(-ld4(fA + (16 * m + r16) * TP + 16 * k + 4 * g4)), pad4(X[k]), acc);
+        X[m] = mfma3(pad4(ld4(fD + (16 * m + r16) * DPT + 4 * g4)), pad4(acc), f32x4{0.f, 0.f, 0.f, 0.f});
+        if (!isw) {
+          *reinterpret_cast<f32x4 *>(rec + RC::UF + size_t(m * NCB + tile) * 1024 + lane * 16) = X[m];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) fW[(16 * m + 4 * g4 + j) * DP + col] = X[m][j];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- F5: -W fragments ------------------------------------------------------
+    for (int it = tid; it < 4 * NKS * 64; it += kPrepThreads) {
+      const int ln = it & 63, tb = (it >> 6) & 3, ks = it >> 8;
+      const int o = (16 * tb + (ln & 15)) * DP + 32 * ks + 4 * (ln >> 4);  // channels o, o+16
+      const f32x4 w0 = ld4(fW + o), w1 = ld4(fW + o + 16);
+      float w[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[j] = -w0[j];
+        w[4 + j] = -w1[j];
+      }
+      frag_store(rec + RC::WF, tb * NKS + ks, ln, split8(w));
+    }
+    return;
+  }
+
+  // ====== blockwise path (any decay) ==============================================
+  if constexpr (KD != D) {  // channel padding of q and k
+    for (int i = tid; i < 64 * (KD - D); i += kPrepThreads) {
+      const int t = i / (KD - D), cc = D + i % (KD - D);
+      sQ[t * DP + cc] = 0.f;
+      sK[t * DP + cc] = 0.f;
+    }
+  }
+  if (conv_thread) {
+    if (cpart == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float *dst = sV + (8 * cg + e) * TP + ct0;
+        if constexpr (R == 4) {
+          st4(dst, f32x4{y[0][e], y[1][e], y[2][e], y[3][e]});
+        } else {
+#pragma unroll
+          for (int r = 0; r < R; ++r) dst[r] = y[r][e];
+        }
+      }
+    } else {
+      float *base = cpart == 0 ? sQ : sK;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        st4(base + (ct0 + r) * DP + 8 * cg, f32x4{y[r][0], y[r][1], y[r][2], y[r][3]});
+        st4(base + (ct0 + r) * DP + 8 * cg + 4, f32x4{y[r][4], y[r][5], y[r][6], y[r][7]});
+      }
+    }
+  }
+  __syncthreads();
+
   if (wave < 10) {
     // ---- phase 2a: A^T and M^T tiles of pair (m, n), n <= m (waves 0..9) ----------
-    const int flags = sWF[0] | (sWF[1] << 1) | (sWF[2] << 2) | (sWF[3] << 3);
+    const int flags = (sWF[0] & 1) | ((sWF[1] & 1) << 1) | ((sWF[2] & 1) << 2) | ((sWF[3] & 1) << 3);
     const int pi = wave;  // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
     const int m = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
     const int n = pi - m * (m + 1) / 2;
