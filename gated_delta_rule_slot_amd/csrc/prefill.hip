@@ -151,6 +151,29 @@ __device__ __forceinline__ f32x4 mfma3(const Split &a, const Split &b, f32x4 c) 
   return c;
 }
 
+// k = 16 products: lane l holds k = 4(l/16) + e of row (A) / column (B) l % 16,
+// which is exactly how a lane holds four rows of a 16x16 accumulator tile
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+struct Split4 {
+  s16x4 hi, lo;
+};
+__device__ __forceinline__ Split4 split4s(const f32x4 &v) {
+  bf16x4 h, l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const __bf16 hv = static_cast<__bf16>(v[j]);
+    h[j] = hv;
+    l[j] = static_cast<__bf16>(v[j] - static_cast<float>(hv));
+  }
+  return Split4{__builtin_bit_cast(s16x4, h), __builtin_bit_cast(s16x4, l)};
+}
+__device__ __forceinline__ f32x4 mfma3k16(const Split4 &a, const Split4 &b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, c, 0, 0, 0);
+  return c;
+}
+
 __device__ __forceinline__ float bf16_elem(const u32x4 &v, int e) {
   const uint32_t w = v[e >> 1];
   return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -192,10 +215,11 @@ struct PrepLds {
   static constexpr int PS = 64 * KP / 2;     // one plane in fp32 words
   static constexpr int DPITCH = 20;          // fp32 pitch of a diagonal inverse row
   static constexpr int RD = 4 * 16 * DPITCH;
-  static constexpr bool A_IN_R = 2 * PS >= 64 * TP + RD;
+  static constexpr int RN = 6 * 64 * 4;      // -N_mk (m > k) as split k = 16 operand fragments
+  static constexpr bool A_IN_R = 2 * PS >= 64 * TP + RD + RN;
   static constexpr int FPH = 0, FPL = PS, FRH = 2 * PS, FRL = 3 * PS, FQH = 4 * PS, FQL = 5 * PS;
-  static constexpr int FA = A_IN_R ? FRH : 6 * PS, FD = FA + 64 * TP, FW = FQH;
-  static constexpr int FAST_END = A_IN_R ? 6 * PS : FD + RD;
+  static constexpr int FA = A_IN_R ? FRH : 6 * PS, FD = FA + 64 * TP, FN = FD + RD, FW = FQH;
+  static constexpr int FAST_END = A_IN_R ? 6 * PS : FN + RN;
   static_assert(64 * DP <= 2 * PS, "W fits the Q planes");
   // common tail
   static constexpr int RL = 64 * DP;                                  // log2 decays, later V (fast path)
@@ -366,6 +390,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
     __bf16 *pRh = reinterpret_cast<__bf16 *>(smem + LY::FRH), *pRl = reinterpret_cast<__bf16 *>(smem + LY::FRL);
     __bf16 *pQh = reinterpret_cast<__bf16 *>(smem + LY::FQH), *pQl = reinterpret_cast<__bf16 *>(smem + LY::FQL);
     float *fA = smem + LY::FA, *fD = smem + LY::FD, *fW = smem + LY::FW;
+    s16x4 *fN = reinterpret_cast<s16x4 *>(smem + LY::FN);  // [pair][lane][hi, lo]
     float *fV = sL;  // V over the decays once the planes are built
     constexpr int DPT = LY::DPITCH;
 
@@ -533,9 +558,16 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
         x[t] = v;
         fD[(16 * m + t) * DPT + j] = v;
       }
+    } else if (wave <= 6) {
+      // -N_mk for the six blocks below the diagonal, split once for every wave
+      const int q = wave - 1;
+      const int m = q < 1 ? 1 : q < 3 ? 2 : 3, k = q - m * (m - 1) / 2;
+      const Split4 nf = split4s(-ld4(fA + (16 * m + r16) * TP + 16 * k + 4 * g4));
+      fN[(q * 64 + lane) * 2] = nf.hi;
+      fN[(q * 64 + lane) * 2 + 1] = nf.lo;
     } else {
       if constexpr (KD != D) {  // W's channel padding (the solve writes channels < D)
-        for (int i = tid - 64; i < 64 * (KD - D); i += kPrepThreads - 64) {
+        for (int i = tid - 448; i < 64 * (KD - D); i += kPrepThreads - 448) {
           const int t = i / (KD - D), cc = D + i % (KD - D);
           fW[t * DP + cc] = 0.f;
         }
@@ -546,17 +578,12 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
     // ---- F4: (I + Diag(b) A) X = Diag(b) [V | g.K] by block forward substitution,
     //      X_m = D_m (Y_m - sum_{k<m} N_mk X_k).  Wave w owns one 16-column tile: V
     //      tiles give U, g.K tiles give W.  The 16-row blocks of X stay in the wave's
-    //      accumulators and enter the next products as operands whose first four k
-    //      values are the block (the rest zero), in the order of the pk mapping.
+    //      accumulators and enter the next k = 16 products as operands unchanged.
     if (wave < 2 * NCB) {
       const bool isw = wave >= NCB;
       const int tile = isw ? wave - NCB : wave;
       const int col = 16 * tile + r16;
-      auto pad4 = [](const f32x4 &x) {
-        float v[8] = {x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f};
-        return split8(v);
-      };
-      f32x4 X[4];
+      Split4 XS[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         f32x4 acc;
@@ -568,14 +595,19 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
           acc[j] = sB[t] * yv;
         }
 #pragma unroll
-        for (int k = 0; k < m; ++k)
-          acc = mfma3(pad4(-ld4(fA + (16 * m + r16) * TP + 16 * k + 4 * g4)), pad4(X[k]), acc);
-        X[m] = mfma3(pad4(ld4(fD + (16 * m + r16) * DPT + 4 * g4)), pad4(acc), f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int k = 0; k < m; ++k) {
+          const int q = m * (m - 1) / 2 + k;
+          const Split4 nf{fN[(q * 64 + lane) * 2], fN[(q * 64 + lane) * 2 + 1]};
+          acc = mfma3k16(nf, XS[k], acc);
+        }
+        const f32x4 X = mfma3k16(split4s(ld4(fD + (16 * m + r16) * DPT + 4 * g4)), split4s(acc),
+                                 f32x4{0.f, 0.f, 0.f, 0.f});
+        XS[m] = split4s(X);
         if (!isw) {
-          *reinterpret_cast<f32x4 *>(rec + RC::UF + size_t(m * NCB + tile) * 1024 + lane * 16) = X[m];
+          *reinterpret_cast<f32x4 *>(rec + RC::UF + size_t(m * NCB + tile) * 1024 + lane * 16) = X;
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) fW[(16 * m + 4 * g4 + j) * DP + col] = X[m][j];
+          for (int j = 0; j < 4; ++j) fW[(16 * m + 4 * g4 + j) * DP + col] = X[j];
         }
       }
     }
