@@ -77,6 +77,14 @@ def lib(precision: str = "f64"):
                                         ct.c_int32, _i32p, _i32p]
     L.oracle_restore_slots.argtypes = [ct.POINTER(_Pool), ct.c_int32,
                                        ct.POINTER(RestoreOp), _i64p]
+    L.oracle_verify_tree.argtypes = [
+        ct.POINTER(_Pool), ct.c_int32, ct.c_int32, ct.c_int32, _i32p, _i32p, _u16p, _u16p,
+        _f32p, ct.c_int32, _f32p, ct.c_float, ct.c_uint32, _u16p, ct.c_void_p, _u16p, _f64p,
+    ]
+    L.oracle_accept_scatter.argtypes = [
+        ct.POINTER(_Pool), ct.c_int32, ct.c_int32, ct.c_int32, _i32p, _i32p, _i32p, _i32p,
+        ct.c_int32, _i32p, _i32p, ct.c_void_p, _u16p,
+    ]
     L.oracle_recurrence_head.argtypes = [ct.c_int32] * 3 + [_f64p] * 5 + [ct.c_double, _f64p, _f64p]
     L.oracle_recurrence_head.restype = None
     L.oracle_chunked_head_f64.argtypes = [ct.c_int32] * 4 + [_f64p] * 5 + [ct.c_double, _f64p, _f64p]
@@ -234,6 +242,66 @@ def restore_slots(pool: Pool, ops, has_initial_state, precision="f64"):
     if err & 4:
         raise ValueError("oracle_restore_slots: bad argument")
     return hi
+
+
+def node_buffers(pool: Pool, batch, nodes):
+    """Zeroed per-node buffers of a draft tree: (node_ssm [B][T][H][V][K] in the
+    pool's ssm dtype, node_conv uint16 [B][T][3][C])."""
+    dt = np.float32 if pool.ssm_dtype == SSM_F32 else np.uint16
+    return (np.zeros((batch, nodes, pool.heads, pool.head_v, pool.head_k), dtype=dt),
+            np.zeros((batch, nodes, 3, pool.channels), dtype=np.uint16))
+
+
+def verify_tree(pool: Pool, layer, slot_table, parent, x, conv_w, alpha, alpha_mode, beta,
+                scale=1.0, flags=L2NORM_K, exact=False, precision="f64"):
+    """Verify a draft tree per request without touching the live slots.
+
+    ``parent`` int [B][T] (-1 = the live slot), ``x`` uint16 [B][T][C], ``alpha``
+    [B][T][H] or [B][T][H][K], ``beta`` [B][T][H].  Returns ``(out[B,T,H,V],
+    node_ssm, node_conv, err)``, plus ``out_exact`` with ``exact=True``."""
+    st = _c(slot_table, np.int32)
+    par = _c(parent, np.int32)
+    B, T = par.shape
+    if st.shape != (B,):
+        raise ValueError("slot_table must have one entry per request")
+    H, V = pool.heads, pool.head_v
+    xs, w = _c(x, np.uint16), _c(conv_w, np.uint16)
+    a, bt = _c(alpha, np.float32), _c(beta, np.float32)
+    out = np.zeros((B, T, H, V), dtype=np.uint16)
+    oe = np.zeros((B, T, H, V), dtype=np.float64) if exact else None
+    ns, nc = node_buffers(pool, B, T)
+    ps = pool._struct()
+    err = lib(precision).oracle_verify_tree(
+        ct.byref(ps), layer, B, T, _p(st, _i32p), _p(par, _i32p), _p(xs, _u16p), _p(w, _u16p),
+        _p(a, _f32p), alpha_mode, _p(bt, _f32p), scale, flags, _p(out, _u16p),
+        ns.ctypes.data_as(ct.c_void_p), _p(nc, _u16p), _p(oe, _f64p))
+    if err & 4:
+        raise ValueError("oracle_verify_tree: bad argument")
+    return (out, ns, nc, err, oe) if exact else (out, ns, nc, err)
+
+
+def accept_scatter(pool: Pool, layer, slot_table, parent, accepted, node_ssm, node_conv,
+                   seq_len_before=None, track_interval=0, track_slots=None,
+                   next_track_idx=None, precision="f64"):
+    """Copy each request's accepted node into its live slot (modifies ``pool``)
+    and, across a multiple of ``track_interval``, into its ping-pong track slot.
+    Returns the error bits."""
+    st = _c(slot_table, np.int32)
+    par = _c(parent, np.int32)
+    B, T = par.shape
+    acc = _c(accepted, np.int32)
+    sb = _c(seq_len_before if seq_len_before is not None else np.zeros(B), np.int32)
+    ts = _c(track_slots, np.int32) if track_slots is not None else None
+    nt = _c(next_track_idx, np.int32) if next_track_idx is not None else None
+    ns, nc = np.ascontiguousarray(node_ssm), _c(node_conv, np.uint16)
+    ps = pool._struct()
+    err = lib(precision).oracle_accept_scatter(
+        ct.byref(ps), layer, B, T, _p(st, _i32p), _p(par, _i32p), _p(acc, _i32p), _p(sb, _i32p),
+        track_interval, _p(ts, _i32p), _p(nt, _i32p), ns.ctypes.data_as(ct.c_void_p),
+        _p(nc, _u16p))
+    if err & 4:
+        raise ValueError("oracle_accept_scatter: bad argument")
+    return err
 
 
 def recurrence_head(q, k, v, alpha, beta, S0, scale=1.0, precision="f64"):

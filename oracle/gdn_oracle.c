@@ -292,6 +292,55 @@ static void store_head(const unit_ctx *u, int slot, int h, const real *S, real R
     for (int i = 0; i < nchan; ++i) cb[(size_t)j * u->C + chan[i]] = oracle_bf16_round((double)R[i][j]);
 }
 
+/* One token of head h: causal conv over [R0, R1, R2, x_t] (tap 3 is the current
+ * token) with the rows then shifted to [R1, R2, x_t], optional SiLU, key (and
+ * query) normalisation, then the recurrence.  y holds the 2K+V conv outputs. */
+static void step_token(const unit_ctx *u, const size_t *chan, int nchan, real *S,
+                       real (*R)[CONV_ROWS], const uint16_t *xt, const float *alpha,
+                       int alpha_mode, real beta, real *y, real *a, real *o) {
+  const int K = u->K, V = u->V;
+  for (int i = 0; i < nchan; ++i) {
+    const uint16_t *w = u->conv_w + chan[i] * CONV_TAPS;
+    real xi = widen(xt[chan[i]]);
+    real acc = 0;
+    acc += widen(w[0]) * R[i][0];
+    acc += widen(w[1]) * R[i][1];
+    acc += widen(w[2]) * R[i][2];
+    acc += widen(w[3]) * xi;
+    if (u->flags & ORACLE_CONV_SILU) acc = acc / (1 + exp(-acc));
+    y[i] = acc;
+    R[i][0] = R[i][1];
+    R[i][1] = R[i][2];
+    R[i][2] = xi;
+  }
+  real *q = y, *k = y + K, *v = y + 2 * K;
+  if (u->flags & ORACLE_L2NORM_K) {
+    real ss = 0;
+    for (int c = 0; c < K; ++c) ss += k[c] * k[c];
+    real inv = 1 / sqrt(ss + (real)L2_EPS);
+    for (int c = 0; c < K; ++c) k[c] = k[c] * inv;
+  }
+  if (u->flags & ORACLE_L2NORM_Q) {
+    real ss = 0;
+    for (int c = 0; c < K; ++c) ss += q[c] * q[c];
+    real inv = 1 / sqrt(ss + (real)L2_EPS);
+    for (int c = 0; c < K; ++c) q[c] = q[c] * inv;
+  }
+  /* alpha points at this (token, head): one value or K channel values */
+  for (int c = 0; c < K; ++c) a[c] = alpha_mode == ORACLE_ALPHA_PER_CHANNEL ? (real)alpha[c] : (real)alpha[0];
+  token_step(K, V, S, q, k, v, a, beta, u->scale, o);
+}
+
+/* The head's channels of x / conv rows: q, then k, then v. */
+static size_t *head_channels(const unit_ctx *u, int h) {
+  const int K = u->K, V = u->V, H = u->H;
+  size_t *chan = malloc(sizeof(size_t) * (2 * K + V));
+  for (int i = 0; i < K; ++i) chan[i] = (size_t)h * K + i;                    /* q */
+  for (int i = 0; i < K; ++i) chan[K + i] = (size_t)H * K + (size_t)h * K + i; /* k */
+  for (int i = 0; i < V; ++i) chan[2 * K + i] = (size_t)2 * H * K + (size_t)h * V + i; /* v */
+  return chan;
+}
+
 /* Fold n tokens (rows x[0..n)) of one request into head h. Returns error bits. */
 static int fold_head(const unit_ctx *u, int h, int live_slot, int warm, int32_t n,
                      const uint16_t *x, const float *alpha, int alpha_mode,
@@ -300,10 +349,7 @@ static int fold_head(const unit_ctx *u, int h, int live_slot, int warm, int32_t 
   const int K = u->K, V = u->V, H = u->H;
   const int nchan = 2 * K + V;
   int err = 0;
-  size_t *chan = malloc(sizeof(size_t) * nchan);
-  for (int i = 0; i < K; ++i) chan[i] = (size_t)h * K + i;                    /* q */
-  for (int i = 0; i < K; ++i) chan[K + i] = (size_t)H * K + (size_t)h * K + i; /* k */
-  for (int i = 0; i < V; ++i) chan[2 * K + i] = (size_t)2 * H * K + (size_t)h * V + i; /* v */
+  size_t *chan = head_channels(u, h);
 
   real *S = malloc(sizeof(real) * (size_t)V * K);
   real (*R)[CONV_ROWS] = malloc(sizeof(real) * CONV_ROWS * nchan);
@@ -326,39 +372,9 @@ static int fold_head(const unit_ctx *u, int h, int live_slot, int warm, int32_t 
 
   int boundaries = 0;
   for (int32_t t = 0; t < n; ++t) {
-    const uint16_t *xt = x + (size_t)t * u->C;
-    /* causal conv over [R0, R1, R2, x_t]; tap 3 is the current token */
-    for (int i = 0; i < nchan; ++i) {
-      const uint16_t *w = u->conv_w + chan[i] * CONV_TAPS;
-      real xi = widen(xt[chan[i]]);
-      real acc = 0;
-      acc += widen(w[0]) * R[i][0];
-      acc += widen(w[1]) * R[i][1];
-      acc += widen(w[2]) * R[i][2];
-      acc += widen(w[3]) * xi;
-      if (u->flags & ORACLE_CONV_SILU) acc = acc / (1 + exp(-acc));
-      y[i] = acc;
-      R[i][0] = R[i][1];
-      R[i][1] = R[i][2];
-      R[i][2] = xi;
-    }
-    real *q = y, *k = y + K, *v = y + 2 * K;
-    if (u->flags & ORACLE_L2NORM_K) {
-      real ss = 0;
-      for (int c = 0; c < K; ++c) ss += k[c] * k[c];
-      real inv = 1 / sqrt(ss + (real)L2_EPS);
-      for (int c = 0; c < K; ++c) k[c] = k[c] * inv;
-    }
-    if (u->flags & ORACLE_L2NORM_Q) {
-      real ss = 0;
-      for (int c = 0; c < K; ++c) ss += q[c] * q[c];
-      real inv = 1 / sqrt(ss + (real)L2_EPS);
-      for (int c = 0; c < K; ++c) q[c] = q[c] * inv;
-    }
-    for (int c = 0; c < K; ++c)
-      a[c] = alpha_mode == ORACLE_ALPHA_PER_CHANNEL ? (real)alpha[((size_t)t * H + h) * K + c]
-                                                    : (real)alpha[(size_t)t * H + h];
-    token_step(K, V, S, q, k, v, a, (real)beta[(size_t)t * H + h], u->scale, o);
+    const float *at = alpha + ((size_t)t * H + h) * (alpha_mode == ORACLE_ALPHA_PER_CHANNEL ? K : 1);
+    step_token(u, chan, nchan, S, R, x + (size_t)t * u->C, at, alpha_mode,
+               (real)beta[(size_t)t * H + h], y, a, o);
     for (int r = 0; r < V; ++r) {
       size_t oi = ((size_t)t * H + h) * V + r;
       out[oi] = oracle_bf16_round((double)o[r]);
@@ -484,6 +500,159 @@ int oracle_decode_step(const oracle_pool *pool, int32_t layer, int32_t batch,
                        beta + (size_t)b * H, out + (size_t)b * H * u.V,
                        out_exact ? out_exact + (size_t)b * H * u.V : NULL, se, rule);
     }
+  }
+  return err;
+}
+
+/* ------------------------------------------------- speculative verify ---- */
+
+/* A draft tree is valid when every parent is -1 (the live state) or an earlier
+ * node, so that visiting nodes in index order visits parents first. */
+static int tree_ok(const int32_t *parent, int32_t nodes) {
+  for (int32_t n = 0; n < nodes; ++n)
+    if (parent[n] < -1 || parent[n] >= n) return 0;
+  return 1;
+}
+
+static unsigned char *node_ssm_block(const oracle_pool *p, void *node_ssm, int32_t nodes, int b, int n) {
+  return (unsigned char *)node_ssm + ((size_t)b * nodes + n) * ssm_block_elems(p) * ssm_esize(p);
+}
+static uint16_t *node_conv_block(const oracle_pool *p, uint16_t *node_conv, int32_t nodes, int b, int n) {
+  return node_conv + ((size_t)b * nodes + n) * CONV_ROWS * conv_channels(p);
+}
+
+/* Verify a draft tree for one layer without updating the live slot (page
+ * "SGLang之MambaRadixCache机制", section 8.3: disable_state_update, one result per
+ * draft position into an intermediate buffer; section 9.6: retrieve_parent_token,
+ * parent before child, parent -1 reads the main state).  Node n of request b
+ * starts from its parent's stored state and conv rows (the live slot's for -1),
+ * takes token x[b][n], and stores its state (rounded to the pool dtype) and conv
+ * rows into node_ssm[b][n], node_conv[b][n]; out[b][n] gets o.  Shapes: parent
+ * [B][T], x [B][T][C], alpha [B][T][H] or [B][T][H][K], beta [B][T][H], out
+ * [B][T][H][V], node_ssm [B][T][H][V][K] (pool ssm dtype), node_conv [B][T][3][C].
+ * A request with an invalid tree or live slot gets zero outputs and no node
+ * writes; error bits 8 (tree) and 1 (live slot >= slots). */
+int oracle_verify_tree(const oracle_pool *pool, int32_t layer, int32_t batch, int32_t nodes,
+                       const int32_t *slot_table, const int32_t *parent, const uint16_t *x,
+                       const uint16_t *conv_w, const float *alpha, int32_t alpha_mode,
+                       const float *beta, float scale, uint32_t flags, uint16_t *out,
+                       void *node_ssm, uint16_t *node_conv, double *out_exact) {
+  if (!pool_ok(pool, layer) || batch < 0 || nodes < 1) return 4;
+  unit_ctx u = {pool, layer, pool->head_k, pool->head_v, pool->heads, conv_channels(pool),
+                conv_w, (real)scale, flags};
+  const int H = pool->heads, K = u.K, V = u.V, nchan = 2 * K + V;
+  const size_t aw = alpha_mode == ORACLE_ALPHA_PER_CHANNEL ? (size_t)K : 1;
+  int err = 0;
+#pragma omp parallel for collapse(2) reduction(| : err) schedule(dynamic)
+  for (int b = 0; b < batch; ++b) {
+    for (int h = 0; h < H; ++h) {
+      const int32_t *par = parent + (size_t)b * nodes;
+      const int slot = slot_table[b];
+      const int ok_tree = tree_ok(par, nodes);
+      if (slot <= 0 || slot >= pool->slots || !ok_tree) {
+        if (slot >= pool->slots) err |= 1;
+        if (!ok_tree) err |= 8;
+        for (int32_t n = 0; n < nodes; ++n)
+          for (int r = 0; r < V; ++r) {
+            size_t oi = (((size_t)b * nodes + n) * H + h) * V + r;
+            out[oi] = 0;
+            if (out_exact) out_exact[oi] = 0;
+          }
+        continue;
+      }
+      size_t *chan = head_channels(&u, h);
+      real *S = malloc(sizeof(real) * (size_t)V * K);
+      real (*R)[CONV_ROWS] = malloc(sizeof(real) * CONV_ROWS * nchan);
+      real *y = malloc(sizeof(real) * nchan);
+      real *a = malloc(sizeof(real) * K);
+      real *o = malloc(sizeof(real) * V);
+      const size_t hb = (size_t)h * V * K;
+      for (int32_t n = 0; n < nodes; ++n) {
+        const int p = par[n];
+        /* the parent's state and conv rows: the live slot or an earlier node */
+        const unsigned char *sblk = p < 0 ? ssm_block(pool, layer, slot) : node_ssm_block(pool, node_ssm, nodes, b, p);
+        const uint16_t *cblk = p < 0 ? conv_block(pool, layer, slot) : node_conv_block(pool, node_conv, nodes, b, p);
+        for (size_t i = 0; i < (size_t)V * K; ++i) S[i] = load_ssm(pool, sblk, hb + i);
+        for (int i = 0; i < nchan; ++i)
+          for (int j = 0; j < CONV_ROWS; ++j) R[i][j] = widen(cblk[(size_t)j * u.C + chan[i]]);
+        const size_t tok = (size_t)b * nodes + n;
+        step_token(&u, chan, nchan, S, R, x + tok * u.C, alpha + (tok * H + h) * aw, alpha_mode,
+                   (real)beta[tok * H + h], y, a, o);
+        for (int r = 0; r < V; ++r) {
+          size_t oi = (tok * H + h) * V + r;
+          out[oi] = oracle_bf16_round((double)o[r]);
+          if (out_exact) out_exact[oi] = (double)o[r];
+        }
+        unsigned char *dblk = node_ssm_block(pool, node_ssm, nodes, b, n);
+        for (size_t i = 0; i < (size_t)V * K; ++i) store_ssm(pool, dblk, hb + i, S[i]);
+        uint16_t *dc = node_conv_block(pool, node_conv, nodes, b, n);
+        for (int j = 0; j < CONV_ROWS; ++j)
+          for (int i = 0; i < nchan; ++i) dc[(size_t)j * u.C + chan[i]] = oracle_bf16_round((double)R[i][j]);
+      }
+      free(chan); free(S); free(R); free(y); free(a); free(o);
+    }
+  }
+  return err;
+}
+
+/* Copy a node's whole block (every head's state and all conv channels) into a
+ * slot of the layer. */
+static void copy_node(const oracle_pool *p, int layer, const void *node_ssm, const uint16_t *node_conv,
+                      int32_t nodes, int b, int n, int dst) {
+  memcpy(ssm_block(p, layer, dst), node_ssm_block(p, (void *)node_ssm, nodes, b, n),
+         ssm_block_elems(p) * ssm_esize(p));
+  memcpy(conv_block(p, layer, dst), node_conv_block(p, (uint16_t *)node_conv, nodes, b, n),
+         (size_t)CONV_ROWS * conv_channels(p) * 2);
+}
+
+/* Commit the accepted step (page "SGLang之MambaRadixCache机制", section 8.4:
+ * main_state[layer, slot] = buffer[layer, req, accepted_step]; section 8.6: when
+ * the accepted tokens cross the track interval, the ping-pong track buffer is
+ * updated too).  accepted[b] is the last accepted node (-1: nothing accepted,
+ * nothing written).  Its depth d (1 + its parent's depth, 0 for the live state)
+ * is the number of tokens it folds.  For each length L = seq_len_before[b] + i,
+ * 0 < i <= d, with L % track_interval == 0 (track_interval > 0), the node at
+ * depth i on the accepted path is copied to track_slots[2b + ((next_track_idx[b]
+ * + j) & 1)] for the j-th such length, as the prefill snapshots do.  Error bits:
+ * 1 live slot >= slots, 2 track slot >= slots, 8 invalid tree or accepted node. */
+int oracle_accept_scatter(const oracle_pool *pool, int32_t layer, int32_t batch, int32_t nodes,
+                          const int32_t *slot_table, const int32_t *parent, const int32_t *accepted,
+                          const int32_t *seq_len_before, int32_t track_interval,
+                          const int32_t *track_slots, const int32_t *next_track_idx,
+                          const void *node_ssm, const uint16_t *node_conv) {
+  if (!pool_ok(pool, layer) || batch < 0 || nodes < 1 || track_interval < 0) return 4;
+  int err = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int32_t *par = parent + (size_t)b * nodes;
+    const int acc = accepted[b], slot = slot_table[b];
+    if (acc == -1) continue;
+    if (acc < -1 || acc >= nodes || !tree_ok(par, nodes)) {
+      err |= 8;
+      continue;
+    }
+    if (slot <= 0 || slot >= pool->slots) {
+      if (slot >= pool->slots) err |= 1;
+      continue;
+    }
+    /* the accepted path, root first */
+    int depth = 0;
+    for (int n = acc; n >= 0; n = par[n]) ++depth;
+    int *path = malloc(sizeof(int) * (depth + 1));
+    { int i = depth; for (int n = acc; n >= 0; n = par[n]) path[--i] = n; }
+    if (track_interval > 0 && track_slots) {
+      int j = 0;
+      for (int i = 1; i <= depth; ++i) {
+        int64_t len = (int64_t)seq_len_before[b] + i;
+        if (len % track_interval != 0) continue;
+        int dst = track_slots[2 * b + (((next_track_idx ? next_track_idx[b] : 0) + j) & 1)];
+        ++j;
+        if (dst <= 0) continue;
+        if (dst >= pool->slots) { err |= 2; continue; }
+        copy_node(pool, layer, node_ssm, node_conv, nodes, b, path[i - 1], dst);
+      }
+    }
+    copy_node(pool, layer, node_ssm, node_conv, nodes, b, acc, slot);
+    free(path);
   }
   return err;
 }

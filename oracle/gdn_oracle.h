@@ -24,7 +24,9 @@
  *     and "Decode 阶段"; Kimi K3 notes, section "--mamba-track-interval");
  *   - the copy semantics of copy_from (page "SGLang之MambaRadixCache机制",
  *     section 3.2) and of restore_linear_state_slots (page "Qwen3.5
- *     Linear-State Prefix Cache", sections 6.1 and 6.4).
+ *     Linear-State Prefix Cache", sections 6.1 and 6.4);
+ *   - the speculative verify over a draft tree and the accepted-step scatter
+ *     (page "SGLang之MambaRadixCache机制", sections 8.3, 8.4, 8.6 and 9.6).
  *
  * Pool byte layout (identical to the product's so that pool images can be
  * compared byte for byte):
@@ -33,7 +35,8 @@
  * Channel order inside x and conv rows: q | k | v, each head-major.
  *
  * Error returns: bitmask, 0 = clean.  1 = a live slot id >= slots was skipped,
- * 2 = a track/destination slot id >= slots was skipped, 4 = bad argument.
+ * 2 = a track/destination slot id >= slots was skipped, 4 = bad argument,
+ * 8 = an invalid draft tree or accepted node was skipped.
  */
 #ifndef GDN_ORACLE_H
 #define GDN_ORACLE_H
@@ -111,6 +114,27 @@ int oracle_track_snapshot(const oracle_pool *pool, int32_t layer_begin, int32_t 
 /* restore_linear_state_slots semantics; has_initial_state updated in place. */
 int oracle_restore_slots(const oracle_pool *pool, int32_t n_ops, const oracle_restore_op *ops,
                          int64_t *has_initial_state);
+
+/* Verify a draft tree of `nodes` nodes per request for one layer; the live slots
+ * are only read.  parent [B][T]: -1 = start from the live slot, else an earlier
+ * node.  x [B][T][C], alpha [B][T][H] or [B][T][H][K], beta [B][T][H], out bf16
+ * [B][T][H][V]; node_ssm [B][T][H][V][K] in the pool's ssm dtype and node_conv
+ * bf16 [B][T][3][C] receive every node's state and conv rows.  out_exact may be
+ * NULL. */
+int oracle_verify_tree(const oracle_pool *pool, int32_t layer, int32_t batch, int32_t nodes,
+                       const int32_t *slot_table, const int32_t *parent, const uint16_t *x,
+                       const uint16_t *conv_w, const float *alpha, int32_t alpha_mode,
+                       const float *beta, float scale, uint32_t flags, uint16_t *out,
+                       void *node_ssm, uint16_t *node_conv, double *out_exact);
+
+/* Copy node accepted[b] (>= 0) of each request into its live slot, and the node
+ * on the accepted path that reaches each multiple of track_interval (counting
+ * from seq_len_before[b]) into the ping-pong track slots. */
+int oracle_accept_scatter(const oracle_pool *pool, int32_t layer, int32_t batch, int32_t nodes,
+                          const int32_t *slot_table, const int32_t *parent, const int32_t *accepted,
+                          const int32_t *seq_len_before, int32_t track_interval,
+                          const int32_t *track_slots, const int32_t *next_track_idx,
+                          const void *node_ssm, const uint16_t *node_conv);
 
 /* The bare recurrence for one head over T prepared tokens (no conv, no norm):
  * q, k, v [T][K|V] as given, alpha [T][K], beta [T]; S [V][K] in/out;

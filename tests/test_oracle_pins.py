@@ -604,3 +604,212 @@ def test_cold_start_ignores_slot_contents():
     assert np.array_equal(o1, o2)
     assert np.array_equal(pool.ssm()[0, 2], zero.ssm()[0, 2])
     assert np.array_equal(pool.conv()[0, 2], zero.conv()[0, 2])
+
+
+# ------------------------------------------------ speculative verify ----
+
+def _spec_setup(seed, B, T, ssm_dtype=oracle.SSM_F32, H=2, K=8, V=8, slots=12):
+    """Warm pool, conv taps and per-node inputs x [B][T][C], alpha [B][T][H][K],
+    beta [B][T][H]."""
+    g = wl.generator(seed)
+    pool = oracle.Pool(1, slots, H, K, V, ssm_dtype)
+    ssm, conv = wl.warm_pool(g, 1, slots, H, K, V, ssm_dtype == oracle.SSM_BF16)
+    pool.ssm()[:] = ssm.numpy() if ssm_dtype == oracle.SSM_F32 else wl.bf16_bits(ssm)
+    pool.conv()[:] = wl.bf16_bits(conv)
+    w = wl.bf16_bits(wl.conv_weights(g, H * (2 * K + V)))
+    inp = wl.projected_inputs(g, B * T, H, K, V, wl.ALPHA_PER_CHANNEL)
+    x = wl.bf16_bits(inp["x"]).reshape(B, T, -1)
+    a = inp["alpha"].numpy().reshape(B, T, H, K)
+    b = inp["beta"].numpy().reshape(B, T, H)
+    return pool, w, x, a, b
+
+
+def _path(parent, n):
+    p = []
+    while n >= 0:
+        p.append(n)
+        n = parent[n]
+    return p[::-1]
+
+
+def _decode_path(pool, slot, path, x, w, a, b, precision, **track):
+    """Decode the path's tokens one by one into ``slot`` of a copy of the pool;
+    returns (copy, outputs per step)."""
+    p = pool.copy()
+    outs = []
+    for i, n in enumerate(path):
+        kw = {k: (v[i] if k == "seq_len_after" else v) for k, v in track.items()}
+        o, err = oracle.decode_step(p, 0, [slot], x[None, n], w, a[None, n],
+                                    oracle.ALPHA_PER_CHANNEL, b[None, n], precision=precision, **kw)
+        assert err == 0
+        outs.append(o[0])
+    return p, outs
+
+
+@pytest.mark.parametrize("ssm_dtype", [oracle.SSM_F32, oracle.SSM_BF16])
+def test_verify_page_tree_equals_decodes_along_each_path(golden_dir, ssm_dtype):
+    """Every node of the pages' 9-node tree equals decoding the tokens on its
+    root path one at a time from the live slot: same output bits, same state
+    and conv rows (each decode stores its state in the pool dtype, as a node
+    does).  The live slot is left as it was."""
+    spec = json.load(open(os.path.join(golden_dir, "eagle_tree.json")))
+    parent = np.array(spec["parent"], dtype=np.int32)
+    T = parent.shape[0]
+    pool, w, x, a, b = _spec_setup(91, 1, T, ssm_dtype)
+    before = pool.copy()
+    out, ns, nc, err = oracle.verify_tree(pool, 0, [5], parent[None], x, w, a,
+                                          oracle.ALPHA_PER_CHANNEL, b, precision="f32")
+    assert err == 0
+    assert np.array_equal(pool.ssm_bytes, before.ssm_bytes)
+    assert np.array_equal(pool.conv_bytes, before.conv_bytes)
+    # the reads the page lists: roots from the main state, the rest from a node
+    for src, nodes in spec["reads"].items():
+        for n in nodes:
+            assert parent[n] == (-1 if src == "main" else int(src))
+    for n in range(T):
+        p, outs = _decode_path(pool, 5, _path(parent, n), x[0], w, a[0], b[0], "f32")
+        assert np.array_equal(out[0, n], outs[-1])
+        assert np.array_equal(ns[0, n], p.ssm()[0, 5])
+        assert np.array_equal(nc[0, n], p.conv()[0, 5])
+
+
+def test_verify_chain_and_star_trees():
+    """A chain (parent n-1) equals sequential decodes; a star (all -1) equals
+    independent one-token decodes from the live slot.  Two requests at once,
+    in different slots."""
+    T = 5
+    pool, w, x, a, b = _spec_setup(92, 2, T)
+    parent = np.array([np.arange(T) - 1, -np.ones(T)], dtype=np.int32)
+    out, ns, nc, err = oracle.verify_tree(pool, 0, [3, 7], parent, x, w, a,
+                                          oracle.ALPHA_PER_CHANNEL, b, precision="f32")
+    assert err == 0
+    p, outs = _decode_path(pool, 3, list(range(T)), x[0], w, a[0], b[0], "f32")
+    assert np.array_equal(out[0], np.stack(outs))
+    assert np.array_equal(ns[0, T - 1], p.ssm()[0, 3])
+    for n in range(T):
+        p, outs = _decode_path(pool, 7, [n], x[1], w, a[1], b[1], "f32")
+        assert np.array_equal(out[1, n], outs[0])
+        assert np.array_equal(ns[1, n], p.ssm()[0, 7])
+        assert np.array_equal(nc[1, n], p.conv()[0, 7])
+
+
+def test_verify_f64_node_states_follow_the_recurrence():
+    """Conv off (identity taps), f64: a chain's last node state equals the bare
+    recurrence over the same prepared tokens from the live state."""
+    H, K, V, T = 1, 4, 4, 4
+    g = wl.generator(93)
+    pool = oracle.Pool(1, 4, H, K, V, oracle.SSM_F32)
+    S0 = (0.25 * torch.randn(V, K, generator=g)).numpy()
+    pool.ssm()[0, 2, 0] = S0
+    q = torch.randn(T, K, generator=g).to(torch.bfloat16)
+    k = torch.randn(T, K, generator=g)
+    k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    v = torch.randn(T, V, generator=g).to(torch.bfloat16)
+    x = wl.bf16_bits(torch.cat([q, k, v], dim=1)).reshape(1, T, -1)
+    a = torch.sigmoid(torch.randn(1, T, H, K, generator=g) + 3).numpy()
+    b = torch.sigmoid(torch.randn(1, T, H, generator=g)).numpy()
+    parent = (np.arange(T, dtype=np.int32) - 1)[None]
+    out, ns, nc, err, oe = oracle.verify_tree(pool, 0, [2], parent, x, identity_taps(H * (2 * K + V)),
+                                              a, oracle.ALPHA_PER_CHANNEL, b, flags=0, exact=True)
+    assert err == 0
+    o, S = oracle.recurrence_head(q.float().numpy(), k.float().numpy(), v.float().numpy(),
+                                  a[0, :, 0], b[0, :, 0], S0.astype(np.float64))
+    # node 0 starts from the live state itself; each later node starts from its
+    # parent's state as stored (fp32 here), so agreement is to fp32 rounding
+    assert np.allclose(oe[0, 0, 0], o[0], rtol=0, atol=1e-12)
+    assert np.allclose(oe[0, :, 0], o, rtol=0, atol=1e-6)
+    assert np.allclose(ns[0, T - 1, 0], S, rtol=0, atol=1e-6)
+
+
+def test_verify_rejects_bad_trees_and_slots():
+    """A parent that is not -1 or an earlier node flags bit 8 and the request
+    gets zero outputs and no node writes; a live slot past the pool flags bit
+    1; the other requests are unaffected."""
+    T = 3
+    pool, w, x, a, b = _spec_setup(94, 3, T)
+    good = [-1, 0, 0]
+    parent = np.array([good, [-1, 2, 0], good], dtype=np.int32)   # node 1 reads a later node
+    out, ns, nc, err = oracle.verify_tree(pool, 0, [1, 2, 99], parent, x, w, a,
+                                          oracle.ALPHA_PER_CHANNEL, b, precision="f32")
+    assert err == 8 | 1
+    assert not out[1].any() and not ns[1].any() and not nc[1].any()
+    assert not out[2].any() and not ns[2].any()
+    ref, _, _, e0 = oracle.verify_tree(pool, 0, [1], parent[:1], x[:1], w, a[:1],
+                                       oracle.ALPHA_PER_CHANNEL, b[:1], precision="f32")
+    assert e0 == 0 and np.array_equal(out[0], ref[0]) and out[0].any()
+    for bad in ([-2, -1, 0], [0, -1, -1]):
+        _, _, _, e = oracle.verify_tree(pool, 0, [1], np.array([bad], dtype=np.int32), x[:1], w,
+                                        a[:1], oracle.ALPHA_PER_CHANNEL, b[:1], precision="f32")
+        assert e == 8
+
+
+def test_verify_buffer_is_nodes_times_the_state(golden_dir):
+    """The per-node buffers hold one state and one set of conv rows per tree
+    node: T times a slot's bytes (the pages' 3x, 7x, 63x)."""
+    spec = json.load(open(os.path.join(golden_dir, "eagle_tree.json")))
+    pool = oracle.Pool(1, 2, 2, 8, 8, oracle.SSM_BF16)
+    slot_bytes = pool.ssm()[0, 0].nbytes
+    for topk, steps, nodes in spec["buffer_ratio"]:
+        ns, nc = oracle.node_buffers(pool, 1, nodes)
+        assert ns.nbytes == nodes * slot_bytes
+        assert nc.nbytes == nodes * pool.conv()[0, 0].nbytes
+
+
+@pytest.mark.parametrize("ssm_dtype", [oracle.SSM_F32, oracle.SSM_BF16])
+def test_accept_scatter_equals_decoding_the_accepted_path(golden_dir, ssm_dtype):
+    """After verify, scattering accepted node n leaves the live slot exactly as
+    decoding n's root path token by token would; accepted -1 changes nothing."""
+    spec = json.load(open(os.path.join(golden_dir, "eagle_tree.json")))
+    parent = np.array([spec["parent"]] * 2, dtype=np.int32)
+    T = parent.shape[1]
+    pool, w, x, a, b = _spec_setup(95, 2, T, ssm_dtype)
+    _, ns, nc, err = oracle.verify_tree(pool, 0, [4, 6], parent, x, w, a,
+                                        oracle.ALPHA_PER_CHANNEL, b, precision="f32")
+    assert err == 0
+    run = pool.copy()
+    assert oracle.accept_scatter(run, 0, [4, 6], parent, [7, -1], ns, nc) == 0
+    p, _ = _decode_path(pool, 4, _path(parent[0], 7), x[0], w, a[0], b[0], "f32")
+    assert np.array_equal(run.ssm_bytes, p.ssm_bytes)
+    assert np.array_equal(run.conv_bytes, p.conv_bytes)
+
+
+@pytest.mark.parametrize("before,hit_depth", [(254, 2), (255, 1), (253, 3), (250, None)])
+def test_accept_scatter_tracks_the_interval_crossing(before, hit_depth):
+    """Accepting a depth-3 node whose tokens cross a multiple of 256 copies the
+    node at the crossing depth into the track slot, exactly as decode steps with
+    tracking place the snapshot (replay-with-tracking rule of the pages)."""
+    T = 4
+    parent = np.array([[-1, 0, 1, 0]], dtype=np.int32)   # node 2 at depth 3
+    pool, w, x, a, b = _spec_setup(96, 1, T)
+    _, ns, nc, err = oracle.verify_tree(pool, 0, [1], parent, x, w, a,
+                                        oracle.ALPHA_PER_CHANNEL, b, precision="f32")
+    run = pool.copy()
+    err = oracle.accept_scatter(run, 0, [1], parent, [2], ns, nc, seq_len_before=[before],
+                                track_interval=256, track_slots=[[9, 10]], next_track_idx=[1])
+    assert err == 0
+    path = _path(parent[0], 2)
+    p, _ = _decode_path(pool, 1, path, x[0], w, a[0], b[0], "f32",
+                        seq_len_after=[[before + i + 1] for i in range(3)], track_interval=256,
+                        track_slots=[[9, 10]], next_track_idx=[1])
+    assert np.array_equal(run.ssm_bytes, p.ssm_bytes)
+    assert np.array_equal(run.conv_bytes, p.conv_bytes)
+    if hit_depth is None:
+        assert np.array_equal(run.ssm()[0, 10], pool.ssm()[0, 10])
+    else:
+        assert np.array_equal(run.ssm()[0, 10], ns[0, path[hit_depth - 1]])
+    assert np.array_equal(run.ssm()[0, 9], pool.ssm()[0, 9])
+
+
+def test_accept_scatter_rejects_bad_input():
+    T = 3
+    pool, w, x, a, b = _spec_setup(97, 2, T)
+    parent = np.array([[-1, 0, 1], [-1, 0, 1]], dtype=np.int32)
+    _, ns, nc, _ = oracle.verify_tree(pool, 0, [1, 2], parent, x, w, a,
+                                      oracle.ALPHA_PER_CHANNEL, b, precision="f32")
+    run = pool.copy()
+    assert oracle.accept_scatter(run, 0, [1, 2], parent, [3, -2], ns, nc) == 8
+    assert np.array_equal(run.ssm_bytes, pool.ssm_bytes)
+    assert oracle.accept_scatter(run, 0, [99, 2], parent, [0, 2], ns, nc) == 1
+    assert np.array_equal(run.ssm()[0, 2], ns[1, 2])
+    assert oracle.accept_scatter(run, 0, [1, 2], parent, [2, -1], ns, nc, seq_len_before=[254],
+                                 track_interval=256, track_slots=[[99, 99], [0, 0]]) == 2
