@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "libgdnslot.so")
 GDN_F32, GDN_BF16 = 0, 1
 ALPHA_PER_HEAD, ALPHA_PER_CHANNEL = 0, 1
 L2NORM_K, L2NORM_Q, CONV_SILU = 1, 2, 4
-ERRW_BAD_SLOT, ERRW_BAD_TRACK_SLOT, ERRW_BAD_SEQLENS = 1, 2, 4
+ERRW_BAD_SLOT, ERRW_BAD_TRACK_SLOT, ERRW_BAD_SEQLENS, ERRW_BAD_TREE = 1, 2, 4, 8
+MAX_TREE_NODES = 1024
 
 
 class GdnError(RuntimeError):
@@ -59,8 +60,13 @@ _lib.gdn_decode_step.argtypes = [
     _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _u32, _vp, _vp, _i32, _vp, _vp, _vp]
 _lib.track_snapshot.argtypes = [_vp, _i32, _i32, _i32, _vp, _vp, _vp]
 _lib.restore_slots.argtypes = [_vp, _i32, ct.POINTER(RestoreOp), ct.POINTER(ct.c_int64), _vp]
+_lib.gdn_verify_tree.argtypes = [
+    _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _u32, _vp, _vp, _vp, _vp]
+_lib.gdn_accept_scatter.argtypes = [
+    _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
 for _f in ("state_pool_bytes", "state_pool_create", "conv_gdn_prefill_chunked",
-           "gdn_prefill_workspace_bytes", "gdn_decode_step", "track_snapshot", "restore_slots"):
+           "gdn_prefill_workspace_bytes", "gdn_decode_step", "track_snapshot", "restore_slots",
+           "gdn_verify_tree", "gdn_accept_scatter"):
     getattr(_lib, _f).restype = ct.c_int
 
 
@@ -223,3 +229,51 @@ def restore_slots(pool: StatePool, ops, has_initial_state, stream=None):
     hi = (ct.c_int64 * max(n, 1))(*[int(v) for v in has_initial_state])
     _check(_lib.restore_slots(pool.handle, n, arr, hi, _stream(stream)))
     return [hi[i] for i in range(n)]
+
+
+def gdn_verify_tree(pool: StatePool, layer, slot_table, parent, x, conv_w, alpha, alpha_mode, beta,
+                    out, node_ssm, node_conv, scale=1.0, flags=L2NORM_K, stream=None):
+    """``parent`` int32 [B, T]; ``x`` bf16 [B, T, C]; ``alpha`` fp32 [B, T, H(, K)];
+    ``beta`` fp32 [B, T, H]; ``out`` bf16 [B, T, H, V]; ``node_ssm`` [B, T, H, V, K]
+    in the pool's ssm dtype; ``node_conv`` bf16 [B, T, 3, C]."""
+    B = slot_table.numel()
+    if parent.dim() != 2 or parent.shape[0] != B:
+        raise ValueError("parent must be [batch, tree_nodes]")
+    T = parent.shape[1]
+    H, V, K = pool.heads, pool.head_v, pool.head_k
+    _need(slot_table, torch.int32, B, "slot_table")
+    _need(parent, torch.int32, B * T, "parent")
+    _need(x, torch.bfloat16, B * T * pool.channels, "x")
+    _need(conv_w, torch.bfloat16, pool.channels * 4, "conv_w")
+    _need(alpha, torch.float32, B * T * H * (K if alpha_mode == ALPHA_PER_CHANNEL else 1), "alpha")
+    _need(beta, torch.float32, B * T * H, "beta")
+    _need(out, torch.bfloat16, B * T * H * V, "out")
+    _need(node_ssm, pool.ssm.dtype, B * T * H * V * K, "node_ssm")
+    _need(node_conv, torch.bfloat16, B * T * 3 * pool.channels, "node_conv")
+    _check(_lib.gdn_verify_tree(
+        pool.handle, layer, B, T, _ptr(slot_table), _ptr(parent), _ptr(x), _ptr(conv_w),
+        _ptr(alpha), alpha_mode, _ptr(beta), float(scale), flags, _ptr(out), _ptr(node_ssm),
+        _ptr(node_conv), _stream(stream)))
+
+
+def gdn_accept_scatter(pool: StatePool, layer, slot_table, parent, accepted, node_ssm, node_conv,
+                       seq_len_before=None, track_interval=0, track_slots=None,
+                       next_track_idx=None, stream=None):
+    """Commit node ``accepted[b]`` (-1: none) of each request's verified tree."""
+    B = slot_table.numel()
+    if parent.dim() != 2 or parent.shape[0] != B:
+        raise ValueError("parent must be [batch, tree_nodes]")
+    T = parent.shape[1]
+    H, V, K = pool.heads, pool.head_v, pool.head_k
+    _need(slot_table, torch.int32, B, "slot_table")
+    _need(parent, torch.int32, B * T, "parent")
+    _need(accepted, torch.int32, B, "accepted")
+    _need(seq_len_before, torch.int32, B, "seq_len_before")
+    _need(track_slots, torch.int32, 2 * B, "track_slots")
+    _need(next_track_idx, torch.int32, B, "next_track_idx")
+    _need(node_ssm, pool.ssm.dtype, B * T * H * V * K, "node_ssm")
+    _need(node_conv, torch.bfloat16, B * T * 3 * pool.channels, "node_conv")
+    _check(_lib.gdn_accept_scatter(
+        pool.handle, layer, B, T, _ptr(slot_table), _ptr(parent), _ptr(accepted),
+        _ptr(seq_len_before), track_interval, _ptr(track_slots), _ptr(next_track_idx),
+        _ptr(node_ssm), _ptr(node_conv), _stream(stream)))

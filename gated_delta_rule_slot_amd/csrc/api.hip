@@ -244,3 +244,60 @@ GDN_API gdn_status restore_slots(gdn_pool_t pool, int32_t n_ops, const gdn_resto
   }
   return ok();
 }
+
+GDN_API gdn_status gdn_verify_tree(gdn_pool_t pool, int32_t layer, int32_t batch,
+                                   int32_t tree_nodes, const int32_t *slot_table,
+                                   const int32_t *parent, const uint16_t *x,
+                                   const uint16_t *conv_w, const float *alpha, int32_t alpha_mode,
+                                   const float *beta, float scale, uint32_t flags, uint16_t *out,
+                                   void *node_ssm, uint16_t *node_conv, void *stream) {
+  gdn_status s = check_pool(pool, layer);
+  if (s != GDN_OK) return s;
+  if (batch < 0 || batch > 65535) return fail(GDN_ERR_RANGE, "batch %d outside [0, 65535]", batch);
+  if (tree_nodes < 1 || tree_nodes > GDN_MAX_TREE_NODES)
+    return fail(GDN_ERR_RANGE, "tree_nodes %d outside [1, %d]", tree_nodes, GDN_MAX_TREE_NODES);
+  if (batch == 0) return ok();
+  if (!slot_table || !parent || !x || !conv_w || !alpha || !beta || !out || !node_ssm ||
+      !node_conv)
+    return fail(GDN_ERR_ARG, "a required pointer is NULL");
+  if (alpha_mode != GDN_ALPHA_PER_HEAD && alpha_mode != GDN_ALPHA_PER_CHANNEL)
+    return fail(GDN_ERR_ARG, "alpha_mode %d unknown", alpha_mode);
+  if (flags & ~uint32_t(GDN_F_L2NORM_K | GDN_F_L2NORM_Q | GDN_F_CONV_SILU))
+    return fail(GDN_ERR_ARG, "unknown flag bits 0x%x", flags);
+  if (!aligned(conv_w, 16) || !aligned(x, 16) || !aligned(alpha, 16))
+    return fail(GDN_ERR_UNSUPPORTED, "x, conv_w and alpha must be 16-byte aligned");
+  if (!aligned(node_ssm, 16) || !aligned(node_conv, 16))
+    return fail(GDN_ERR_UNSUPPORTED, "node_ssm and node_conv must be 16-byte aligned");
+  gdn::VerifyArgs a{layer, batch,      tree_nodes, slot_table, parent, x,        conv_w,
+                    alpha, alpha_mode, beta,       scale,      flags,  out,      node_ssm,
+                    node_conv};
+  return launched(gdn::launch_verify(pool, a, static_cast<hipStream_t>(stream)),
+                  "gdn_verify_tree launch");
+}
+
+GDN_API gdn_status gdn_accept_scatter(gdn_pool_t pool, int32_t layer, int32_t batch,
+                                      int32_t tree_nodes, const int32_t *slot_table,
+                                      const int32_t *parent, const int32_t *accepted,
+                                      const int32_t *seq_len_before, int32_t track_interval,
+                                      const int32_t *track_slots, const int32_t *next_track_idx,
+                                      const void *node_ssm, const uint16_t *node_conv,
+                                      void *stream) {
+  gdn_status s = check_pool(pool, layer);
+  if (s != GDN_OK) return s;
+  if (batch < 0 || batch > 65535) return fail(GDN_ERR_RANGE, "batch %d outside [0, 65535]", batch);
+  if (tree_nodes < 1 || tree_nodes > GDN_MAX_TREE_NODES)
+    return fail(GDN_ERR_RANGE, "tree_nodes %d outside [1, %d]", tree_nodes, GDN_MAX_TREE_NODES);
+  if (track_interval < 0) return fail(GDN_ERR_ARG, "track_interval < 0");
+  if (batch == 0) return ok();
+  if (!slot_table || !parent || !accepted || !node_ssm || !node_conv)
+    return fail(GDN_ERR_ARG, "a required pointer is NULL");
+  if (track_interval > 0 && (!seq_len_before || !track_slots || !next_track_idx))
+    return fail(GDN_ERR_ARG, "tracking needs seq_len_before, track_slots and next_track_idx");
+  if (!aligned(node_ssm, 16) || !aligned(node_conv, 16))
+    return fail(GDN_ERR_UNSUPPORTED, "node_ssm and node_conv must be 16-byte aligned");
+  gdn::ScatterArgs a{layer,          batch,       tree_nodes,     slot_table,
+                     parent,         accepted,    seq_len_before, track_interval,
+                     track_slots,    next_track_idx, node_ssm,    node_conv};
+  return launched(gdn::launch_accept_scatter(pool, a, static_cast<hipStream_t>(stream)),
+                  "gdn_accept_scatter launch");
+}

@@ -80,6 +80,41 @@ struct PrefillArgs {
   size_t workspace_bytes;
 };
 hipError_t launch_prefill(const gdn_pool *p, const PrefillArgs &a, hipStream_t s);
+
+// Draft trees: nodes per request are limited so that a workgroup can hold the
+// parent list in shared memory.
+constexpr int kMaxTreeNodes = GDN_MAX_TREE_NODES;
+
+struct VerifyArgs {
+  int layer, batch, nodes;
+  const int32_t *slot_table;
+  const int32_t *parent;
+  const uint16_t *x;
+  const uint16_t *conv_w;
+  const float *alpha;
+  int alpha_mode;
+  const float *beta;
+  float scale;
+  uint32_t flags;
+  uint16_t *out;
+  void *node_ssm;
+  uint16_t *node_conv;
+};
+hipError_t launch_verify(const gdn_pool *p, const VerifyArgs &a, hipStream_t s);
+
+struct ScatterArgs {
+  int layer, batch, nodes;
+  const int32_t *slot_table;
+  const int32_t *parent;
+  const int32_t *accepted;
+  const int32_t *seq_len_before;
+  int track_interval;
+  const int32_t *track_slots;
+  const int32_t *next_track_idx;
+  const void *node_ssm;
+  const uint16_t *node_conv;
+};
+hipError_t launch_accept_scatter(const gdn_pool *p, const ScatterArgs &a, hipStream_t s);
 // Workspace of the two-phase prefill: one record per (request, chunk, head) of
 // the chunks processed in one window, plus an fp32 state carry per (request, head).
 size_t prefill_record_bytes(const gdn_pool *p);

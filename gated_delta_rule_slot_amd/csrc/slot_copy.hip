@@ -39,10 +39,10 @@ struct HostPairs {
   int32_t dst[kMaxHostPairs];
 };
 
-__device__ __forceinline__ void copy_tile(char *base, int64_t block_bytes, int64_t src_off,
-                                          int64_t dst_off, int64_t tile_off) {
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(base + src_off);
-  u32x4 *dst = reinterpret_cast<u32x4 *>(base + dst_off);
+__device__ __forceinline__ void copy_tile(const char *src_block, char *dst_block,
+                                          int64_t block_bytes, int64_t tile_off) {
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(src_block);
+  u32x4 *dst = reinterpret_cast<u32x4 *>(dst_block);
   const int64_t nvec = block_bytes >> 4;
   const int64_t v0 = (tile_off >> 4) + threadIdx.x;
   u32x4 buf[kVecPerThread];
@@ -80,11 +80,83 @@ __global__ __launch_bounds__(kThreads) void slot_copy_kernel(CopyGeom g, const i
   const int64_t layer = g.layer_begin + blockIdx.y;
   const int tile = blockIdx.x;
   if (tile < g.ssm_tiles) {
-    copy_tile(g.ssm, g.ssm_block, layer * g.ssm_layer + src * g.ssm_block,
-              layer * g.ssm_layer + dst * g.ssm_block, int64_t(tile) * kTileBytes);
+    copy_tile(g.ssm + layer * g.ssm_layer + src * g.ssm_block,
+              g.ssm + layer * g.ssm_layer + dst * g.ssm_block, g.ssm_block,
+              int64_t(tile) * kTileBytes);
   } else {
-    copy_tile(g.conv, g.conv_block, layer * g.conv_layer + src * g.conv_block,
-              layer * g.conv_layer + dst * g.conv_block, int64_t(tile - g.ssm_tiles) * kTileBytes);
+    copy_tile(g.conv + layer * g.conv_layer + src * g.conv_block,
+              g.conv + layer * g.conv_layer + dst * g.conv_block, g.conv_block,
+              int64_t(tile - g.ssm_tiles) * kTileBytes);
+  }
+}
+
+// Accepted-step scatter (page "SGLang之MambaRadixCache机制解析", section 8.4: the
+// slot takes the intermediate state of the request's last accepted step;
+// section 8.6: when the accepted tokens cross a track-interval boundary the
+// ping-pong track slot is written too; section 9.10 places the snapshot at the
+// token that completes the multiple).  Grid: x tiles of the (ssm + conv)
+// block, y request, z job.  Job 0 copies the accepted node into the live slot.
+// Jobs 1 and 2 copy the nodes at the last and the second-to-last crossing: the
+// j-th crossing of the call goes to track slot (next_track_idx + j) & 1, so
+// earlier crossings would be overwritten and only these two decide the result.
+__global__ __launch_bounds__(kThreads) void accept_scatter_kernel(CopyGeom g, ScatterArgs a) {
+  const int tile = blockIdx.x, b = blockIdx.y, job = blockIdx.z;
+  const int acc = a.accepted[b];
+  if (acc == -1) return;
+  const int T = a.nodes;
+  __shared__ int spar[kMaxTreeNodes];
+  const int32_t *par = a.parent + int64_t(b) * T;
+  int bad = acc < -1 || acc >= T;
+  for (int i = threadIdx.x; i < T; i += kThreads) {
+    const int p = par[i];
+    spar[i] = p;
+    bad |= (p < -1 || p >= i);
+  }
+  bad = __syncthreads_or(bad);
+  const bool reporter = g.err && tile == 0 && threadIdx.x == 0;
+  if (bad) {
+    if (reporter && job == 0) atomicOr(g.err, GDN_ERRW_BAD_TREE);
+    return;
+  }
+  const int slot = a.slot_table[b];
+  if (slot <= 0 || slot >= g.slots) {
+    if (reporter && job == 0 && slot >= g.slots) atomicOr(g.err, GDN_ERRW_BAD_SLOT);
+    return;
+  }
+  int node = acc, dst = slot;
+  if (job > 0) {
+    if (a.track_interval <= 0) return;
+    int depth = 0;  // tokens the accepted node folds beyond the live state
+    for (int n = acc; n >= 0; n = spar[n]) ++depth;
+    const int64_t before = a.seq_len_before[b];
+    int crossings = 0, last = 0, prev = 0;  // count and depths of the last two crossings
+    for (int i = 1; i <= depth; ++i)
+      if ((before + i) % a.track_interval == 0) {
+        prev = last;
+        last = i;
+        ++crossings;
+      }
+    const int j = crossings - job;
+    if (j < 0) return;
+    const int at = job == 1 ? last : prev;
+    for (int s = depth; s > at; --s) node = spar[node];
+    dst = a.track_slots[2 * b + ((a.next_track_idx[b] + j) & 1)];
+    if (dst <= 0) return;
+    if (dst >= g.slots) {
+      if (reporter) atomicOr(g.err, GDN_ERRW_BAD_TRACK_SLOT);
+      return;
+    }
+  }
+  const int64_t layer = a.layer;
+  const int64_t src_node = int64_t(b) * T + node;
+  if (tile < g.ssm_tiles) {
+    copy_tile(static_cast<const char *>(a.node_ssm) + src_node * g.ssm_block,
+              g.ssm + layer * g.ssm_layer + dst * g.ssm_block, g.ssm_block,
+              int64_t(tile) * kTileBytes);
+  } else {
+    copy_tile(reinterpret_cast<const char *>(a.node_conv) + src_node * g.conv_block,
+              g.conv + layer * g.conv_layer + dst * g.conv_block, g.conv_block,
+              int64_t(tile - g.ssm_tiles) * kTileBytes);
   }
 }
 
@@ -123,6 +195,14 @@ hipError_t launch_copy_device_pairs(const gdn_pool *p, int layer_begin, int laye
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_accept_scatter(const gdn_pool *p, const ScatterArgs &a, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  CopyGeom g = make_geom(p, 0);
+  dim3 grid(tiles_total(g), a.batch, 3);
+  hipLaunchKernelGGL(accept_scatter_kernel, grid, dim3(kThreads), 0, s, g, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_copy_host_pairs(const gdn_pool *p, int n, const int32_t *src, const int32_t *dst,

@@ -24,7 +24,9 @@
  * extra_buffer 模式的 Ping-Pong 缓冲机制", sections "Prefill 阶段" and "Decode
  * 阶段"), and a prefix hit copies the deepest checkpoint slot into the live
  * slot across all layers before a warm prefill (page "Qwen3.5 Linear-State
- * Prefix Cache", sections 5.1, 6.1 and 6.4).
+ * Prefix Cache", sections 5.1, 6.1 and 6.4).  Speculative decoding verifies a
+ * draft tree without touching the live slot and then commits the accepted step
+ * (page "SGLang之MambaRadixCache机制解析", sections 8.3, 8.4, 8.6 and 9.6).
  *
  * Memory.  The caller owns every buffer (pool bytes, inputs, outputs, tables,
  * the error word, the prefill workspace); the library allocates and frees no
@@ -82,7 +84,15 @@ enum { GDN_ALPHA_PER_HEAD = 0, GDN_ALPHA_PER_CHANNEL = 1 };
 enum { GDN_F_L2NORM_K = 1u, GDN_F_L2NORM_Q = 2u, GDN_F_CONV_SILU = 4u };
 
 /* bits a kernel may set in the pool's error word (sticky; the caller clears it) */
-enum { GDN_ERRW_BAD_SLOT = 1, GDN_ERRW_BAD_TRACK_SLOT = 2, GDN_ERRW_BAD_SEQLENS = 4 };
+enum {
+  GDN_ERRW_BAD_SLOT = 1,
+  GDN_ERRW_BAD_TRACK_SLOT = 2,
+  GDN_ERRW_BAD_SEQLENS = 4,
+  GDN_ERRW_BAD_TREE = 8  /* a draft tree or accepted node that is not valid */
+};
+
+/* Largest draft tree (nodes per request) the verify and scatter calls accept. */
+#define GDN_MAX_TREE_NODES 1024
 
 typedef struct {
   int32_t layers, slots, heads, head_k, head_v;
@@ -191,6 +201,54 @@ gdn_status track_snapshot(gdn_pool_t pool, int32_t layer_begin, int32_t layer_en
  * is returned.  The copies are queued on the stream (no synchronisation). */
 gdn_status restore_slots(gdn_pool_t pool, int32_t n_ops, const gdn_restore_op *ops,
                          int64_t *has_initial_state, void *stream);
+
+/* Verify a draft tree for one layer (page "SGLang之MambaRadixCache机制解析",
+ * section 8.3: the main state is not updated and every draft position's result
+ * goes to an intermediate buffer; section 9.6: parent -> child inheritance
+ * through retrieve_parent_token, parents processed first).  Each request has
+ * tree_nodes nodes (1 <= tree_nodes <= GDN_MAX_TREE_NODES).
+ * parent      device int32 [batch][tree_nodes]: -1 = start from the live slot,
+ *             otherwise an earlier node (parent[b][n] < n)
+ * x           device bf16 [batch][tree_nodes][C]: the node's projected token
+ * alpha, beta device fp32 [batch][tree_nodes][heads](*head_k for per-channel alpha)
+ * out         device bf16 [batch][tree_nodes][heads][head_v]
+ * node_ssm    device, pool ssm dtype, [batch][tree_nodes][heads][head_v][head_k]
+ * node_conv   device bf16 [batch][tree_nodes][3][C]
+ * Node n starts from its parent's state as stored (pool dtype) and conv rows,
+ * takes its token as gdn_decode_step would, and stores its state, conv rows
+ * and output.  The live slot is only read.  A request whose tree is invalid
+ * sets GDN_ERRW_BAD_TREE; it and any request with a skipped slot (see "Slot
+ * ids") get zero outputs and no node writes.  node_ssm and node_conv are caller
+ * scratch (16-byte aligned) that gdn_accept_scatter reads afterwards. */
+gdn_status gdn_verify_tree(gdn_pool_t pool, int32_t layer, int32_t batch, int32_t tree_nodes,
+                           const int32_t *slot_table, const int32_t *parent, const uint16_t *x,
+                           const uint16_t *conv_w, const float *alpha, int32_t alpha_mode,
+                           const float *beta, float scale, uint32_t flags, uint16_t *out,
+                           void *node_ssm, uint16_t *node_conv, void *stream);
+
+/* Commit the accepted step of each request after a verify (page
+ * "SGLang之MambaRadixCache机制解析", section 8.4: main state of the slot =
+ * intermediate state of the last accepted step; section 8.6: the ping-pong
+ * track slot too when the accepted tokens cross the track interval; section
+ * 9.10: the snapshot is the state at the token that completes the multiple).
+ * accepted        device int32 [batch]: last accepted node, -1 = none (no writes)
+ * seq_len_before  device int32 [batch]: tokens in the slot before the tree
+ * track_interval  0 (no tracking) or > 0
+ * track_slots     device int32 [batch][2], next_track_idx device int32 [batch]
+ * The accepted node (all heads' state and the conv rows) is copied into the
+ * live slot.  With d = depth of the accepted node (1 for a root), every i in
+ * [1, d] with (seq_len_before + i) % track_interval == 0 is a crossing; the
+ * j-th crossing copies the accepted path's node at depth i into
+ * track_slots[2b + ((next_track_idx[b] + j) & 1)] (an entry <= 0 skips it, one
+ * >= slots sets GDN_ERRW_BAD_TRACK_SLOT).  An invalid tree or accepted index
+ * sets GDN_ERRW_BAD_TREE and skips the request.  Track slots must differ from
+ * the live slot.  Byte-exact copies. */
+gdn_status gdn_accept_scatter(gdn_pool_t pool, int32_t layer, int32_t batch, int32_t tree_nodes,
+                              const int32_t *slot_table, const int32_t *parent,
+                              const int32_t *accepted, const int32_t *seq_len_before,
+                              int32_t track_interval, const int32_t *track_slots,
+                              const int32_t *next_track_idx, const void *node_ssm,
+                              const uint16_t *node_conv, void *stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,8 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert {"state_pool_bytes", "state_pool_create", "state_pool_destroy", "gdn_last_error",
             "conv_gdn_prefill_chunked", "gdn_prefill_workspace_bytes", "gdn_decode_step",
-            "track_snapshot", "restore_slots"} <= set(names)
+            "track_snapshot", "restore_slots", "gdn_verify_tree",
+            "gdn_accept_scatter"} <= set(names)
     lib = ct.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -99,6 +100,25 @@ def test_calls_reject_bad_arguments_before_launch():
         assert "workspace" in B.last_error()
         # layer range for copies
         assert B._lib.track_snapshot(h, 0, 2, 1, fake, fake, None) == -2
+        # draft trees: node count range, required buffers, alignment of node buffers
+        v = B._lib.gdn_verify_tree
+        args = [fake, fake, fake, fake, fake, 0, fake, 1.0, 1, fake, fake, fake, None]
+        assert v(h, 0, 1, 0, *args) == -2
+        assert v(h, 0, 1, B.MAX_TREE_NODES + 1, *args) == -2
+        assert v(h, 1, 1, 4, *args) == -2
+        bad = list(args)
+        bad[11] = None      # node_conv
+        assert v(h, 0, 1, 4, *bad) == -1
+        bad = list(args)
+        bad[10] = ct.c_void_p(0x30008)  # node_ssm not 16-byte aligned
+        assert v(h, 0, 1, 4, *bad) == -3
+        assert v(h, 0, 0, 4, *args) == 0    # empty batch launches nothing
+        sc = B._lib.gdn_accept_scatter
+        assert sc(h, 0, 1, 4, fake, fake, fake, fake, -1, fake, fake, fake, fake, None) == -1
+        assert sc(h, 0, 1, 4, fake, fake, fake, None, 256, fake, fake, fake, fake, None) == -1
+        assert sc(h, 0, 1, 4, fake, fake, None, None, 0, None, None, fake, fake, None) == -1
+        assert sc(h, 0, 1, 2000, fake, fake, fake, None, 0, None, None, fake, fake, None) == -2
+        assert sc(h, 0, 0, 4, fake, fake, fake, None, 0, None, None, fake, fake, None) == 0
     finally:
         B._lib.state_pool_destroy(h)
 
