@@ -12,7 +12,9 @@ cache.  Inputs are resident in HBM before timing starts.
 
 Secondary lines (in "extra"): the KDA chunked prefill (12 heads, one request of
 6144 tokens, snapshot every 64 tokens), the KDA decode with tracking over 69
-layers, and a prefix-hit restore across 24 layers followed by a warm prefill.
+layers, a prefix-hit restore across 24 layers followed by a warm prefill, and
+a speculative-decoding round (draft-tree verify in 32 layers, then the
+accepted-step commit).
 
 Run on one GPU only: --gpus N with N > 1 exits with a message.
 """
@@ -361,6 +363,93 @@ def run_restore(torch, gdn, wl, dev, reps=5):
             "bytes": byts}
 
 
+# ------------------------------------------------------ speculative verify --
+def bfs_forest(topk, T):
+    """Draft tree of T nodes: topk roots on the live state, then breadth-first
+    topk children per node (topk 3 and 9 nodes is the tree the pages draw)."""
+    return [-1 if n < topk else (n - topk) // topk for n in range(T)]
+
+
+def run_spec_verify(torch, gdn, wl, dev, rounds=3, warmup=1):
+    """One speculative-decoding round over 32 linear layers: every layer verifies
+    a 63-node draft tree (4 roots, 4 children per node, breadth first) for 32
+    requests and keeps its node states; then every layer commits the accepted
+    node (depth 3) into the live slot, and into a track slot where the accepted
+    tokens cross a multiple of 256.  32 heads, K = V = 128, bf16 state (524K
+    elements per layer and request), scalar decay per head."""
+    L, B, T, topk, H, D = 32, 32, 63, 4, 32, 128
+    C = H * 3 * D
+    N = 1 + 3 * B
+    g = torch.Generator(device=dev)
+    g.manual_seed(106)
+    ssm = torch.empty(L, N, H, D, D, dtype=torch.bfloat16, device=dev).normal_(0.0, 0.25, generator=g)
+    conv = torch.empty(L, N, 3, C, dtype=torch.bfloat16, device=dev).normal_(0.0, 1.0, generator=g)
+    pool = gdn.state_pool_create(ssm, conv, torch.zeros(1, dtype=torch.int32, device=dev))
+    gc = wl.generator(106)
+    perm = (torch.randperm(N - 1, generator=gc) + 1).to(torch.int32)
+    slots = perm[:B].to(dev)
+    track = perm[B:3 * B].view(B, 2).contiguous().to(dev)
+    parent = torch.tensor([bfs_forest(topk, T)] * B, dtype=torch.int32, device=dev)
+    accepted = torch.randint(topk + topk * topk, T, (B,), generator=gc, dtype=torch.int32).to(dev)
+    before = torch.randint(256, 8192, (B,), generator=gc, dtype=torch.int32).to(dev)
+    nxt = torch.zeros(B, dtype=torch.int32, device=dev)
+    inp = {k: v.to(dev) for k, v in wl.projected_inputs(gc, B * T, H, D, D, 0).items()}
+    x = inp["x"].view(B, T, C)
+    alpha, beta = inp["alpha"].view(B, T, H), inp["beta"].view(B, T, H)
+    w = wl.conv_weights(gc, C).to(dev)
+    out = torch.empty(B, T, H, D, dtype=torch.bfloat16, device=dev)
+    node_ssm = [torch.empty(B, T, H, D, D, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    node_conv = [torch.empty(B, T, 3, C, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+
+    def verify():
+        for l in range(L):
+            gdn.gdn_verify_tree(pool, l, slots, parent, x, w, alpha, 0, beta, out, node_ssm[l],
+                                node_conv[l])
+
+    def commit():
+        for l in range(L):
+            gdn.gdn_accept_scatter(pool, l, slots, parent, accepted, node_ssm[l], node_conv[l],
+                                   seq_len_before=before, track_interval=256, track_slots=track,
+                                   next_track_idx=nxt)
+
+    for _ in range(warmup):
+        verify()
+        commit()
+    torch.cuda.synchronize()
+    ev = [event_pair() + event_pair() for _ in range(rounds)]
+    for a, b, c, d in ev:
+        a.record()
+        verify()
+        b.record()
+        c.record()
+        commit()
+        d.record()
+    torch.cuda.synchronize()
+    tv = sorted(a.elapsed_time(b) for a, b, _, _ in ev)[rounds // 2] / 1e3
+    tc = sorted(c.elapsed_time(d) for _, _, c, d in ev)[rounds // 2] / 1e3
+    assert int(pool.err_word.item()) == 0
+    # crossings per request: multiples of 256 in (before, before + 3]
+    crossed = int(((before + 3) // 256 - before // 256).clamp(max=2).sum())
+    state, rows = H * D * D * 2, 3 * C * 2
+    v_bytes = (B * state + B * T * state + B * T * C * 2 + B * rows + B * T * rows +
+               B * T * H * D * 2 + B * T * H * 8 + C * 8 + B * T * 4)
+    c_bytes = 2 * (B + crossed) * (state + rows)
+    res = {"workload": "speculative round: 32 layers, 32 requests, 63-node draft tree (topk 4, "
+                       "breadth first), 32 heads, K=V=128, bf16 state, accept depth 3, "
+                       "track every 256",
+           "verify_ms_per_layer": tv / L * 1e3, "commit_ms_per_layer": tc / L * 1e3,
+           "round_ms": (tv + tc) * 1e3,
+           "draft_tokens_per_s": B * T / (tv + tc),
+           "verify_GB_per_s": v_bytes * L / tv / 1e9,
+           "verify_hbm_frac": v_bytes * L / tv / 1e9 / HBM_PEAK_GBS,
+           "commit_GB_per_s": c_bytes * L / tc / 1e9,
+           "verify_bytes_per_launch": v_bytes,
+           "node_buffer_GB": L * (node_ssm[0].numel() + node_conv[0].numel()) * 2 / 1e9}
+    del pool, ssm, conv, node_ssm, node_conv
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------ cpu baseline --
 def cpu_baseline(wl, seconds=10.0):
     import numpy as np
@@ -392,6 +481,8 @@ def main():
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--extra", default="kda_prefill,restore,kda_decode_tracking,warm_prefill,"
+                    "spec_verify", help="comma-separated secondary workloads to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -409,15 +500,17 @@ def main():
     r = run_headline(torch, gdn, wl, dev, args.steps, args.warmup)
     value = r["tokens"] / r["elapsed"]
     extra = {"hbm_copy_calibration_GBps": copy_calibration(torch, dev)}
-    if not args.no_extra:
-        log("extra: KDA prefill")
-        extra["kda_prefill"] = run_kda_prefill(torch, gdn, wl, dev)
-        log("extra: restore")
-        extra["restore"] = run_restore(torch, gdn, wl, dev)
-        log("extra: KDA decode with tracking (69 layers)")
-        extra["kda_decode_tracking"] = run_kda_decode_tracking(torch, gdn, wl, dev)
-        log("extra: prefix-hit restore + warm prefill (24 layers)")
-        extra["warm_prefill"] = run_warm_prefill(torch, gdn, wl, dev)
+    runs = {"kda_prefill": ("KDA prefill", run_kda_prefill),
+            "restore": ("restore", run_restore),
+            "kda_decode_tracking": ("KDA decode with tracking (69 layers)", run_kda_decode_tracking),
+            "warm_prefill": ("prefix-hit restore + warm prefill (24 layers)", run_warm_prefill),
+            "spec_verify": ("speculative verify + commit (32 layers)", run_spec_verify)}
+    chosen = [] if args.no_extra else [n for n in args.extra.split(",") if n]
+    for name in chosen:
+        if name not in runs:
+            sys.exit(f"unknown --extra workload {name!r}; choose from {', '.join(runs)}")
+        log(f"extra: {runs[name][0]}")
+        extra[name] = runs[name][1](torch, gdn, wl, dev)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

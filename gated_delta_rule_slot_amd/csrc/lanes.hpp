@@ -37,29 +37,30 @@ struct StateVec<uint16_t> {  // bf16
   static __device__ __forceinline__ raw from_f32(const float *f) {
     raw r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r[i] = uint32_t(f32_to_bf16(f[2 * i])) | (uint32_t(f32_to_bf16(f[2 * i + 1])) << 16);
+    for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
     return r;
   }
 };
 
 // Sum over each aligned group of N lanes, left in every lane of the group.  The
 // first four steps are DPP lane permutes inside the VALU (swap neighbours, swap
-// pairs, mirror within 8, mirror within 16); wider groups use the gfx950 row swaps
-// (lane ^ 16, lane ^ 32).  Each step adds the same two partial sums in every lane
-// of a group, so all lanes end with the same bits.
+// pairs, mirror within 8, mirror within 16), each folded into its add as one
+// v_add_f32_dpp (every source lane exists for these patterns, so the bound
+// control setting that allows the fold changes nothing); wider groups use the
+// gfx950 row swaps (lane ^ 16, lane ^ 32).  Each step adds the same two partial
+// sums in every lane of a group, so all lanes end with the same bits.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
   static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "group of 2^k lanes");
   const int lane = threadIdx.x & 63;
-  if constexpr (N >= 2) v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-  if constexpr (N >= 4) v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  if constexpr (N >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror
-  if constexpr (N >= 16) v += dpp_mov<0x140>(v); // row_mirror
+  if constexpr (N >= 2) v = dpp_mov<0xB1>(v) + v;   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) v = dpp_mov<0x4E>(v) + v;   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v = dpp_mov<0x141>(v) + v;  // row_half_mirror
+  if constexpr (N >= 16) v = dpp_mov<0x140>(v) + v; // row_mirror
   if constexpr (N >= 32) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     v += __uint_as_float((lane & 16) ? r[0] : r[1]);

@@ -943,8 +943,8 @@ __device__ __forceinline__ f32x4 load_state4<uint16_t>(const uint16_t *p) {
 __device__ __forceinline__ void store_state4(float *p, const f32x4 &v) { st4(p, v); }
 __device__ __forceinline__ void store_state4(uint16_t *p, const f32x4 &v) {
   u32x2 u;
-  u[0] = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
-  u[1] = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+  u[0] = pack_bf16x2(v[0], v[1]);
+  u[1] = pack_bf16x2(v[2], v[3]);
   *reinterpret_cast<u32x2 *>(p) = u;
 }
 __device__ __forceinline__ void store_state(float *p, float v) { *p = v; }

@@ -15,15 +15,19 @@
 //             out[b][n]
 //
 // Layout and work split.  A workgroup owns a block of state rows of one
-// (request, head) and walks the tree's nodes in index order (a valid tree lists
-// parents first).  Every lane owns the same 16-byte row pieces for every node,
-// so a node's state is re-read only by the lane that stored it: in-order
-// memory access within a lane makes that read see the store, and no barrier is
-// needed for the state.  When a node's parent is the node just computed (a
-// chain), the state stays in registers and only the stores go out.  The conv
-// windows are built from x and the live rows alone, never from another
-// workgroup's node buffers, so the row blocks of one head are independent;
-// the block with the first rows writes the node conv rows.
+// (request, head).  It visits the nodes grouped by parent (a stable sort by
+// parent index, which still puts every parent before its children because a
+// parent's index is smaller than its children's): a parent's state is loaded
+// once into registers and every child of it is computed from that copy, so the
+// state stream reads each parent once instead of once per child.  When a group's
+// parent is the node computed just before (a chain), its state is carried over
+// in registers and not read at all.  Every lane owns the same 16-byte row pieces
+// for every node, so a node's state is re-read only by the lane that stored it:
+// in-order memory access within a lane makes that read see the store, and no
+// barrier is needed for the state.  The conv windows are built from x and the
+// live rows alone, never from another workgroup's node buffers, so the row
+// blocks of one head are independent; the block with the first rows writes the
+// node conv rows.
 #include "common.hpp"
 #include "lanes.hpp"
 
@@ -35,7 +39,11 @@ struct VerifyShape {
   static constexpr int VEC = StateVec<TS>::N;
   static constexpr int LPR = D / VEC;                                 // lanes per row
   static constexpr int RPI = 64 / LPR;                                // rows per load instruction
-  static constexpr int ROWS = RPI * 8 < D ? RPI * 8 : D;              // state rows per wave
+  // state rows per wave: up to 8 pieces per lane, and at least two waves per
+  // head where the rows allow it
+  static constexpr int HALF = D / 2 > RPI ? D / 2 : RPI;
+  static constexpr int ROWS0 = RPI * 8 < HALF ? RPI * 8 : HALF;
+  static constexpr int ROWS = ROWS0 < D ? ROWS0 : D;
   static constexpr int WAVES = D / ROWS < 4 ? D / ROWS : 4;           // waves per workgroup
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int SPLIT = D / (ROWS * WAVES);                    // workgroups per head
@@ -43,7 +51,8 @@ struct VerifyShape {
 };
 
 template <int D, typename TS, int kAlphaMode>
-__global__ __launch_bounds__((VerifyShape<D, TS>::THREADS)) void gdn_verify_kernel(
+__global__ __launch_bounds__((VerifyShape<D, TS>::THREADS))
+__attribute__((amdgpu_waves_per_eu(4))) void gdn_verify_kernel(
     const TS *__restrict__ ssm, const uint16_t *__restrict__ conv, int32_t *err, int slots,
     int heads, VerifyArgs a) {
   using SV = StateVec<TS>;
@@ -70,7 +79,8 @@ __global__ __launch_bounds__((VerifyShape<D, TS>::THREADS)) void gdn_verify_kern
   const int slot = a.slot_table[b];
   const int64_t tok0 = int64_t(b) * T;  // node 0's row in x, alpha, beta and out
 
-  __shared__ int spar[kMaxTreeNodes];
+  __shared__ int spar[kMaxTreeNodes];  // parent of each node
+  __shared__ int sord[kMaxTreeNodes];  // nodes in visiting order: by parent, then index
   __shared__ __attribute__((aligned(16))) float sy[2][3 * D];  // q | k | v, double buffered
 
   const int32_t *par = a.parent + tok0;
@@ -81,6 +91,19 @@ __global__ __launch_bounds__((VerifyShape<D, TS>::THREADS)) void gdn_verify_kern
     bad |= (p < -1 || p >= i);
   }
   bad = __syncthreads_or(bad);
+  if (!bad) {
+    // rank of node c = nodes with a smaller parent + earlier nodes with the same parent
+    for (int c = threadIdx.x; c < T; c += SH::THREADS) {
+      const int p = spar[c];
+      int pos = 0;
+      for (int i = 0; i < T; ++i) {
+        const int q = spar[i];
+        pos += (q < p) | ((q == p) & (i < c));
+      }
+      sord[pos] = c;
+    }
+    __syncthreads();
+  }
 
   if (bad || slot <= 0 || slot >= slots) {
     for (int n = 0; n < T; ++n)
@@ -92,58 +115,106 @@ __global__ __launch_bounds__((VerifyShape<D, TS>::THREADS)) void gdn_verify_kern
     return;
   }
 
-  // ---- node 0 reads the live state (a valid tree's first node is a root) ----
+  // ---- the first group's parent is the live state (node 0 is a root) --------
   const int64_t hd = int64_t(D) * D;
   const TS *live = ssm + ((int64_t(a.layer) * slots + slot) * H + h) * hd;
   TS *nodes = static_cast<TS *>(a.node_ssm) + (tok0 * H + h) * hd;
   const int64_t nstride = int64_t(H) * hd;
   const int row_in_group = lane / LPR;
   const int col0 = (lane % LPR) * VEC;
-  SR cur[ITERS];
-  auto load_state = [&](const TS *blk) {
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int r = r0 + it * RPI + row_in_group;
-      if (r < r0 + ROWS) cur[it] = *reinterpret_cast<const SR *>(blk + int64_t(r) * D + col0);
-    }
+  // State blocks are addressed through buffer resources: one 32-bit lane offset
+  // plus a per-piece constant instead of a 64-bit address per piece.
+  constexpr int kBlockBytes = D * D * int(sizeof(TS));
+  constexpr int kPieceStep = RPI * D * int(sizeof(TS));  // bytes between a lane's pieces
+  const int loff = ((r0 + row_in_group) * D + col0) * int(sizeof(TS));
+  auto block = [&](const TS *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<TS *>(base), 0, kBlockBytes, 0x00020000);
   };
-  load_state(live);
+  SR cur[ITERS];  // the current group's parent state, in the pool dtype
+  {
+    const __amdgpu_buffer_rsrc_t lr = block(live);
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it)
+      if (ROWS % RPI == 0 || it * RPI + row_in_group < ROWS)
+        cur[it] = __builtin_bit_cast(SR, __builtin_amdgcn_raw_buffer_load_b128(lr, loff, it * kPieceStep, 0));
+  }
 
   // ---- conv items: CW channels of the head's q | k | v per thread ------------
   const uint16_t *lconv = conv + (int64_t(a.layer) * slots + slot) * kConvRows * C;
   uint16_t *nconv = a.node_conv + tok0 * kConvRows * C;
-  const int item = threadIdx.x;
-  const bool conv_lane = item < ITEMS;
+  const bool conv_lane = int(threadIdx.x) < ITEMS;
   const bool conv_writer = conv_lane && split == 0;
+  // lanes past the conv items still load item 0's x slice (unused), so that the
+  // number of loads in flight does not depend on the lane
+  const int item = conv_lane ? int(threadIdx.x) : 0;
   const int pt = item / (D / CW), jc = (item % (D / CW)) * CW;
   const int64_t ch = int64_t(pt) * H * D + int64_t(h) * D + jc;
-  CR w0v, w1v, w2v, xv;  // the window: three rows before the token, then the token
-  u32x4 wv[CW / 2];      // taps [C][4]: channels 2i and 2i+1 make up wv[i]
+  u32x4 wv[CW / 2];  // taps [C][4]: channels 2i and 2i+1 make up wv[i]
   if (conv_lane) {
-    w0v = *reinterpret_cast<const CR *>(lconv + ch);
-    w1v = *reinterpret_cast<const CR *>(lconv + C + ch);
-    w2v = *reinterpret_cast<const CR *>(lconv + 2 * C + ch);
     const u32x4 *wp = reinterpret_cast<const u32x4 *>(a.conv_w + ch * 4);
 #pragma unroll
     for (int i = 0; i < CW / 2; ++i) wv[i] = wp[i];
   }
-  // row j (0..2) of a window whose token follows node p: an ancestor's x, or
-  // the live row once the path runs out
+  // tree indices are the same in every lane: keep them in scalar registers so
+  // that branches on them stay branches (not selects that wait for loads)
+  auto parent_of = [&](int n) { return __builtin_amdgcn_readfirstlane(spar[n]); };
+  // row j (0..2) of the window whose token follows node p: an ancestor's x, or
+  // the live row once the path runs out; one load from a selected address
   auto window_row = [&](int p, int j) -> CR {
     int q = p;
-    for (int s = j; s < 2 && q >= 0; ++s) q = spar[q];   // climb 2 - j steps
-    if (q >= 0) return *reinterpret_cast<const CR *>(a.x + (tok0 + q) * C + ch);
-    // the path reached the live state after `used` of its rows were x rows
-    int used = 0;
-    for (int qq = p; qq >= 0 && used < 3; qq = spar[qq]) ++used;
-    return *reinterpret_cast<const CR *>(lconv + int64_t(j + used) * C + ch);
+    for (int s = j; s < 2 && q >= 0; ++s) q = parent_of(q);   // climb 2 - j steps
+    int used = 0;  // x rows on the path before it reaches the live state
+    for (int qq = p; qq >= 0 && used < 3; qq = parent_of(qq)) ++used;
+    const uint16_t *src = q >= 0 ? a.x + (tok0 + q) * C : lconv + int64_t(j + used) * C;
+    return *reinterpret_cast<const CR *>(src + ch);
   };
 
-  for (int n = 0; n < T; ++n) {
+  // What one node needs besides the parent state: the window rows (the parent's
+  // conv rows), its x slice, the decay of this lane's columns and beta.  Two
+  // sets alternate between consecutive nodes, so a successor's loads land in
+  // registers of their own and nothing has to be copied (a copy would have to
+  // wait for its load).
+  constexpr int NAL = kAlphaMode == GDN_ALPHA_PER_CHANNEL ? VEC : 1;
+  struct In {
+    CR w0, w1, w2, x;
+    float al[NAL];
+    float beta;
+  };
+  auto load_inputs = [&](int node, In &o) {
+    const int64_t tok = tok0 + node;
+    o.x = *reinterpret_cast<const CR *>(a.x + tok * C + ch);
+    if (kAlphaMode == GDN_ALPHA_PER_CHANNEL) {
+      const float *ap = a.alpha + (tok * H + h) * D + col0;
+#pragma unroll
+      for (int e = 0; e < NAL; ++e) o.al[e] = ap[e];
+    } else {
+      o.al[0] = a.alpha[tok * H + h];
+    }
+    o.beta = a.beta[tok * H + h];
+  };
+  In in0, in1;
+  in0.w0 = *reinterpret_cast<const CR *>(lconv + ch);
+  in0.w1 = *reinterpret_cast<const CR *>(lconv + C + ch);
+  in0.w2 = *reinterpret_cast<const CR *>(lconv + 2 * C + ch);
+  load_inputs(__builtin_amdgcn_readfirstlane(sord[0]), in0);
+
+  // Software pipeline: the loads a node's successor needs (its inputs, and on a
+  // change of group its window rows and parent state) are issued before this
+  // node's state stores.  Loads and stores share one in-order completion
+  // counter, so a load issued after the stores could only be waited for by
+  // waiting for the stores as well.
+  auto node_step = [&](int i, In &c, In &nx) {
+    const int n = __builtin_amdgcn_readfirstlane(sord[i]);
     const int64_t tok = tok0 + n;
-    float *y = sy[n & 1];
+    float *y = sy[i & 1];
+    // the next node: a sibling (same parent state), the child of this node
+    // (carry this node's state), or the first child of an earlier node (load)
+    const int nn = i + 1 < T ? __builtin_amdgcn_readfirstlane(sord[i + 1]) : -1;
+    const int np = nn >= 0 ? parent_of(nn) : -1;
+    const int p = parent_of(n);
+    const bool carry = nn >= 0 && np == n;
+    const bool regroup = nn >= 0 && !carry && np != p;  // np >= 0: only the first group has -1
     if (conv_lane) {
-      xv = *reinterpret_cast<const CR *>(a.x + tok * C + ch);
 #pragma unroll
       for (int e = 0; e < CW; ++e) {
         const int sh = (e & 1) ? 16 : 0;
@@ -152,47 +223,36 @@ __global__ __launch_bounds__((VerifyShape<D, TS>::THREADS)) void gdn_verify_kern
         };
         const u32x4 &w2 = wv[e >> 1];
         const int wb = (e & 1) * 2;
-        float acc = __uint_as_float(w2[wb] << 16) * pick(w0v);
-        acc = fmaf(__uint_as_float(w2[wb] & 0xffff0000u), pick(w1v), acc);
-        acc = fmaf(__uint_as_float(w2[wb + 1] << 16), pick(w2v), acc);
-        acc = fmaf(__uint_as_float(w2[wb + 1] & 0xffff0000u), pick(xv), acc);
+        float acc = __uint_as_float(w2[wb] << 16) * pick(c.w0);
+        acc = fmaf(__uint_as_float(w2[wb] & 0xffff0000u), pick(c.w1), acc);
+        acc = fmaf(__uint_as_float(w2[wb + 1] << 16), pick(c.w2), acc);
+        acc = fmaf(__uint_as_float(w2[wb + 1] & 0xffff0000u), pick(c.x), acc);
         if (a.flags & GDN_F_CONV_SILU) acc = acc / (1.f + __expf(-acc));
         y[pt * D + jc + e] = acc;
       }
       if (conv_writer) {
         uint16_t *dst = nconv + int64_t(n) * kConvRows * C;
-        *reinterpret_cast<CR *>(dst + ch) = w1v;
-        *reinterpret_cast<CR *>(dst + C + ch) = w2v;
-        *reinterpret_cast<CR *>(dst + 2 * C + ch) = xv;
+        *reinterpret_cast<CR *>(dst + ch) = c.w1;
+        *reinterpret_cast<CR *>(dst + C + ch) = c.w2;
+        *reinterpret_cast<CR *>(dst + 2 * C + ch) = c.x;
       }
     }
-    float al[VEC];
-    if (kAlphaMode == GDN_ALPHA_PER_CHANNEL) {
-      const float *ap = a.alpha + (tok * H + h) * D + col0;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) al[e] = ap[e];
-    } else {
-      const float av = a.alpha[tok * H + h];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) al[e] = av;
-    }
-    const float beta = a.beta[tok * H + h];
-    __syncthreads();  // y complete (the other buffer is free again for node n + 1)
+    __syncthreads();  // y complete (the other buffer is free again for the next node)
 
     const float *sq = y, *sk = y + D, *sv = y + 2 * D;
     float kinv = 1.f, qinv = 1.f;
     if (a.flags & GDN_F_L2NORM_K) {
       float ss = 0.f;
-      for (int i = lane; i < D; i += 64) ss = fmaf(sk[i], sk[i], ss);
+      for (int j = lane; j < D; j += 64) ss = fmaf(sk[j], sk[j], ss);
       kinv = 1.f / sqrtf(wave_sum(ss) + 1e-6f);
     }
     if (a.flags & GDN_F_L2NORM_Q) {
       float ss = 0.f;
-      for (int i = lane; i < D; i += 64) ss = fmaf(sq[i], sq[i], ss);
+      for (int j = lane; j < D; j += 64) ss = fmaf(sq[j], sq[j], ss);
       qinv = 1.f / sqrtf(wave_sum(ss) + 1e-6f);
     }
     float kq = 0.f;
-    for (int i = lane; i < D; i += 64) kq = fmaf(sk[i] * kinv, sq[i] * qinv, kq);
+    for (int j = lane; j < D; j += 64) kq = fmaf(sk[j] * kinv, sq[j] * qinv, kq);
     kq = wave_sum(kq);
     float kk[VEC], qq[VEC];
 #pragma unroll
@@ -201,18 +261,35 @@ __global__ __launch_bounds__((VerifyShape<D, TS>::THREADS)) void gdn_verify_kern
       qq[e] = sq[col0 + e] * qinv;
     }
 
-    TS *dst = nodes + int64_t(n) * nstride;
-    uint16_t *out = a.out + (tok * H + h) * D;
+    // ---- the successor's loads, ahead of this node's stores -------------------
+    // (issued for every node, the last one re-reading its own, so that the wait
+    // counts the compiler derives hold on every path)
+    load_inputs(nn >= 0 ? nn : n, nx);
+    // the successor's window rows, always loaded (x rows and live rows are small
+    // and cached), so they never wait on a select
+    {
+      const int wp = nn >= 0 ? np : p;
+      nx.w0 = window_row(wp, 0);
+      nx.w1 = window_row(wp, 1);
+      nx.w2 = window_row(wp, 2);
+    }
+    const __amdgpu_buffer_rsrc_t nsrc = block(nodes + int64_t(regroup ? np : 0) * nstride);
+    const __amdgpu_buffer_rsrc_t dst = block(nodes + int64_t(n) * nstride);
+    const __amdgpu_buffer_rsrc_t orow =
+        __builtin_amdgcn_make_buffer_rsrc(a.out + (tok * H + h) * D, 0, D * 2, 0x00020000);
+    const float beta = c.beta;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       const int r = r0 + it * RPI + row_in_group;
-      const bool on = r < r0 + ROWS;
+      // whole row blocks (every supported shape but the smallest) need no test,
+      // which keeps the stores unconditional for the wait counts
+      const bool on = ROWS % RPI == 0 || r < r0 + ROWS;
       float s[VEC];
       SV::to_f32(cur[it], s);
       float pu = 0.f, pq = 0.f;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        s[e] *= al[e];
+        s[e] *= c.al[NAL == 1 ? 0 : e];
         pu = fmaf(s[e], kk[e], pu);
         pq = fmaf(s[e], qq[e], pq);
       }
@@ -222,29 +299,26 @@ __global__ __launch_bounds__((VerifyShape<D, TS>::THREADS)) void gdn_verify_kern
         const float d = beta * (sv[r] - pu);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) s[e] = fmaf(d, kk[e], s[e]);
-        cur[it] = SV::from_f32(s);  // what the pool dtype holds: a child starts from this
-        *reinterpret_cast<SR *>(dst + int64_t(r) * D + col0) = cur[it];
-        if ((lane % LPR) == 0) out[r] = f32_to_bf16(a.scale * fmaf(d, kq, pq));
+        const SR w = SV::from_f32(s);  // what the pool dtype holds: a child starts from this
+        if (carry) cur[it] = w;
+        else if (regroup)
+          cur[it] = __builtin_bit_cast(SR, __builtin_amdgcn_raw_buffer_load_b128(nsrc, loff, it * kPieceStep, 0));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), dst, loff, it * kPieceStep, 0);
+        // every lane of the row stores the same value: no divergent branch
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(a.scale * fmaf(d, kq, pq)), orow, r * 2, 0, 0);
       }
     }
+  };
 
-    // ---- the next node's parent: carried, or re-read -----------------------
-    if (n + 1 < T) {
-      const int p = spar[n + 1];
-      if (p != n) {
-        load_state(p < 0 ? live : nodes + int64_t(p) * nstride);
-        if (conv_lane) {
-          w0v = window_row(p, 0);
-          w1v = window_row(p, 1);
-          w2v = window_row(p, 2);
-        }
-      } else if (conv_lane) {
-        w0v = w1v;
-        w1v = w2v;
-        w2v = xv;
-      }
-    }
+  // node 0 runs ahead of the loop, so that every entry into the loop body
+  // follows a whole node step and the wait counts are the same on each entry
+  node_step(0, in0, in1);
+  int i = 1;
+  for (; i + 1 < T; i += 2) {
+    node_step(i, in1, in0);
+    node_step(i + 1, in0, in1);
   }
+  if (i < T) node_step(i, in1, in0);
 }
 
 template <int D, typename TS>
