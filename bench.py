@@ -126,7 +126,7 @@ def measured_traffic():
     except OSError:
         return None
     src = b"".join(open(os.path.join(ROOT, "gated_delta_rule_slot_amd", "csrc", f), "rb").read()
-                   for f in ("decode.hip", "common.hpp"))
+                   for f in ("decode.hip", "lanes.hpp", "common.hpp"))
     if hashlib.sha256(src).hexdigest() != rec.get("sources_sha256"):
         return None
     return rec["traffic_bytes_per_launch"]

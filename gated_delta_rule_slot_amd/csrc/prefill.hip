@@ -35,11 +35,19 @@
 // (pad tokens have a = 1, b = 0, k = q = v = 0, which leaves the state exactly
 // unchanged), so every snapshot boundary is a chunk end.
 //
-// Decay products are handled in log2 space inside a chunk: every factor is
-// exp2 of a difference of partial sums that is <= 0, except on the diagonal
-// 16x16 blocks where the factorisation goes through the block's middle token
-// (factors up to 2^60); a block whose channels span more than that uses an
-// exact per-pair evaluation instead.
+// Decay products are handled in log2 space inside a chunk, on one of two paths
+// chosen per chunk by the prep workgroup:
+//   chunk reference (no 16-token block decays a channel by more than 2^-24):
+//         with L the log2 decay cumulated from the chunk start, the factors split
+//         exactly into P = k 2^L, R = k 2^-L, Q = q 2^L (all within 2^+-96), so
+//         A = P R^T and M = Q R^T are single products of planes built once, and
+//         (I + Diag(b) A) X = Diag(b) [V | P] is solved by block forward
+//         substitution on k = 16 MFMA;
+//   blockwise (any decay): every factor is exp2 of a difference of partial sums
+//         that is <= 0, except on the diagonal 16x16 blocks where the
+//         factorisation goes through the block's middle token (factors up to
+//         2^60); a block whose channels span more than that uses an exact
+//         per-pair evaluation instead.
 #include "common.hpp"
 
 namespace gdn {

@@ -81,6 +81,8 @@ __attribute__((amdgpu_waves_per_eu(4))) void gdn_verify_kernel(
 
   __shared__ int spar[kMaxTreeNodes];  // parent of each node
   __shared__ int sord[kMaxTreeNodes];  // nodes in visiting order: by parent, then index
+  // per visiting position: {node, successor, successor's parent, flags}, see below
+  __shared__ int4 splan[kMaxTreeNodes];
   __shared__ __attribute__((aligned(16))) float sy[2][3 * D];  // q | k | v, double buffered
 
   const int32_t *par = a.parent + tok0;
@@ -101,6 +103,27 @@ __attribute__((amdgpu_waves_per_eu(4))) void gdn_verify_kernel(
         pos += (q < p) | ((q == p) & (i < c));
       }
       sord[pos] = c;
+    }
+    __syncthreads();
+    // The walk's plan, one entry per position i, so that a step reads its tree
+    // facts with one shared-memory load instead of chasing parents:
+    //   x: node n,  y: successor nn (n itself after the last node),
+    //   z: nn's parent np (the group's parent state),
+    //   w: bits 0-1 used = x rows in nn's window (its nearest ancestors, up to 3),
+    //      bits 2-11 np's parent, 12-21 np's grandparent (window rows 1 and 0),
+    //      bit 22 carry (np is n: keep n's state), bit 23 regroup (load np's state).
+    for (int i = threadIdx.x; i < T; i += SH::THREADS) {
+      const int n = sord[i], p = spar[n];
+      const bool last = i + 1 == T;
+      const int nn = last ? n : sord[i + 1];
+      const int np = last ? p : spar[nn];
+      const bool carry = !last && np == n;
+      const bool regroup = !last && !carry && np != p;
+      const int a1 = np >= 0 ? spar[np] : -1;
+      const int a2 = a1 >= 0 ? spar[a1] : -1;
+      const int used = np < 0 ? 0 : a1 < 0 ? 1 : a2 < 0 ? 2 : 3;
+      splan[i] = make_int4(n, nn, np, used | (max(a1, 0) << 2) | (max(a2, 0) << 12) |
+                                          (int(carry) << 22) | (int(regroup) << 23));
     }
     __syncthreads();
   }
@@ -155,17 +178,12 @@ __attribute__((amdgpu_waves_per_eu(4))) void gdn_verify_kernel(
 #pragma unroll
     for (int i = 0; i < CW / 2; ++i) wv[i] = wp[i];
   }
-  // tree indices are the same in every lane: keep them in scalar registers so
-  // that branches on them stay branches (not selects that wait for loads)
-  auto parent_of = [&](int n) { return __builtin_amdgcn_readfirstlane(spar[n]); };
-  // row j (0..2) of the window whose token follows node p: an ancestor's x, or
-  // the live row once the path runs out; one load from a selected address
-  auto window_row = [&](int p, int j) -> CR {
-    int q = p;
-    for (int s = j; s < 2 && q >= 0; ++s) q = parent_of(q);   // climb 2 - j steps
-    int used = 0;  // x rows on the path before it reaches the live state
-    for (int qq = p; qq >= 0 && used < 3; qq = parent_of(qq)) ++used;
-    const uint16_t *src = q >= 0 ? a.x + (tok0 + q) * C : lconv + int64_t(j + used) * C;
+  // Row j (0..2) of a window whose last `used` rows are x rows of the nodes
+  // q2 (row 2), q1 (row 1), q0 (row 0) and whose first rows are live rows:
+  // one load from a selected (scalar) address.
+  auto window_row = [&](int j, int used, int q0, int q1, int q2) -> CR {
+    const int q = j == 0 ? q0 : j == 1 ? q1 : q2;
+    const uint16_t *src = j >= 3 - used ? a.x + (tok0 + q) * C : lconv + int64_t(j + used) * C;
     return *reinterpret_cast<const CR *>(src + ch);
   };
 
@@ -196,7 +214,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void gdn_verify_kernel(
   in0.w0 = *reinterpret_cast<const CR *>(lconv + ch);
   in0.w1 = *reinterpret_cast<const CR *>(lconv + C + ch);
   in0.w2 = *reinterpret_cast<const CR *>(lconv + 2 * C + ch);
-  load_inputs(__builtin_amdgcn_readfirstlane(sord[0]), in0);
+  load_inputs(__builtin_amdgcn_readfirstlane(splan[0].x), in0);
 
   // Software pipeline: the loads a node's successor needs (its inputs, and on a
   // change of group its window rows and parent state) are issued before this
@@ -204,16 +222,19 @@ __attribute__((amdgpu_waves_per_eu(4))) void gdn_verify_kernel(
   // counter, so a load issued after the stores could only be waited for by
   // waiting for the stores as well.
   auto node_step = [&](int i, In &c, In &nx) {
-    const int n = __builtin_amdgcn_readfirstlane(sord[i]);
+    // tree facts in scalar registers, so that branches on them stay branches
+    // (not selects that would wait for loads)
+    const int4 pl = splan[i];
+    const int n = __builtin_amdgcn_readfirstlane(pl.x);
+    const int nn = __builtin_amdgcn_readfirstlane(pl.y);
+    const int np = __builtin_amdgcn_readfirstlane(pl.z);
+    const int fl = __builtin_amdgcn_readfirstlane(pl.w);
     const int64_t tok = tok0 + n;
     float *y = sy[i & 1];
     // the next node: a sibling (same parent state), the child of this node
     // (carry this node's state), or the first child of an earlier node (load)
-    const int nn = i + 1 < T ? __builtin_amdgcn_readfirstlane(sord[i + 1]) : -1;
-    const int np = nn >= 0 ? parent_of(nn) : -1;
-    const int p = parent_of(n);
-    const bool carry = nn >= 0 && np == n;
-    const bool regroup = nn >= 0 && !carry && np != p;  // np >= 0: only the first group has -1
+    const bool carry = (fl >> 22) & 1;
+    const bool regroup = (fl >> 23) & 1;  // then np >= 0: only the first group has -1
     if (conv_lane) {
 #pragma unroll
       for (int e = 0; e < CW; ++e) {
@@ -264,14 +285,14 @@ __attribute__((amdgpu_waves_per_eu(4))) void gdn_verify_kernel(
     // ---- the successor's loads, ahead of this node's stores -------------------
     // (issued for every node, the last one re-reading its own, so that the wait
     // counts the compiler derives hold on every path)
-    load_inputs(nn >= 0 ? nn : n, nx);
+    load_inputs(nn, nx);
     // the successor's window rows, always loaded (x rows and live rows are small
     // and cached), so they never wait on a select
     {
-      const int wp = nn >= 0 ? np : p;
-      nx.w0 = window_row(wp, 0);
-      nx.w1 = window_row(wp, 1);
-      nx.w2 = window_row(wp, 2);
+      const int used = fl & 3, q1 = (fl >> 2) & 1023, q0 = (fl >> 12) & 1023;
+      nx.w0 = window_row(0, used, q0, q1, np);
+      nx.w1 = window_row(1, used, q0, q1, np);
+      nx.w2 = window_row(2, used, q0, q1, np);
     }
     const __amdgpu_buffer_rsrc_t nsrc = block(nodes + int64_t(regroup ? np : 0) * nstride);
     const __amdgpu_buffer_rsrc_t dst = block(nodes + int64_t(n) * nstride);
@@ -303,7 +324,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void gdn_verify_kernel(
         if (carry) cur[it] = w;
         else if (regroup)
           cur[it] = __builtin_bit_cast(SR, __builtin_amdgcn_raw_buffer_load_b128(nsrc, loff, it * kPieceStep, 0));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), dst, loff, it * kPieceStep, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), dst, loff, it * kPieceStep, 2);
         // every lane of the row stores the same value: no divergent branch
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(a.scale * fmaf(d, kq, pq)), orow, r * 2, 0, 0);
       }
