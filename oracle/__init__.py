@@ -39,6 +39,13 @@ class _Pool(ct.Structure):
     ]
 
 
+class _Ring(ct.Structure):
+    _fields_ = [
+        ("positions", ct.c_int32), ("alpha_mode", ct.c_int32), ("rawk", _u16p), ("rawv", _u16p),
+        ("g", _f32p), ("beta", _f32p), ("xrow", _u16p),
+    ]
+
+
 class RestoreOp(ct.Structure):
     _fields_ = [
         ("linear_state_id", ct.c_int32),
@@ -84,6 +91,15 @@ def lib(precision: str = "f64"):
     L.oracle_accept_scatter.argtypes = [
         ct.POINTER(_Pool), ct.c_int32, ct.c_int32, ct.c_int32, _i32p, _i32p, _i32p, _i32p,
         ct.c_int32, _i32p, _i32p, ct.c_void_p, _u16p,
+    ]
+    L.oracle_ring_bytes.argtypes = [ct.POINTER(_Pool), ct.c_int32, ct.c_int32, ct.POINTER(ct.c_size_t)]
+    L.oracle_replay_verify.argtypes = [
+        ct.POINTER(_Pool), ct.POINTER(_Ring), ct.c_int32, ct.c_int32, ct.c_int32, _i32p, _u16p,
+        _u16p, _f32p, ct.c_int32, _f32p, ct.c_float, ct.c_uint32, _u16p, _f64p,
+    ]
+    L.oracle_replay_commit.argtypes = [
+        ct.POINTER(_Pool), ct.POINTER(_Ring), ct.c_int32, ct.c_int32, _i32p, _i32p, ct.c_int32,
+        ct.c_uint32, _i32p, ct.c_int32, _i32p, _i32p,
     ]
     L.oracle_recurrence_head.argtypes = [ct.c_int32] * 3 + [_f64p] * 5 + [ct.c_double, _f64p, _f64p]
     L.oracle_recurrence_head.restype = None
@@ -301,6 +317,81 @@ def accept_scatter(pool: Pool, layer, slot_table, parent, accepted, node_ssm, no
         _p(nc, _u16p))
     if err & 4:
         raise ValueError("oracle_accept_scatter: bad argument")
+    return err
+
+
+def ring_bytes(pool: Pool, positions, alpha_mode, precision="f64"):
+    """Byte sizes (rawk, rawv, g, beta, xrow) of a ReplaySSM ring for the pool's shape."""
+    b = (ct.c_size_t * 5)()
+    ps = pool._struct()
+    if lib(precision).oracle_ring_bytes(ct.byref(ps), positions, alpha_mode, b):
+        raise ValueError("bad ring shape")
+    return tuple(b[i] for i in range(5))
+
+
+class Ring:
+    """Host image of a ReplaySSM ring for a pool (zero-filled)."""
+
+    def __init__(self, pool: Pool, positions, alpha_mode):
+        L, N, H, K, V = pool.layers, pool.slots, pool.heads, pool.head_k, pool.head_v
+        self.positions, self.alpha_mode = positions, alpha_mode
+        self.rawk = np.zeros((L, N, H, positions, K), dtype=np.uint16)
+        self.rawv = np.zeros((L, N, H, positions, V), dtype=np.uint16)
+        gshape = (L, N, H, positions, K) if alpha_mode == ALPHA_PER_CHANNEL else (L, N, H, positions)
+        self.g = np.zeros(gshape, dtype=np.float32)
+        self.beta = np.zeros((L, N, H, positions), dtype=np.float32)
+        self.xrow = np.zeros((L, N, positions, pool.channels), dtype=np.uint16)
+
+    def copy(self):
+        r = object.__new__(Ring)
+        r.positions, r.alpha_mode = self.positions, self.alpha_mode
+        for n in ("rawk", "rawv", "g", "beta", "xrow"):
+            setattr(r, n, getattr(self, n).copy())
+        return r
+
+    def _struct(self):
+        return _Ring(self.positions, self.alpha_mode, _p(self.rawk, _u16p), _p(self.rawv, _u16p),
+                     _p(self.g, _f32p), _p(self.beta, _f32p), _p(self.xrow, _u16p))
+
+
+def replay_verify(pool: Pool, ring: Ring, layer, slot_table, x, conv_w, alpha, alpha_mode, beta,
+                  scale=1.0, flags=L2NORM_K, exact=False, precision="f64"):
+    """Verify a draft chain of D tokens per request (x [B][D][C], alpha [B][D][H](,K), beta
+    [B][D][H]) from the live slots, which stay as they are; fills ring positions 0..D-1.
+    Returns ``(out[B,D,H,V], err)`` or, with ``exact=True``, ``(out, err, out_exact)``."""
+    st = _c(slot_table, np.int32)
+    xs = _c(x, np.uint16)
+    B, D = xs.shape[0], xs.shape[1]
+    H, V = pool.heads, pool.head_v
+    w = _c(conv_w, np.uint16)
+    a, bt = _c(alpha, np.float32), _c(beta, np.float32)
+    out = np.zeros((B, D, H, V), dtype=np.uint16)
+    oe = np.zeros((B, D, H, V), dtype=np.float64) if exact else None
+    ps, rs = pool._struct(), ring._struct()
+    err = lib(precision).oracle_replay_verify(
+        ct.byref(ps), ct.byref(rs), layer, B, D, _p(st, _i32p), _p(xs, _u16p), _p(w, _u16p),
+        _p(a, _f32p), alpha_mode, _p(bt, _f32p), scale, flags, _p(out, _u16p), _p(oe, _f64p))
+    if err & 4:
+        raise ValueError("oracle_replay_verify: bad argument")
+    return (out, err, oe) if exact else (out, err)
+
+
+def replay_commit(pool: Pool, ring: Ring, layer, slot_table, accepted, alpha_mode, flags=L2NORM_K,
+                  seq_len_before=None, track_interval=0, track_slots=None, next_track_idx=None,
+                  precision="f64"):
+    """Fold ring positions 0..accepted[b]-1 into each live slot (modifies ``pool``)."""
+    st = _c(slot_table, np.int32)
+    B = st.shape[0]
+    acc = _c(accepted, np.int32)
+    sb = _c(seq_len_before if seq_len_before is not None else np.zeros(B), np.int32)
+    ts = _c(track_slots, np.int32) if track_slots is not None else None
+    nt = _c(next_track_idx, np.int32) if next_track_idx is not None else None
+    ps, rs = pool._struct(), ring._struct()
+    err = lib(precision).oracle_replay_commit(
+        ct.byref(ps), ct.byref(rs), layer, B, _p(st, _i32p), _p(acc, _i32p), alpha_mode, flags,
+        _p(sb, _i32p), track_interval, _p(ts, _i32p), _p(nt, _i32p))
+    if err & 4:
+        raise ValueError("oracle_replay_commit: bad argument")
     return err
 
 

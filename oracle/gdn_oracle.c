@@ -294,10 +294,12 @@ static void store_head(const unit_ctx *u, int slot, int h, const real *S, real R
 
 /* One token of head h: causal conv over [R0, R1, R2, x_t] (tap 3 is the current
  * token) with the rows then shifted to [R1, R2, x_t], optional SiLU, key (and
- * query) normalisation, then the recurrence.  y holds the 2K+V conv outputs. */
+ * query) normalisation, then the recurrence.  y holds the 2K+V conv outputs; raw
+ * (K+V values, may be NULL) receives k and v as they leave the conv, before the
+ * key is normalised. */
 static void step_token(const unit_ctx *u, const size_t *chan, int nchan, real *S,
                        real (*R)[CONV_ROWS], const uint16_t *xt, const float *alpha,
-                       int alpha_mode, real beta, real *y, real *a, real *o) {
+                       int alpha_mode, real beta, real *y, real *a, real *o, real *raw) {
   const int K = u->K, V = u->V;
   for (int i = 0; i < nchan; ++i) {
     const uint16_t *w = u->conv_w + chan[i] * CONV_TAPS;
@@ -314,6 +316,8 @@ static void step_token(const unit_ctx *u, const size_t *chan, int nchan, real *S
     R[i][2] = xi;
   }
   real *q = y, *k = y + K, *v = y + 2 * K;
+  if (raw)
+    for (int i = 0; i < K + V; ++i) raw[i] = y[K + i];
   if (u->flags & ORACLE_L2NORM_K) {
     real ss = 0;
     for (int c = 0; c < K; ++c) ss += k[c] * k[c];
@@ -374,7 +378,7 @@ static int fold_head(const unit_ctx *u, int h, int live_slot, int warm, int32_t 
   for (int32_t t = 0; t < n; ++t) {
     const float *at = alpha + ((size_t)t * H + h) * (alpha_mode == ORACLE_ALPHA_PER_CHANNEL ? K : 1);
     step_token(u, chan, nchan, S, R, x + (size_t)t * u->C, at, alpha_mode,
-               (real)beta[(size_t)t * H + h], y, a, o);
+               (real)beta[(size_t)t * H + h], y, a, o, NULL);
     for (int r = 0; r < V; ++r) {
       size_t oi = ((size_t)t * H + h) * V + r;
       out[oi] = oracle_bf16_round((double)o[r]);
@@ -577,7 +581,7 @@ int oracle_verify_tree(const oracle_pool *pool, int32_t layer, int32_t batch, in
           for (int j = 0; j < CONV_ROWS; ++j) R[i][j] = widen(cblk[(size_t)j * u.C + chan[i]]);
         const size_t tok = (size_t)b * nodes + n;
         step_token(&u, chan, nchan, S, R, x + tok * u.C, alpha + (tok * H + h) * aw, alpha_mode,
-                   (real)beta[tok * H + h], y, a, o);
+                   (real)beta[tok * H + h], y, a, o, NULL);
         for (int r = 0; r < V; ++r) {
           size_t oi = (tok * H + h) * V + r;
           out[oi] = oracle_bf16_round((double)o[r]);
@@ -653,6 +657,183 @@ int oracle_accept_scatter(const oracle_pool *pool, int32_t layer, int32_t batch,
     }
     copy_node(pool, layer, node_ssm, node_conv, nodes, b, acc, slot);
     free(path);
+  }
+  return err;
+}
+
+/* --------------------------------------------------------- ReplaySSM ring ---- */
+
+/* Element offsets into the ring arrays of (layer, slot, head, position). */
+static size_t ring_row(const oracle_pool *p, const oracle_ring *r, int layer, int slot, int h, int t) {
+  return (((size_t)layer * p->slots + slot) * p->heads + h) * r->positions + t;
+}
+
+int oracle_ring_bytes(const oracle_pool *pool, int32_t positions, int32_t alpha_mode,
+                      size_t bytes[5]) {
+  if (!pool || positions <= 0 || (alpha_mode != ORACLE_ALPHA_PER_HEAD && alpha_mode != ORACLE_ALPHA_PER_CHANNEL))
+    return 4;
+  const size_t rows = (size_t)pool->layers * pool->slots * pool->heads * positions;
+  bytes[0] = rows * pool->head_k * 2;                                         /* rawk */
+  bytes[1] = rows * pool->head_v * 2;                                         /* rawv */
+  bytes[2] = rows * (alpha_mode == ORACLE_ALPHA_PER_CHANNEL ? pool->head_k : 1) * 4;  /* g */
+  bytes[3] = rows * 4;                                                        /* beta */
+  bytes[4] = (size_t)pool->layers * pool->slots * positions * conv_channels(pool) * 2;  /* xrow */
+  return 0;
+}
+
+static int ring_ok(const oracle_pool *p, const oracle_ring *r, int32_t alpha_mode) {
+  return r && r->positions > 0 && r->alpha_mode == alpha_mode && r->rawk && r->rawv && r->g &&
+         r->beta && r->xrow && p;
+}
+
+/* Speculative verify of a draft chain with a ReplaySSM ring (page
+ * "企业官网建设流程全解析", Kimi K3 notes, section "ReplaySSM": the verify still
+ * produces every position's output but keeps no per-position state; it records
+ * the inputs that regenerate the state: k before L2 normalisation and v before
+ * the delta correction, both as they leave the conv, in bf16, the decay g and
+ * beta in fp32).  Draft token t of request b follows token t-1 (t = 0 follows
+ * the live slot).  out [B][D][H][V] equals D consecutive decode steps; the live
+ * slot is only read.  Ring position t of the request's slot receives rawk, rawv,
+ * g = alpha, beta, and the conv input row x_t (the conv state must advance with
+ * the accepted tokens; post-conv values cannot give it back). */
+int oracle_replay_verify(const oracle_pool *pool, const oracle_ring *ring, int32_t layer,
+                         int32_t batch, int32_t draft, const int32_t *slot_table,
+                         const uint16_t *x, const uint16_t *conv_w, const float *alpha,
+                         int32_t alpha_mode, const float *beta, float scale, uint32_t flags,
+                         uint16_t *out, double *out_exact) {
+  if (!pool_ok(pool, layer) || batch < 0 || draft < 1 || !ring_ok(pool, ring, alpha_mode) ||
+      draft > ring->positions)
+    return 4;
+  unit_ctx u = {pool, layer, pool->head_k, pool->head_v, pool->heads, conv_channels(pool),
+                conv_w, (real)scale, flags};
+  const int H = pool->heads, K = u.K, V = u.V, nchan = 2 * K + V;
+  const size_t aw = alpha_mode == ORACLE_ALPHA_PER_CHANNEL ? (size_t)K : 1;
+  int err = 0;
+#pragma omp parallel for collapse(2) reduction(| : err) schedule(dynamic)
+  for (int b = 0; b < batch; ++b) {
+    for (int h = 0; h < H; ++h) {
+      const int slot = slot_table[b];
+      if (slot <= 0 || slot >= pool->slots) {
+        if (slot >= pool->slots) err |= 1;
+        for (int t = 0; t < draft; ++t)
+          for (int r = 0; r < V; ++r) {
+            size_t oi = (((size_t)b * draft + t) * H + h) * V + r;
+            out[oi] = 0;
+            if (out_exact) out_exact[oi] = 0;
+          }
+        continue;
+      }
+      size_t *chan = head_channels(&u, h);
+      real *S = malloc(sizeof(real) * (size_t)V * K);
+      real (*R)[CONV_ROWS] = malloc(sizeof(real) * CONV_ROWS * nchan);
+      real *y = malloc(sizeof(real) * nchan), *a = malloc(sizeof(real) * K);
+      real *o = malloc(sizeof(real) * V), *raw = malloc(sizeof(real) * (K + V));
+      const unsigned char *sblk = ssm_block(pool, layer, slot);
+      const uint16_t *cblk = conv_block(pool, layer, slot);
+      for (size_t i = 0; i < (size_t)V * K; ++i) S[i] = load_ssm(pool, sblk, (size_t)h * V * K + i);
+      for (int i = 0; i < nchan; ++i)
+        for (int j = 0; j < CONV_ROWS; ++j) R[i][j] = widen(cblk[(size_t)j * u.C + chan[i]]);
+      for (int t = 0; t < draft; ++t) {
+        const size_t tok = (size_t)b * draft + t;
+        const uint16_t *xt = x + tok * u.C;
+        step_token(&u, chan, nchan, S, R, xt, alpha + (tok * H + h) * aw, alpha_mode,
+                   (real)beta[tok * H + h], y, a, o, raw);
+        for (int r = 0; r < V; ++r) {
+          size_t oi = (tok * H + h) * V + r;
+          out[oi] = oracle_bf16_round((double)o[r]);
+          if (out_exact) out_exact[oi] = (double)o[r];
+        }
+        const size_t row = ring_row(pool, ring, layer, slot, h, t);
+        for (int c = 0; c < K; ++c) ring->rawk[row * K + c] = oracle_bf16_round((double)raw[c]);
+        for (int c = 0; c < V; ++c) ring->rawv[row * V + c] = oracle_bf16_round((double)raw[K + c]);
+        for (size_t c = 0; c < aw; ++c) ring->g[row * aw + c] = alpha[(tok * H + h) * aw + c];
+        ring->beta[row] = beta[tok * H + h];
+        uint16_t *xr = ring->xrow + (((size_t)layer * pool->slots + slot) * ring->positions + t) * u.C;
+        for (int i = 0; i < nchan; ++i) xr[chan[i]] = xt[chan[i]];
+      }
+      free(chan); free(S); free(R); free(y); free(a); free(o); free(raw);
+    }
+  }
+  return err;
+}
+
+/* The exact-fold commit (same page and section: after acceptance only the
+ * accepted prefix is replayed, in recurrent order, and the result is written
+ * back to the slot; page "SGLang之MambaRadixCache机制解析", section 9.10: the
+ * 256-boundary check happens during the replay).  accepted[b] tokens (0 .. ring
+ * positions) are folded from ring positions 0 .. accepted-1 of the request's
+ * slot: k = rawk normalised (flag), v = rawv, S' = S Diag(g), d = beta (v - S'k),
+ * S = S' + d k^T, conv rows shifted through the x rows.  For every i in
+ * [1, accepted] with (seq_len_before + i) % track_interval == 0 the state and
+ * conv rows after token i go to track_slots[2b + ((next_track_idx[b] + j) & 1)]
+ * for the j-th such i.  The state is rounded to the pool dtype only where it is
+ * stored.  Error bits: 1 bad live slot, 2 bad track slot, 8 accepted outside
+ * [0, positions]. */
+int oracle_replay_commit(const oracle_pool *pool, const oracle_ring *ring, int32_t layer,
+                         int32_t batch, const int32_t *slot_table, const int32_t *accepted,
+                         int32_t alpha_mode, uint32_t flags, const int32_t *seq_len_before,
+                         int32_t track_interval, const int32_t *track_slots,
+                         const int32_t *next_track_idx) {
+  if (!pool_ok(pool, layer) || batch < 0 || !ring_ok(pool, ring, alpha_mode) || track_interval < 0)
+    return 4;
+  unit_ctx u = {pool, layer, pool->head_k, pool->head_v, pool->heads, conv_channels(pool),
+                NULL, 1, flags};
+  const int H = pool->heads, K = u.K, V = u.V, nchan = 2 * K + V;
+  const size_t aw = alpha_mode == ORACLE_ALPHA_PER_CHANNEL ? (size_t)K : 1;
+  int err = 0;
+#pragma omp parallel for collapse(2) reduction(| : err) schedule(dynamic)
+  for (int b = 0; b < batch; ++b) {
+    for (int h = 0; h < H; ++h) {
+      const int slot = slot_table[b], n = accepted[b];
+      if (n < 0 || n > ring->positions) {
+        err |= 8;
+        continue;
+      }
+      if (slot <= 0 || slot >= pool->slots) {
+        if (slot >= pool->slots) err |= 1;
+        continue;
+      }
+      if (n == 0) continue;
+      size_t *chan = head_channels(&u, h);
+      real *S = malloc(sizeof(real) * (size_t)V * K);
+      real (*R)[CONV_ROWS] = malloc(sizeof(real) * CONV_ROWS * nchan);
+      real *k = malloc(sizeof(real) * K), *v = malloc(sizeof(real) * V);
+      real *a = malloc(sizeof(real) * K), *q = calloc(K, sizeof(real)), *o = malloc(sizeof(real) * V);
+      const unsigned char *sblk = ssm_block(pool, layer, slot);
+      const uint16_t *cblk = conv_block(pool, layer, slot);
+      for (size_t i = 0; i < (size_t)V * K; ++i) S[i] = load_ssm(pool, sblk, (size_t)h * V * K + i);
+      for (int i = 0; i < nchan; ++i)
+        for (int j = 0; j < CONV_ROWS; ++j) R[i][j] = widen(cblk[(size_t)j * u.C + chan[i]]);
+      int crossings = 0;
+      for (int t = 0; t < n; ++t) {
+        const size_t row = ring_row(pool, ring, layer, slot, h, t);
+        for (int c = 0; c < K; ++c) k[c] = widen(ring->rawk[row * K + c]);
+        for (int c = 0; c < V; ++c) v[c] = widen(ring->rawv[row * V + c]);
+        if (flags & ORACLE_L2NORM_K) {
+          real ss = 0;
+          for (int c = 0; c < K; ++c) ss += k[c] * k[c];
+          real inv = 1 / sqrt(ss + (real)L2_EPS);
+          for (int c = 0; c < K; ++c) k[c] = k[c] * inv;
+        }
+        for (int c = 0; c < K; ++c) a[c] = (real)ring->g[row * aw + (aw == 1 ? 0 : c)];
+        token_step(K, V, S, q, k, v, a, (real)ring->beta[row], 0, o);   /* output unused */
+        const uint16_t *xr = ring->xrow + (((size_t)layer * pool->slots + slot) * ring->positions + t) * u.C;
+        for (int i = 0; i < nchan; ++i) {
+          R[i][0] = R[i][1];
+          R[i][1] = R[i][2];
+          R[i][2] = widen(xr[chan[i]]);
+        }
+        if (track_interval > 0 && track_slots &&
+            ((int64_t)seq_len_before[b] + t + 1) % track_interval == 0) {
+          const int dst = track_slots[2 * b + (((next_track_idx ? next_track_idx[b] : 0) + crossings) & 1)];
+          ++crossings;
+          if (dst >= pool->slots) err |= 2;
+          else if (dst > 0) store_head(&u, dst, h, S, R, chan, nchan);
+        }
+      }
+      store_head(&u, slot, h, S, R, chan, nchan);
+      free(chan); free(S); free(R); free(k); free(v); free(a); free(q); free(o);
+    }
   }
   return err;
 }

@@ -26,7 +26,10 @@
  *     section 3.2) and of restore_linear_state_slots (page "Qwen3.5
  *     Linear-State Prefix Cache", sections 6.1 and 6.4);
  *   - the speculative verify over a draft tree and the accepted-step scatter
- *     (page "SGLang之MambaRadixCache机制", sections 8.3, 8.4, 8.6 and 9.6).
+ *     (page "SGLang之MambaRadixCache机制", sections 8.3, 8.4, 8.6 and 9.6);
+ *   - the ReplaySSM ring verify and exact-fold commit (page "企业官网建设流程全解析",
+ *     Kimi K3 notes, section "ReplaySSM"; page "SGLang之MambaRadixCache机制",
+ *     sections 9.2 and 9.10).
  *
  * Pool byte layout (identical to the product's so that pool images can be
  * compared byte for byte):
@@ -58,6 +61,20 @@ typedef struct {
   void *ssm;           /* host bytes, layout above */
   uint16_t *conv;      /* host bf16, layout above */
 } oracle_pool;
+
+/* ReplaySSM ring: per (layer, slot, head, position) the inputs that regenerate
+ * a draft step's state.  rawk/rawv bf16 [L][N][H][P][K|V]; g fp32 [L][N][H][P]
+ * (per-head decay) or [L][N][H][P][K] (per channel); beta fp32 [L][N][H][P];
+ * xrow bf16 [L][N][P][C] (the conv input row of the position). */
+typedef struct {
+  int32_t positions;   /* P */
+  int32_t alpha_mode;  /* ORACLE_ALPHA_PER_HEAD | ORACLE_ALPHA_PER_CHANNEL */
+  uint16_t *rawk;
+  uint16_t *rawv;
+  float *g;
+  float *beta;
+  uint16_t *xrow;
+} oracle_ring;
 
 typedef struct {
   int32_t linear_state_id;
@@ -135,6 +152,28 @@ int oracle_accept_scatter(const oracle_pool *pool, int32_t layer, int32_t batch,
                           const int32_t *seq_len_before, int32_t track_interval,
                           const int32_t *track_slots, const int32_t *next_track_idx,
                           const void *node_ssm, const uint16_t *node_conv);
+
+/* Byte sizes of the ring arrays {rawk, rawv, g, beta, xrow} for the pool's shape. */
+int oracle_ring_bytes(const oracle_pool *pool, int32_t positions, int32_t alpha_mode,
+                      size_t bytes[5]);
+
+/* Verify a chain of `draft` tokens per request from its live slot (only read),
+ * out [B][D][H][V]; ring positions 0 .. draft-1 of the slot receive the inputs
+ * the commit replays.  x [B][D][C], alpha [B][D][H] or [B][D][H][K], beta
+ * [B][D][H].  out_exact may be NULL. */
+int oracle_replay_verify(const oracle_pool *pool, const oracle_ring *ring, int32_t layer,
+                         int32_t batch, int32_t draft, const int32_t *slot_table,
+                         const uint16_t *x, const uint16_t *conv_w, const float *alpha,
+                         int32_t alpha_mode, const float *beta, float scale, uint32_t flags,
+                         uint16_t *out, double *out_exact);
+
+/* Fold ring positions 0 .. accepted[b]-1 into each live slot (state and conv
+ * rows), snapshotting at multiples of track_interval. */
+int oracle_replay_commit(const oracle_pool *pool, const oracle_ring *ring, int32_t layer,
+                         int32_t batch, const int32_t *slot_table, const int32_t *accepted,
+                         int32_t alpha_mode, uint32_t flags, const int32_t *seq_len_before,
+                         int32_t track_interval, const int32_t *track_slots,
+                         const int32_t *next_track_idx);
 
 /* The bare recurrence for one head over T prepared tokens (no conv, no norm):
  * q, k, v [T][K|V] as given, alpha [T][K], beta [T]; S [V][K] in/out;

@@ -813,3 +813,175 @@ def test_accept_scatter_rejects_bad_input():
     assert np.array_equal(run.ssm()[0, 2], ns[1, 2])
     assert oracle.accept_scatter(run, 0, [1, 2], parent, [2, -1], ns, nc, seq_len_before=[254],
                                  track_interval=256, track_slots=[[99, 99], [0, 0]]) == 2
+
+
+# ------------------------------------------------------ ReplaySSM ring ----
+
+def test_replay_ring_sizes_from_the_page(golden_dir):
+    """The ring arrays the commit replays from (rawk, rawv, g, beta) have the
+    sizes the pages print; with the pages' two further rings (d, k) the total
+    and the per-slot figure match too."""
+    spec = json.load(open(os.path.join(golden_dir, "replay_ring.json")))
+    pool = oracle.Pool(spec["layers"], spec["slots"], spec["heads"], spec["head_k"], spec["head_v"],
+                       oracle.SSM_BF16)
+    rk, rv, g, beta, xrow = oracle.ring_bytes(pool, spec["positions"], oracle.ALPHA_PER_CHANNEL)
+    assert (rk, rv, g, beta) == (spec["rawk_bytes"], spec["rawv_bytes"], spec["g_per_channel_bytes"],
+                                 spec["beta_bytes"])
+    _, _, g_head, _, _ = oracle.ring_bytes(pool, spec["positions"], oracle.ALPHA_PER_HEAD)
+    assert g_head * 128 == g
+    total = rk + rv + g + beta + spec["d_bytes"] + spec["k_bytes"]
+    # the printed GiB total (1.539063) is one unit of its last decimal above the
+    # exact 1.5390623 of its own byte figures; the per-slot byte count is exact
+    assert abs(total / 2 ** 30 - spec["total_gib_6dp"]) <= 1e-6
+    assert total == spec["per_slot_bytes"] * spec["slots"]
+    # the conv input rows the commit needs in addition: one row of C per position
+    assert xrow == spec["layers"] * spec["slots"] * spec["positions"] * pool.channels * 2
+
+
+def _replay_setup(seed, B, D, ssm_dtype=oracle.SSM_F32, identity=True, H=2, K=8, V=8, slots=12,
+                  positions=8, amode=oracle.ALPHA_PER_CHANNEL):
+    pool, w, x, a, b = _spec_setup(seed, B, D, ssm_dtype, H, K, V, slots)
+    if identity:
+        w = identity_taps(H * (2 * K + V))
+    if amode == oracle.ALPHA_PER_HEAD:
+        a = np.ascontiguousarray(a[..., 0])
+    ring = oracle.Ring(pool, positions, amode)
+    return pool, w, x, a, b, ring
+
+
+@pytest.mark.parametrize("identity", [True, False])
+def test_replay_verify_equals_chain_of_decodes(identity):
+    """Verify with the ring gives the outputs of consecutive decode steps (bit-exact,
+    fp32 build), leaves the live slots as they are, and records the conv outputs
+    k and v (bf16), the decay, beta and the conv input rows."""
+    B, D = 2, 5
+    pool, w, x, a, b, ring = _replay_setup(101, B, D, identity=identity)
+    before = pool.copy()
+    out, err = oracle.replay_verify(pool, ring, 0, [3, 7], x, w, a, oracle.ALPHA_PER_CHANNEL, b,
+                                    precision="f32")
+    assert err == 0
+    assert np.array_equal(pool.ssm_bytes, before.ssm_bytes)
+    assert np.array_equal(pool.conv_bytes, before.conv_bytes)
+    for i, s in enumerate((3, 7)):
+        _, outs = _decode_path(before, s, list(range(D)), x[i], w, a[i], b[i], "f32")
+        assert np.array_equal(out[i], np.stack(outs))
+        assert np.array_equal(ring.g[0, s, :, :D], a[i].transpose(1, 0, 2))
+        assert np.array_equal(ring.beta[0, s, :, :D], b[i].T)
+        assert np.array_equal(ring.xrow[0, s, :D], x[i])
+        if identity:   # taps (0, 0, 0, 1): the conv outputs are the inputs, exactly
+            H, K, V = pool.heads, pool.head_k, pool.head_v
+            xk = x[i][:, H * K:2 * H * K].reshape(D, H, K).transpose(1, 0, 2)
+            xv = x[i][:, 2 * H * K:].reshape(D, H, V).transpose(1, 0, 2)
+            assert np.array_equal(ring.rawk[0, s, :, :D], xk)
+            assert np.array_equal(ring.rawv[0, s, :, :D], xv)
+    assert not ring.rawk[0, 5].any()   # other slots' rings untouched
+
+
+@pytest.mark.parametrize("ssm_dtype", [oracle.SSM_F32, oracle.SSM_BF16])
+@pytest.mark.parametrize("n", [0, 1, 3, 5])
+def test_replay_commit_equals_decoding_the_accepted_prefix(ssm_dtype, n):
+    """With identity taps (so the ring's bf16 k and v are exact), committing n
+    accepted tokens leaves the slot exactly as n decode steps would (fp32
+    build; the state is rounded to the pool dtype once, at the end)."""
+    B, D = 2, 5
+    pool, w, x, a, b, ring = _replay_setup(102, B, D, ssm_dtype)
+    oracle.replay_verify(pool, ring, 0, [3, 7], x, w, a, oracle.ALPHA_PER_CHANNEL, b,
+                         precision="f32")
+    run = pool.copy()
+    assert oracle.replay_commit(run, ring, 0, [3, 7], [n, 2], oracle.ALPHA_PER_CHANNEL,
+                                precision="f32") == 0
+    want = pool.copy()
+    # decode steps store the state every step; with an fp32 pool that is exact,
+    # with a bf16 pool the fold (one rounding) is compared with tolerance
+    for i, (s, m) in enumerate(((3, n), (7, 2))):
+        if m:
+            p, _ = _decode_path(pool, s, list(range(m)), x[i], w, a[i], b[i], "f32")
+            want.ssm()[0, s] = p.ssm()[0, s]
+            want.conv()[0, s] = p.conv()[0, s]
+    assert np.array_equal(run.conv_bytes, want.conv_bytes)
+    if ssm_dtype == oracle.SSM_F32:
+        assert np.array_equal(run.ssm_bytes, want.ssm_bytes)
+    else:
+        got, exp = oracle.bf16_widen(run.ssm()), oracle.bf16_widen(want.ssm())
+        assert np.linalg.norm(got - exp) <= 1e-2 * np.linalg.norm(exp)
+        untouched = [s for s in range(pool.slots) if s not in (3, 7)]
+        assert np.array_equal(run.ssm()[0, untouched], pool.ssm()[0, untouched])
+
+
+def test_replay_commit_with_conv_taps_folds_the_ring_values():
+    """With real conv taps the ring holds k and v rounded to bf16 (the pages' ring
+    dtype).  The fold is the bare recurrence on exactly those values (k
+    normalised, decay g, beta), and it lies within bf16-level distance of
+    decoding the same tokens."""
+    H, K, V = 2, 16, 16
+    pool, w, x, a, b, ring = _replay_setup(103, 1, 6, identity=False, K=K, V=V)
+    oracle.replay_verify(pool, ring, 0, [4], x, w, a, oracle.ALPHA_PER_CHANNEL, b)
+    run = pool.copy()
+    oracle.replay_commit(run, ring, 0, [4], [6], oracle.ALPHA_PER_CHANNEL)
+    for h in range(H):
+        k = oracle.bf16_widen(ring.rawk[0, 4, h, :6])
+        k = k / np.sqrt((k * k).sum(axis=1, keepdims=True) + 1e-6)
+        v = oracle.bf16_widen(ring.rawv[0, 4, h, :6])
+        _, S = oracle.recurrence_head(np.zeros((6, K)), k, v, ring.g[0, 4, h, :6].astype(np.float64),
+                                      ring.beta[0, 4, h, :6].astype(np.float64),
+                                      pool.ssm()[0, 4, h].astype(np.float64))
+        got = run.ssm()[0, 4, h].astype(np.float64)
+        assert np.linalg.norm(got - S) <= 1e-6 * np.linalg.norm(S)   # fp32 pool rounding
+    p, _ = _decode_path(pool, 4, list(range(6)), x[0], w, a[0], b[0], "f64")
+    got, want = run.ssm()[0, 4].astype(np.float64), p.ssm()[0, 4].astype(np.float64)
+    d = np.linalg.norm(got - want) / np.linalg.norm(want)
+    assert 0 < d < 1e-2
+    assert np.array_equal(run.conv()[0, 4], p.conv()[0, 4])
+
+
+@pytest.mark.parametrize("before,interval,hits", [(254, 256, [2]), (255, 256, [1]), (250, 256, []),
+                                                   (3, 2, [1, 3])])
+def test_replay_commit_tracks_crossings(before, interval, hits):
+    """The state after the token that completes a multiple of the interval goes
+    to the track slot, the j-th crossing to (next + j) & 1 (decode-with-tracking
+    and prefill rules; identity taps, bit-exact)."""
+    pool, w, x, a, b, ring = _replay_setup(104, 1, 4, identity=True)
+    oracle.replay_verify(pool, ring, 0, [1], x, w, a, oracle.ALPHA_PER_CHANNEL, b, precision="f32")
+    run = pool.copy()
+    track = np.array([[9, 10]], dtype=np.int32)
+    assert oracle.replay_commit(run, ring, 0, [1], [4], oracle.ALPHA_PER_CHANNEL,
+                                seq_len_before=[before], track_interval=interval, track_slots=track,
+                                next_track_idx=[1], precision="f32") == 0
+    for j, i in enumerate(hits):
+        p, _ = _decode_path(pool, 1, list(range(i)), x[0], w, a[0], b[0], "f32")
+        dst = int(track[0, (1 + j) & 1])
+        assert np.array_equal(run.ssm()[0, dst], p.ssm()[0, 1])
+        assert np.array_equal(run.conv()[0, dst], p.conv()[0, 1])
+    if not hits:
+        assert np.array_equal(run.ssm()[0, 9:11], pool.ssm()[0, 9:11])
+
+
+def test_replay_gdn_scalar_decay_and_errors():
+    """Per-head decay rings hold one g per position; accepted beyond the ring
+    flags bit 8 and writes nothing; bad live and track slots flag bits 1 and 2."""
+    pool, w, x, a, b, ring = _replay_setup(105, 2, 3, amode=oracle.ALPHA_PER_HEAD, positions=4)
+    out, err = oracle.replay_verify(pool, ring, 0, [2, 5], x, w, a, oracle.ALPHA_PER_HEAD, b,
+                                    precision="f32")
+    assert err == 0 and ring.g.shape == (1, pool.slots, pool.heads, 4)
+    _, outs = _decode_path_head(pool, 2, 3, x[0], w, a[0], b[0])
+    assert np.array_equal(out[0], np.stack(outs))
+    run = pool.copy()
+    assert oracle.replay_commit(run, ring, 0, [2, 5], [5, 1], oracle.ALPHA_PER_HEAD) == 8
+    assert np.array_equal(run.ssm()[0, 2], pool.ssm()[0, 2])
+    assert not np.array_equal(run.ssm()[0, 5], pool.ssm()[0, 5])
+    assert oracle.replay_commit(pool.copy(), ring, 0, [99, 5], [1, 1], oracle.ALPHA_PER_HEAD) == 1
+    assert oracle.replay_commit(pool.copy(), ring, 0, [2, 5], [2, 0], oracle.ALPHA_PER_HEAD,
+                                seq_len_before=[0, 0], track_interval=1,
+                                track_slots=[[99, 0], [0, 0]]) == 2
+
+
+def _decode_path_head(pool, slot, n, x, w, a, b):
+    """n decode steps with per-head decay (a [D][H])."""
+    p = pool.copy()
+    outs = []
+    for t in range(n):
+        o, err = oracle.decode_step(p, 0, [slot], x[None, t], w, a[None, t], oracle.ALPHA_PER_HEAD,
+                                    b[None, t], precision="f32")
+        assert err == 0
+        outs.append(o[0])
+    return p, outs
