@@ -20,6 +20,7 @@ ALPHA_PER_HEAD, ALPHA_PER_CHANNEL = 0, 1
 L2NORM_K, L2NORM_Q, CONV_SILU = 1, 2, 4
 ERRW_BAD_SLOT, ERRW_BAD_TRACK_SLOT, ERRW_BAD_SEQLENS, ERRW_BAD_TREE = 1, 2, 4, 8
 MAX_TREE_NODES = 1024
+MAX_RING_POSITIONS = 64
 
 
 class GdnError(RuntimeError):
@@ -35,6 +36,12 @@ class PoolDesc(ct.Structure):
         ("ssm_dtype", ct.c_int32), ("conv_dtype", ct.c_int32),
         ("ssm_base", ct.c_void_p), ("conv_base", ct.c_void_p), ("err_word", ct.c_void_p),
     ]
+
+
+class RingDesc(ct.Structure):
+    _fields_ = [("positions", ct.c_int32), ("alpha_mode", ct.c_int32), ("rawk", ct.c_void_p),
+                ("rawv", ct.c_void_p), ("g", ct.c_void_p), ("beta", ct.c_void_p),
+                ("xrow", ct.c_void_p)]
 
 
 class RestoreOp(ct.Structure):
@@ -64,9 +71,15 @@ _lib.gdn_verify_tree.argtypes = [
     _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _u32, _vp, _vp, _vp, _vp]
 _lib.gdn_accept_scatter.argtypes = [
     _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+_lib.replayssm_ring_bytes.argtypes = [_vp, _i32, _i32, ct.POINTER(_sz)]
+_lib.replayssm_verify.argtypes = [
+    _vp, ct.POINTER(RingDesc), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _f32, _u32, _vp, _vp]
+_lib.replayssm_commit.argtypes = [
+    _vp, ct.POINTER(RingDesc), _i32, _i32, _vp, _vp, _u32, _vp, _i32, _vp, _vp, _vp]
 for _f in ("state_pool_bytes", "state_pool_create", "conv_gdn_prefill_chunked",
            "gdn_prefill_workspace_bytes", "gdn_decode_step", "track_snapshot", "restore_slots",
-           "gdn_verify_tree", "gdn_accept_scatter"):
+           "gdn_verify_tree", "gdn_accept_scatter", "replayssm_ring_bytes", "replayssm_verify",
+           "replayssm_commit"):
     getattr(_lib, _f).restype = ct.c_int
 
 
@@ -277,3 +290,66 @@ def gdn_accept_scatter(pool: StatePool, layer, slot_table, parent, accepted, nod
         pool.handle, layer, B, T, _ptr(slot_table), _ptr(parent), _ptr(accepted),
         _ptr(seq_len_before), track_interval, _ptr(track_slots), _ptr(next_track_idx),
         _ptr(node_ssm), _ptr(node_conv), _stream(stream)))
+
+
+def replayssm_ring_bytes(pool: StatePool, positions, alpha_mode):
+    """Byte sizes (rawk, rawv, g, beta, xrow) of a ReplaySSM ring for the pool."""
+    b = (_sz * 5)()
+    _check(_lib.replayssm_ring_bytes(pool.handle, positions, alpha_mode, b))
+    return tuple(b[i] for i in range(5))
+
+
+class ReplayRing:
+    """Caller-owned ReplaySSM ring tensors (see gdn_replay_ring in the header)."""
+
+    def __init__(self, pool: StatePool, positions, alpha_mode, device=None):
+        L, N, H, K, V = pool.layers, pool.slots, pool.heads, pool.head_k, pool.head_v
+        dev = device if device is not None else pool.ssm.device
+        self.positions, self.alpha_mode = positions, alpha_mode
+        self.rawk = torch.zeros(L, N, H, positions, K, dtype=torch.bfloat16, device=dev)
+        self.rawv = torch.zeros(L, N, H, positions, V, dtype=torch.bfloat16, device=dev)
+        gshape = (L, N, H, positions, K) if alpha_mode == ALPHA_PER_CHANNEL else (L, N, H, positions)
+        self.g = torch.zeros(gshape, dtype=torch.float32, device=dev)
+        self.beta = torch.zeros(L, N, H, positions, dtype=torch.float32, device=dev)
+        self.xrow = torch.zeros(L, N, positions, pool.channels, dtype=torch.bfloat16, device=dev)
+
+    def desc(self):
+        return RingDesc(self.positions, self.alpha_mode, _ptr(self.rawk), _ptr(self.rawv),
+                        _ptr(self.g), _ptr(self.beta), _ptr(self.xrow))
+
+
+def replayssm_verify(pool: StatePool, ring: ReplayRing, layer, slot_table, x, conv_w, alpha, beta,
+                     out, scale=1.0, flags=L2NORM_K, stream=None):
+    """``x`` bf16 [B, D, C]; ``alpha`` fp32 [B, D, H(, K)]; ``beta`` fp32 [B, D, H];
+    ``out`` bf16 [B, D, H, V].  The live slots are only read."""
+    B = slot_table.numel()
+    if x.dim() != 3 or x.shape[0] != B:
+        raise ValueError("x must be [batch, draft, C]")
+    D = x.shape[1]
+    H, V, K = pool.heads, pool.head_v, pool.head_k
+    _need(slot_table, torch.int32, B, "slot_table")
+    _need(x, torch.bfloat16, B * D * pool.channels, "x")
+    _need(conv_w, torch.bfloat16, pool.channels * 4, "conv_w")
+    _need(alpha, torch.float32, B * D * H * (K if ring.alpha_mode == ALPHA_PER_CHANNEL else 1), "alpha")
+    _need(beta, torch.float32, B * D * H, "beta")
+    _need(out, torch.bfloat16, B * D * H * V, "out")
+    d = ring.desc()
+    _check(_lib.replayssm_verify(pool.handle, ct.byref(d), layer, B, D, _ptr(slot_table), _ptr(x),
+                                 _ptr(conv_w), _ptr(alpha), _ptr(beta), float(scale), flags,
+                                 _ptr(out), _stream(stream)))
+
+
+def replayssm_commit(pool: StatePool, ring: ReplayRing, layer, slot_table, accepted, flags=L2NORM_K,
+                     seq_len_before=None, track_interval=0, track_slots=None, next_track_idx=None,
+                     stream=None):
+    """Fold ring positions 0..accepted[b]-1 into each live slot."""
+    B = slot_table.numel()
+    _need(slot_table, torch.int32, B, "slot_table")
+    _need(accepted, torch.int32, B, "accepted")
+    _need(seq_len_before, torch.int32, B, "seq_len_before")
+    _need(track_slots, torch.int32, 2 * B, "track_slots")
+    _need(next_track_idx, torch.int32, B, "next_track_idx")
+    d = ring.desc()
+    _check(_lib.replayssm_commit(pool.handle, ct.byref(d), layer, B, _ptr(slot_table), _ptr(accepted),
+                                 flags, _ptr(seq_len_before), track_interval, _ptr(track_slots),
+                                 _ptr(next_track_idx), _stream(stream)))

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdnslot.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.hip", "slot_copy.hip", "decode.hip", "prefill.hip", "verify.hip"]
+SOURCES = ["api.hip", "slot_copy.hip", "decode.hip", "prefill.hip", "verify.hip", "replay.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -301,3 +301,102 @@ GDN_API gdn_status gdn_accept_scatter(gdn_pool_t pool, int32_t layer, int32_t ba
   return launched(gdn::launch_accept_scatter(pool, a, static_cast<hipStream_t>(stream)),
                   "gdn_accept_scatter launch");
 }
+
+namespace {
+gdn_status check_ring(gdn_pool_t pool, const gdn_replay_ring *r) {
+  if (!r) return fail(GDN_ERR_ARG, "ring is NULL");
+  if (r->positions < 1 || r->positions > GDN_MAX_RING_POSITIONS)
+    return fail(GDN_ERR_RANGE, "ring positions %d outside [1, %d]", r->positions, GDN_MAX_RING_POSITIONS);
+  if (r->alpha_mode != GDN_ALPHA_PER_HEAD && r->alpha_mode != GDN_ALPHA_PER_CHANNEL)
+    return fail(GDN_ERR_ARG, "ring alpha_mode %d unknown", r->alpha_mode);
+  if (!r->rawk || !r->rawv || !r->g || !r->beta || !r->xrow)
+    return fail(GDN_ERR_ARG, "a ring array is NULL");
+  if (!aligned(r->rawk, 16) || !aligned(r->rawv, 16) || !aligned(r->xrow, 16) || !aligned(r->g, 4) ||
+      !aligned(r->beta, 4))
+    return fail(GDN_ERR_UNSUPPORTED, "rawk, rawv, xrow must be 16-byte aligned, g and beta 4-byte");
+  return GDN_OK;
+}
+}  // namespace
+
+GDN_API gdn_status replayssm_ring_bytes(gdn_pool_t pool, int32_t positions, int32_t alpha_mode,
+                                        size_t bytes[5]) {
+  if (!pool || !bytes) return fail(GDN_ERR_ARG, "pool or bytes is NULL");
+  if (positions < 1 || positions > GDN_MAX_RING_POSITIONS)
+    return fail(GDN_ERR_RANGE, "positions %d outside [1, %d]", positions, GDN_MAX_RING_POSITIONS);
+  if (alpha_mode != GDN_ALPHA_PER_HEAD && alpha_mode != GDN_ALPHA_PER_CHANNEL)
+    return fail(GDN_ERR_ARG, "alpha_mode %d unknown", alpha_mode);
+  const size_t rows = size_t(pool->d.layers) * pool->d.slots * pool->d.heads * positions;
+  bytes[0] = rows * pool->d.head_k * 2;
+  bytes[1] = rows * pool->d.head_v * 2;
+  bytes[2] = rows * (alpha_mode == GDN_ALPHA_PER_CHANNEL ? pool->d.head_k : 1) * 4;
+  bytes[3] = rows * 4;
+  bytes[4] = size_t(pool->d.layers) * pool->d.slots * positions * size_t(pool->C) * 2;
+  return ok();
+}
+
+GDN_API gdn_status replayssm_verify(gdn_pool_t pool, const gdn_replay_ring *ring, int32_t layer,
+                                    int32_t batch, int32_t draft, const int32_t *slot_table,
+                                    const uint16_t *x, const uint16_t *conv_w, const float *alpha,
+                                    const float *beta, float scale, uint32_t flags, uint16_t *out,
+                                    void *stream) {
+  gdn_status s = check_pool(pool, layer);
+  if (s != GDN_OK) return s;
+  if ((s = check_ring(pool, ring)) != GDN_OK) return s;
+  if (batch < 0 || batch > 65535) return fail(GDN_ERR_RANGE, "batch %d outside [0, 65535]", batch);
+  if (draft < 1 || draft > ring->positions)
+    return fail(GDN_ERR_RANGE, "draft %d outside [1, %d]", draft, ring->positions);
+  if (batch == 0) return ok();
+  if (!slot_table || !x || !conv_w || !alpha || !beta || !out)
+    return fail(GDN_ERR_ARG, "a required pointer is NULL");
+  if (flags & ~uint32_t(GDN_F_L2NORM_K | GDN_F_L2NORM_Q | GDN_F_CONV_SILU))
+    return fail(GDN_ERR_ARG, "unknown flag bits 0x%x", flags);
+  if (!aligned(conv_w, 16) || !aligned(x, 16) || !aligned(alpha, 16))
+    return fail(GDN_ERR_UNSUPPORTED, "x, conv_w and alpha must be 16-byte aligned");
+  gdn::ReplayArgs a{};
+  a.ring = *ring;
+  a.layer = layer;
+  a.batch = batch;
+  a.draft = draft;
+  a.slot_table = slot_table;
+  a.x = x;
+  a.conv_w = conv_w;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.scale = scale;
+  a.flags = flags;
+  a.out = out;
+  return launched(gdn::launch_replay_verify(pool, a, static_cast<hipStream_t>(stream)),
+                  "replayssm_verify launch");
+}
+
+GDN_API gdn_status replayssm_commit(gdn_pool_t pool, const gdn_replay_ring *ring, int32_t layer,
+                                    int32_t batch, const int32_t *slot_table,
+                                    const int32_t *accepted, uint32_t flags,
+                                    const int32_t *seq_len_before, int32_t track_interval,
+                                    const int32_t *track_slots, const int32_t *next_track_idx,
+                                    void *stream) {
+  gdn_status s = check_pool(pool, layer);
+  if (s != GDN_OK) return s;
+  if ((s = check_ring(pool, ring)) != GDN_OK) return s;
+  if (batch < 0 || batch > 65535) return fail(GDN_ERR_RANGE, "batch %d outside [0, 65535]", batch);
+  if (track_interval < 0) return fail(GDN_ERR_ARG, "track_interval < 0");
+  if (batch == 0) return ok();
+  if (!slot_table || !accepted) return fail(GDN_ERR_ARG, "slot_table or accepted is NULL");
+  if (flags & ~uint32_t(GDN_F_L2NORM_K | GDN_F_L2NORM_Q | GDN_F_CONV_SILU))
+    return fail(GDN_ERR_ARG, "unknown flag bits 0x%x", flags);
+  if (track_interval > 0 && (!seq_len_before || !track_slots || !next_track_idx))
+    return fail(GDN_ERR_ARG, "tracking needs seq_len_before, track_slots and next_track_idx");
+  gdn::ReplayArgs a{};
+  a.ring = *ring;
+  a.layer = layer;
+  a.batch = batch;
+  a.slot_table = slot_table;
+  a.flags = flags;
+  a.accepted = accepted;
+  a.seq_len_before = seq_len_before;
+  a.track_interval = track_interval;
+  a.track_slots = track_slots;
+  a.next_track_idx = next_track_idx;
+  return launched(gdn::launch_replay_commit(pool, a, static_cast<hipStream_t>(stream)),
+                  "replayssm_commit launch");
+}

@@ -120,6 +120,28 @@ struct ScatterArgs {
   const uint16_t *node_conv;
 };
 hipError_t launch_accept_scatter(const gdn_pool *p, const ScatterArgs &a, hipStream_t s);
+
+struct ReplayArgs {
+  gdn_replay_ring ring;
+  int layer, batch, draft;
+  const int32_t *slot_table;
+  // verify
+  const uint16_t *x;
+  const uint16_t *conv_w;
+  const float *alpha;
+  const float *beta;
+  float scale;
+  uint32_t flags;
+  uint16_t *out;
+  // commit
+  const int32_t *accepted;
+  const int32_t *seq_len_before;
+  int track_interval;
+  const int32_t *track_slots;
+  const int32_t *next_track_idx;
+};
+hipError_t launch_replay_verify(const gdn_pool *p, const ReplayArgs &a, hipStream_t s);
+hipError_t launch_replay_commit(const gdn_pool *p, const ReplayArgs &a, hipStream_t s);
 // Workspace of the two-phase prefill: one record per (request, chunk, head) of
 // the chunks processed in one window, plus an fp32 state carry per (request, head).
 size_t prefill_record_bytes(const gdn_pool *p);

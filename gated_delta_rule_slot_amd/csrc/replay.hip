@@ -1,0 +1,429 @@
+// replay.hip -- ReplaySSM: a draft-chain verify that records a ring of inputs
+// instead of per-step states, and the exact-fold commit of the accepted prefix.
+//
+// Semantics (page "企业官网建设流程全解析", Kimi K3 notes, section "ReplaySSM"):
+// the verify computes every draft position's output but keeps no per-position
+// [V, K] state; it records what regenerates it (k as it leaves the conv, before
+// L2 normalisation, and v, both bf16; the decay g and beta in fp32).  After
+// acceptance only the accepted prefix is replayed, in recurrent order, and
+// written back to the slot (page "SGLang之MambaRadixCache机制解析", section 9.10:
+// with the track-interval check during the replay).  The ring also keeps each
+// position's conv input row, so the commit can advance the conv state.
+//
+// Both kernels use the decode kernel's lane layout (one workgroup per (request,
+// head), a lane owns 16-byte pieces of K-contiguous state rows, row sums with
+// DPP and row swaps) and keep the state in fp32 registers across the tokens:
+// the verify reads the live state once and stores no state at all; the commit
+// reads it once, folds every accepted token, and stores it once (and at a
+// snapshot).
+#include "common.hpp"
+#include "lanes.hpp"
+
+namespace gdn {
+namespace {
+
+template <int D, typename TS>
+struct ReplayShape {
+  static constexpr int VEC = StateVec<TS>::N;
+  static constexpr int LPR = D / VEC;                        // lanes per row
+  static constexpr int RPI = 64 / LPR;                       // rows per load instruction
+  static constexpr int ROWS = RPI * 8 < D ? RPI * 8 : D;     // state rows per wave
+  static constexpr int THREADS = 64 * (D / ROWS);
+  static constexpr int ITERS = (ROWS + RPI - 1) / RPI;
+  static constexpr bool FULL = ROWS % RPI == 0;              // every piece of every lane is a row
+  // conv items of CW channels, one per thread
+  static constexpr int CW = 3 * D / 2 <= THREADS ? 2 : 3 * D / 4 <= THREADS ? 4 : 8;
+  static_assert(D <= THREADS, "one staging thread per channel");
+};
+
+// CW bf16 values packed for one store
+template <int CW>
+struct PackCW;
+template <>
+struct PackCW<2> {
+  static __device__ __forceinline__ uint32_t pack(const float *v) { return pack_bf16x2(v[0], v[1]); }
+};
+template <>
+struct PackCW<4> {
+  static __device__ __forceinline__ u32x2 pack(const float *v) {
+    return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+};
+template <>
+struct PackCW<8> {
+  static __device__ __forceinline__ u32x4 pack(const float *v) {
+    return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                 pack_bf16x2(v[6], v[7])};
+  }
+};
+
+template <int D, typename TS, int kAlphaMode>
+__global__ __launch_bounds__((ReplayShape<D, TS>::THREADS)) void replay_verify_kernel(
+    const TS *__restrict__ ssm, const uint16_t *__restrict__ conv, int32_t *err, int slots,
+    int heads, ReplayArgs a) {
+  using SV = StateVec<TS>;
+  using SH = ReplayShape<D, TS>;
+  constexpr int VEC = SV::N, LPR = SH::LPR, RPI = SH::RPI, ROWS = SH::ROWS, ITERS = SH::ITERS;
+  constexpr int CW = SH::CW, ITEMS = 3 * D / CW;
+  static_assert(ITEMS <= SH::THREADS, "one conv item per thread");
+  using CV = ConvVec<CW>;
+  typedef typename CV::raw CR;
+  constexpr int NAL = kAlphaMode == GDN_ALPHA_PER_CHANNEL ? VEC : 1;
+
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int T = a.draft, H = heads, P = a.ring.positions;
+  const int lane = threadIdx.x & 63, part = threadIdx.x >> 6;
+  const int64_t C = int64_t(H) * 3 * D;
+  const int slot = a.slot_table[b];
+  const int r0 = part * ROWS;
+  const int64_t tok0 = int64_t(b) * T;
+
+  if (slot <= 0 || slot >= slots) {
+    for (int t = 0; t < T; ++t)
+      if (lane < ROWS) a.out[((tok0 + t) * H + h) * D + r0 + lane] = 0;
+    if (slot >= slots && err && h == 0 && threadIdx.x == 0) atomicOr(err, GDN_ERRW_BAD_SLOT);
+    return;
+  }
+
+  // ---- the live state, once, into fp32 registers --------------------------
+  const TS *S0 = ssm + ((int64_t(a.layer) * slots + slot) * H + h) * int64_t(D) * D;
+  const int row_in_group = lane / LPR;
+  const int col0 = (lane % LPR) * VEC;
+  float s[ITERS][VEC];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int r = r0 + it * RPI + row_in_group;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s[it][e] = 0.f;
+    if (SH::FULL || r < r0 + ROWS)
+      SV::to_f32(__builtin_nontemporal_load(reinterpret_cast<const typename SV::raw *>(S0 + int64_t(r) * D + col0)),
+                 s[it]);
+  }
+
+  // ---- conv items and the ring rows of (layer, slot, head) ------------------
+  const bool conv_lane = int(threadIdx.x) < ITEMS;
+  const int item = conv_lane ? int(threadIdx.x) : 0;
+  const int pt = item / (D / CW), jc = (item % (D / CW)) * CW;
+  const int64_t ch = int64_t(pt) * H * D + int64_t(h) * D + jc;
+  const uint16_t *crow = conv + (int64_t(a.layer) * slots + slot) * kConvRows * C;
+  CR w0 = *reinterpret_cast<const CR *>(crow + ch);
+  CR w1 = *reinterpret_cast<const CR *>(crow + C + ch);
+  CR w2 = *reinterpret_cast<const CR *>(crow + 2 * C + ch);
+  u32x4 wv[CW / 2];
+  {
+    const u32x4 *wp = reinterpret_cast<const u32x4 *>(a.conv_w + ch * 4);
+#pragma unroll
+    for (int i = 0; i < CW / 2; ++i) wv[i] = wp[i];
+  }
+  const int64_t rrow = ((int64_t(a.layer) * slots + slot) * H + h) * P;  // ring row of position 0
+  uint16_t *rk = a.ring.rawk + rrow * D;
+  uint16_t *rv = a.ring.rawv + rrow * D;
+  float *rg = a.ring.g + rrow * (kAlphaMode == GDN_ALPHA_PER_CHANNEL ? D : 1);
+  float *rb = a.ring.beta + rrow;
+  uint16_t *rx = a.ring.xrow + (int64_t(a.layer) * slots + slot) * P * C;
+
+  __shared__ __attribute__((aligned(16))) float sy[2][3 * D];  // q | k | v, double buffered
+
+  auto load_x = [&](int t) { return *reinterpret_cast<const CR *>(a.x + (tok0 + t) * C + ch); };
+  CR xv = load_x(0);
+
+  for (int t = 0; t < T; ++t) {
+    const int64_t tok = tok0 + t;
+    float *y = sy[t & 1];
+    if (conv_lane) {
+      float yv[CW];
+#pragma unroll
+      for (int e = 0; e < CW; ++e) {
+        const int sh = (e & 1) ? 16 : 0;
+        auto pick = [&](const CR &v) {
+          return __uint_as_float(((CV::word(v, e >> 1) >> sh) & 0xffffu) << 16);
+        };
+        const u32x4 &w = wv[e >> 1];
+        const int wb = (e & 1) * 2;
+        float acc = __uint_as_float(w[wb] << 16) * pick(w0);
+        acc = fmaf(__uint_as_float(w[wb] & 0xffff0000u), pick(w1), acc);
+        acc = fmaf(__uint_as_float(w[wb + 1] << 16), pick(w2), acc);
+        acc = fmaf(__uint_as_float(w[wb + 1] & 0xffff0000u), pick(xv), acc);
+        if (a.flags & GDN_F_CONV_SILU) acc = acc / (1.f + __expf(-acc));
+        yv[e] = acc;
+        y[pt * D + jc + e] = acc;
+      }
+      // the ring: k and v as they leave the conv (bf16), and the conv input row
+      if (pt == 1) *reinterpret_cast<decltype(PackCW<CW>::pack(yv)) *>(rk + t * D + jc) = PackCW<CW>::pack(yv);
+      if (pt == 2) *reinterpret_cast<decltype(PackCW<CW>::pack(yv)) *>(rv + t * D + jc) = PackCW<CW>::pack(yv);
+      *reinterpret_cast<CR *>(rx + int64_t(t) * C + ch) = xv;
+    }
+    if (kAlphaMode == GDN_ALPHA_PER_CHANNEL) {
+      for (int i = threadIdx.x; i < D; i += SH::THREADS) rg[t * D + i] = a.alpha[(tok * H + h) * D + i];
+    } else if (threadIdx.x == 0) {
+      rg[t] = a.alpha[tok * H + h];
+    }
+    if (threadIdx.x == 0) rb[t] = a.beta[tok * H + h];
+    float al[NAL];
+    if (kAlphaMode == GDN_ALPHA_PER_CHANNEL) {
+      const float *ap = a.alpha + (tok * H + h) * D + col0;
+#pragma unroll
+      for (int e = 0; e < NAL; ++e) al[e] = ap[e];
+    } else {
+      al[0] = a.alpha[tok * H + h];
+    }
+    const float beta = a.beta[tok * H + h];
+    // the window of the next token, and its x, ahead of the barrier
+    w0 = w1;
+    w1 = w2;
+    w2 = xv;
+    xv = load_x(t + 1 < T ? t + 1 : t);
+    __syncthreads();  // y complete; the other buffer is free again for token t + 1
+
+    const float *sq = y, *sk = y + D, *sv = y + 2 * D;
+    float kinv = 1.f, qinv = 1.f;
+    if (a.flags & GDN_F_L2NORM_K) {
+      float ss = 0.f;
+      for (int j = lane; j < D; j += 64) ss = fmaf(sk[j], sk[j], ss);
+      kinv = 1.f / sqrtf(wave_sum(ss) + 1e-6f);
+    }
+    if (a.flags & GDN_F_L2NORM_Q) {
+      float ss = 0.f;
+      for (int j = lane; j < D; j += 64) ss = fmaf(sq[j], sq[j], ss);
+      qinv = 1.f / sqrtf(wave_sum(ss) + 1e-6f);
+    }
+    float kq = 0.f;
+    for (int j = lane; j < D; j += 64) kq = fmaf(sk[j] * kinv, sq[j] * qinv, kq);
+    kq = wave_sum(kq);
+    float kk[VEC], qq[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      kk[e] = sk[col0 + e] * kinv;
+      qq[e] = sq[col0 + e] * qinv;
+    }
+    uint16_t *out = a.out + (tok * H + h) * D;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int r = r0 + it * RPI + row_in_group;
+      float pu = 0.f, pq = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        s[it][e] *= al[NAL == 1 ? 0 : e];
+        pu = fmaf(s[it][e], kk[e], pu);
+        pq = fmaf(s[it][e], qq[e], pq);
+      }
+      pu = group_sum<LPR>(pu);
+      pq = group_sum<LPR>(pq);
+      if (SH::FULL || r < r0 + ROWS) {
+        const float d = beta * (sv[r] - pu);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[it][e] = fmaf(d, kk[e], s[it][e]);
+        if ((lane % LPR) == 0) out[r] = f32_to_bf16(a.scale * fmaf(d, kq, pq));
+      }
+    }
+  }
+}
+
+template <int D, typename TS, int kAlphaMode>
+__global__ __launch_bounds__((ReplayShape<D, TS>::THREADS)) void replay_commit_kernel(
+    TS *__restrict__ ssm, uint16_t *__restrict__ conv, int32_t *err, int slots, int heads,
+    ReplayArgs a) {
+  using SV = StateVec<TS>;
+  using SH = ReplayShape<D, TS>;
+  constexpr int VEC = SV::N, LPR = SH::LPR, RPI = SH::RPI, ROWS = SH::ROWS, ITERS = SH::ITERS;
+  constexpr int CW = SH::CW, ITEMS = 3 * D / CW;
+  using CV = ConvVec<CW>;
+  typedef typename CV::raw CR;
+  constexpr bool PERCH = kAlphaMode == GDN_ALPHA_PER_CHANNEL;
+
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int H = heads, P = a.ring.positions;
+  const int lane = threadIdx.x & 63, part = threadIdx.x >> 6;
+  const int64_t C = int64_t(H) * 3 * D;
+  const int n = a.accepted[b];
+  if (n < 0 || n > P) {
+    if (err && h == 0 && threadIdx.x == 0) atomicOr(err, GDN_ERRW_BAD_TREE);
+    return;
+  }
+  const int slot = a.slot_table[b];
+  if (slot <= 0 || slot >= slots) {
+    if (slot >= slots && err && h == 0 && threadIdx.x == 0) atomicOr(err, GDN_ERRW_BAD_SLOT);
+    return;
+  }
+  if (n == 0) return;
+
+  // ---- the live state, once, into fp32 registers --------------------------
+  const int64_t hd = int64_t(D) * D;
+  auto state_block = [&](int sl) { return ssm + ((int64_t(a.layer) * slots + sl) * H + h) * hd; };
+  const TS *S0 = state_block(slot);
+  const int r0 = part * ROWS;
+  const int row_in_group = lane / LPR;
+  const int col0 = (lane % LPR) * VEC;
+  float s[ITERS][VEC];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int r = r0 + it * RPI + row_in_group;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s[it][e] = 0.f;
+    if (SH::FULL || r < r0 + ROWS)
+      SV::to_f32(__builtin_nontemporal_load(reinterpret_cast<const typename SV::raw *>(S0 + int64_t(r) * D + col0)),
+                 s[it]);
+  }
+
+  // ---- conv rows of the head's channels -----------------------------------
+  const bool conv_lane = int(threadIdx.x) < ITEMS;
+  const int item = conv_lane ? int(threadIdx.x) : 0;
+  const int pt = item / (D / CW), jc = (item % (D / CW)) * CW;
+  const int64_t ch = int64_t(pt) * H * D + int64_t(h) * D + jc;
+  auto conv_rows = [&](int sl) { return conv + (int64_t(a.layer) * slots + sl) * kConvRows * C; };
+  const uint16_t *crow = conv_rows(slot);
+  CR c0 = *reinterpret_cast<const CR *>(crow + ch);
+  CR c1 = *reinterpret_cast<const CR *>(crow + C + ch);
+  CR c2 = *reinterpret_cast<const CR *>(crow + 2 * C + ch);
+
+  // ---- the ring of (layer, slot, head) --------------------------------------
+  const int64_t rrow = ((int64_t(a.layer) * slots + slot) * H + h) * P;
+  const uint16_t *rk = a.ring.rawk + rrow * D;
+  const uint16_t *rv = a.ring.rawv + rrow * D;
+  const float *rg = a.ring.g + rrow * (PERCH ? D : 1);
+  const float *rb = a.ring.beta + rrow;
+  const uint16_t *rx = a.ring.xrow + (int64_t(a.layer) * slots + slot) * P * C;
+  // staging: thread i < D holds channel i of a position's k, v (and g)
+  const int ci = int(threadIdx.x) < D ? int(threadIdx.x) : 0;
+  struct Pos {
+    uint16_t k, v;
+    float g;
+    CR x;
+  };
+  auto load_pos = [&](int t) {
+    Pos p;
+    p.k = rk[t * D + ci];
+    p.v = rv[t * D + ci];
+    p.g = PERCH ? rg[t * D + ci] : 0.f;
+    p.x = *reinterpret_cast<const CR *>(rx + int64_t(t) * C + ch);
+    return p;
+  };
+  __shared__ float sk[2][D], svv[2][D], sg[2][D];
+  Pos cur = load_pos(0);
+
+  const bool track = a.track_interval > 0;
+  const int64_t before = track ? a.seq_len_before[b] : 0;
+  int crossings = 0;
+  auto store_to = [&](int sl) {
+    TS *dst = state_block(sl);
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int r = r0 + it * RPI + row_in_group;
+      if (SH::FULL || r < r0 + ROWS)
+        __builtin_nontemporal_store(SV::from_f32(s[it]),
+                                    reinterpret_cast<typename SV::raw *>(dst + int64_t(r) * D + col0));
+    }
+    if (conv_lane) {
+      uint16_t *cr = conv_rows(sl);
+      *reinterpret_cast<CR *>(cr + ch) = c0;
+      *reinterpret_cast<CR *>(cr + C + ch) = c1;
+      *reinterpret_cast<CR *>(cr + 2 * C + ch) = c2;
+    }
+  };
+
+  for (int t = 0; t < n; ++t) {
+    const int buf = t & 1;
+    if (int(threadIdx.x) < D) {
+      sk[buf][ci] = __uint_as_float(uint32_t(cur.k) << 16);
+      svv[buf][ci] = __uint_as_float(uint32_t(cur.v) << 16);
+      if (PERCH) sg[buf][ci] = cur.g;
+    }
+    c0 = c1;
+    c1 = c2;
+    c2 = cur.x;
+    const float gh = PERCH ? 0.f : rg[t];
+    const float beta = rb[t];
+    cur = load_pos(t + 1 < n ? t + 1 : t);  // the next position, ahead of the barrier
+    __syncthreads();
+
+    const float *kr = sk[buf], *vr = svv[buf], *gr = sg[buf];
+    float kinv = 1.f;
+    if (a.flags & GDN_F_L2NORM_K) {
+      float ss = 0.f;
+      for (int j = lane; j < D; j += 64) ss = fmaf(kr[j], kr[j], ss);
+      kinv = 1.f / sqrtf(wave_sum(ss) + 1e-6f);
+    }
+    float kk[VEC], gg[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      kk[e] = kr[col0 + e] * kinv;
+      gg[e] = PERCH ? gr[col0 + e] : gh;
+    }
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int r = r0 + it * RPI + row_in_group;
+      float pu = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        s[it][e] *= gg[e];
+        pu = fmaf(s[it][e], kk[e], pu);
+      }
+      pu = group_sum<LPR>(pu);
+      if (SH::FULL || r < r0 + ROWS) {
+        const float d = beta * (vr[r] - pu);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[it][e] = fmaf(d, kk[e], s[it][e]);
+      }
+    }
+    // a snapshot where the replayed length completes a multiple of the interval
+    if (track && (before + t + 1) % a.track_interval == 0) {
+      const int dst = a.track_slots[2 * b + ((a.next_track_idx[b] + crossings) & 1)];
+      ++crossings;
+      if (dst >= slots) {
+        if (err && threadIdx.x == 0) atomicOr(err, GDN_ERRW_BAD_TRACK_SLOT);
+      } else if (dst > 0) {
+        store_to(dst);
+      }
+    }
+  }
+  store_to(slot);
+}
+
+template <int D, typename TS, bool kVerify>
+hipError_t launch_r(const gdn_pool *p, const ReplayArgs &a, hipStream_t s) {
+  using SH = ReplayShape<D, TS>;
+  dim3 grid(p->d.heads, a.batch);
+  TS *ssm = static_cast<TS *>(p->d.ssm_base);
+  uint16_t *conv = static_cast<uint16_t *>(p->d.conv_base);
+  const bool pc = a.ring.alpha_mode == GDN_ALPHA_PER_CHANNEL;
+  if (kVerify) {
+    if (pc)
+      hipLaunchKernelGGL((replay_verify_kernel<D, TS, GDN_ALPHA_PER_CHANNEL>), grid, dim3(SH::THREADS), 0, s,
+                         ssm, conv, p->d.err_word, p->d.slots, p->d.heads, a);
+    else
+      hipLaunchKernelGGL((replay_verify_kernel<D, TS, GDN_ALPHA_PER_HEAD>), grid, dim3(SH::THREADS), 0, s,
+                         ssm, conv, p->d.err_word, p->d.slots, p->d.heads, a);
+  } else {
+    if (pc)
+      hipLaunchKernelGGL((replay_commit_kernel<D, TS, GDN_ALPHA_PER_CHANNEL>), grid, dim3(SH::THREADS), 0, s,
+                         ssm, conv, p->d.err_word, p->d.slots, p->d.heads, a);
+    else
+      hipLaunchKernelGGL((replay_commit_kernel<D, TS, GDN_ALPHA_PER_HEAD>), grid, dim3(SH::THREADS), 0, s,
+                         ssm, conv, p->d.err_word, p->d.slots, p->d.heads, a);
+  }
+  return hipGetLastError();
+}
+
+template <bool kVerify>
+hipError_t launch_any(const gdn_pool *p, const ReplayArgs &a, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  const bool f32 = p->d.ssm_dtype == GDN_F32;
+  switch (p->d.head_k) {
+    case 16: return f32 ? launch_r<16, float, kVerify>(p, a, s) : launch_r<16, uint16_t, kVerify>(p, a, s);
+    case 32: return f32 ? launch_r<32, float, kVerify>(p, a, s) : launch_r<32, uint16_t, kVerify>(p, a, s);
+    case 64: return f32 ? launch_r<64, float, kVerify>(p, a, s) : launch_r<64, uint16_t, kVerify>(p, a, s);
+    case 128: return f32 ? launch_r<128, float, kVerify>(p, a, s) : launch_r<128, uint16_t, kVerify>(p, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_replay_verify(const gdn_pool *p, const ReplayArgs &a, hipStream_t s) {
+  return launch_any<true>(p, a, s);
+}
+hipError_t launch_replay_commit(const gdn_pool *p, const ReplayArgs &a, hipStream_t s) {
+  return launch_any<false>(p, a, s);
+}
+
+}  // namespace gdn

@@ -94,6 +94,9 @@ enum {
 /* Largest draft tree (nodes per request) the verify and scatter calls accept. */
 #define GDN_MAX_TREE_NODES 1024
 
+/* Largest ReplaySSM ring (positions per slot). */
+#define GDN_MAX_RING_POSITIONS 64
+
 typedef struct {
   int32_t layers, slots, heads, head_k, head_v;
   int32_t conv_kernel;   /* must be 4 */
@@ -103,6 +106,29 @@ typedef struct {
   void *conv_base;       /* device, 16-byte aligned */
   int32_t *err_word;     /* device int32 or NULL */
 } gdn_pool_desc;
+
+/* ReplaySSM ring (page "企业官网建设流程全解析", Kimi K3 notes, section
+ * "ReplaySSM"): per (layer, slot, head, position) the inputs that regenerate a
+ * draft step's state, so that a verify keeps no per-step state.  All arrays are
+ * device memory owned by the caller, indexed by the pool's layers and slots:
+ *   rawk  bf16 [layers][slots][heads][positions][head_k]  k as it leaves the conv
+ *         (before L2 normalisation)
+ *   rawv  bf16 [layers][slots][heads][positions][head_v]  v as it leaves the conv
+ *   g     fp32 [layers][slots][heads][positions] (GDN_ALPHA_PER_HEAD) or
+ *         [layers][slots][heads][positions][head_k] (GDN_ALPHA_PER_CHANNEL): the decay
+ *   beta  fp32 [layers][slots][heads][positions]
+ *   xrow  bf16 [layers][slots][positions][C]: the conv input row of the position
+ *         (the conv state must advance with the accepted tokens)
+ * Sizes: replayssm_ring_bytes.  rawk, rawv, xrow 16-byte aligned. */
+typedef struct {
+  int32_t positions;   /* 1 .. GDN_MAX_RING_POSITIONS */
+  int32_t alpha_mode;  /* GDN_ALPHA_PER_HEAD | GDN_ALPHA_PER_CHANNEL: layout of g and of alpha */
+  uint16_t *rawk;
+  uint16_t *rawv;
+  float *g;
+  float *beta;
+  uint16_t *xrow;
+} gdn_replay_ring;
 
 /* Restore request, one per sequence (page "Qwen3.5 Linear-State Prefix Cache",
  * section 6.1): copy restore_src_slot_id into linear_state_id. */
@@ -249,6 +275,46 @@ gdn_status gdn_accept_scatter(gdn_pool_t pool, int32_t layer, int32_t batch, int
                               int32_t track_interval, const int32_t *track_slots,
                               const int32_t *next_track_idx, const void *node_ssm,
                               const uint16_t *node_conv, void *stream);
+
+/* Byte sizes {rawk, rawv, g, beta, xrow} of a ReplaySSM ring for the pool's
+ * shape.  Pure host arithmetic. */
+gdn_status replayssm_ring_bytes(gdn_pool_t pool, int32_t positions, int32_t alpha_mode,
+                                size_t bytes[5]);
+
+/* Verify a chain of `draft` draft tokens per request with a ReplaySSM ring
+ * (page "企业官网建设流程全解析", section "ReplaySSM": every position's output is
+ * computed, no per-position state is kept, and the lightweight inputs are
+ * recorded).  Token t of request b follows token t-1 (t = 0 follows the live
+ * slot); the state stays in fp32 between the tokens, as in a prefill call.
+ * x [batch][draft][C], alpha [batch][draft][heads] (or ...[head_k], following
+ * ring->alpha_mode), beta [batch][draft][heads], out [batch][draft][heads][head_v];
+ * 1 <= draft <= ring->positions.  The live slot is only read; ring positions
+ * 0 .. draft-1 of the request's slot are overwritten.  Slot rules as for decode. */
+gdn_status replayssm_verify(gdn_pool_t pool, const gdn_replay_ring *ring, int32_t layer,
+                            int32_t batch, int32_t draft, const int32_t *slot_table,
+                            const uint16_t *x, const uint16_t *conv_w, const float *alpha,
+                            const float *beta, float scale, uint32_t flags, uint16_t *out,
+                            void *stream);
+
+/* Exact-fold commit (page "企业官网建设流程全解析", section "ReplaySSM": only the
+ * accepted prefix is replayed, in recurrent order, into the slot; page
+ * "SGLang之MambaRadixCache机制解析", section 9.10: the track boundary is checked
+ * during the replay).  accepted device int32 [batch]: 0 .. ring->positions
+ * tokens from ring positions 0 .. accepted-1 of the request's slot are folded:
+ * k = rawk normalised (flags & GDN_F_L2NORM_K), v = rawv, S' = S Diag(g),
+ * d = beta (v - S'k), S = S' + d k^T; conv rows shift through the x rows.  The
+ * state is rounded to the pool dtype once, at the end (and at a snapshot).
+ * Tracking (track_interval > 0; seq_len_before, track_slots [batch][2],
+ * next_track_idx [batch] device int32): for every i in [1, accepted] with
+ * (seq_len_before + i) % track_interval == 0, the state and conv rows after
+ * token i go to track_slots[2b + ((next_track_idx[b] + j) & 1)] for the j-th
+ * such i (entry <= 0 skips, >= slots sets GDN_ERRW_BAD_TRACK_SLOT).  accepted
+ * outside [0, positions] sets GDN_ERRW_BAD_TREE and skips the request. */
+gdn_status replayssm_commit(gdn_pool_t pool, const gdn_replay_ring *ring, int32_t layer,
+                            int32_t batch, const int32_t *slot_table, const int32_t *accepted,
+                            uint32_t flags, const int32_t *seq_len_before, int32_t track_interval,
+                            const int32_t *track_slots, const int32_t *next_track_idx,
+                            void *stream);
 
 #ifdef __cplusplus
 }

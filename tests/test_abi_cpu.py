@@ -25,7 +25,8 @@ def test_library_exports_every_declared_function():
     assert {"state_pool_bytes", "state_pool_create", "state_pool_destroy", "gdn_last_error",
             "conv_gdn_prefill_chunked", "gdn_prefill_workspace_bytes", "gdn_decode_step",
             "track_snapshot", "restore_slots", "gdn_verify_tree",
-            "gdn_accept_scatter"} <= set(names)
+            "gdn_accept_scatter", "replayssm_ring_bytes", "replayssm_verify",
+            "replayssm_commit"} <= set(names)
     lib = ct.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -119,6 +120,24 @@ def test_calls_reject_bad_arguments_before_launch():
         assert sc(h, 0, 1, 4, fake, fake, None, None, 0, None, None, fake, fake, None) == -1
         assert sc(h, 0, 1, 2000, fake, fake, fake, None, 0, None, None, fake, fake, None) == -2
         assert sc(h, 0, 0, 4, fake, fake, fake, None, 0, None, None, fake, fake, None) == 0
+        # ReplaySSM: ring shape, draft range, alignment, tracking tables
+        ring = B.RingDesc(16, 1, 0x40000, 0x50000, 0x60000, 0x70000, 0x80000)
+        rv, rc = B._lib.replayssm_verify, B._lib.replayssm_commit
+        vargs = [fake, fake, fake, fake, fake, 1.0, 1, fake, None]
+        assert rv(h, ct.byref(ring), 0, 1, 17, *vargs) == -2
+        assert rv(h, ct.byref(ring), 0, 1, 0, *vargs) == -2
+        assert rv(h, None, 0, 1, 4, *vargs) == -1
+        bad = B.RingDesc(0, 1, 0x40000, 0x50000, 0x60000, 0x70000, 0x80000)
+        assert rv(h, ct.byref(bad), 0, 1, 1, *vargs) == -2
+        bad = B.RingDesc(16, 3, 0x40000, 0x50000, 0x60000, 0x70000, 0x80000)
+        assert rv(h, ct.byref(bad), 0, 1, 1, *vargs) == -1
+        bad = B.RingDesc(16, 1, 0x40008, 0x50000, 0x60000, 0x70000, 0x80000)
+        assert rv(h, ct.byref(bad), 0, 1, 1, *vargs) == -3
+        assert rv(h, ct.byref(ring), 0, 0, 4, *vargs) == 0
+        assert rc(h, ct.byref(ring), 0, 1, fake, fake, 1, None, 256, None, None, None) == -1
+        assert rc(h, ct.byref(ring), 0, 1, fake, None, 1, None, 0, None, None, None) == -1
+        assert rc(h, ct.byref(ring), 0, 1, fake, fake, 1, None, -1, None, None, None) == -1
+        assert rc(h, ct.byref(ring), 0, 0, fake, fake, 1, None, 0, None, None, None) == 0
     finally:
         B._lib.state_pool_destroy(h)
 
