@@ -12,9 +12,10 @@ cache.  Inputs are resident in HBM before timing starts.
 
 Secondary lines (in "extra"): the KDA chunked prefill (12 heads, one request of
 6144 tokens, snapshot every 64 tokens), the KDA decode with tracking over 69
-layers, a prefix-hit restore across 24 layers followed by a warm prefill, and
-a speculative-decoding round (draft-tree verify in 32 layers, then the
-accepted-step commit).
+layers, a prefix-hit restore across 24 layers followed by a warm prefill, a
+speculative-decoding round (draft-tree verify in 32 layers, then the
+accepted-step commit), and a ReplaySSM round (ring verify of a draft chain in
+69 layers, then the exact-fold commit).
 
 Run on one GPU only: --gpus N with N > 1 exits with a message.
 """
@@ -450,6 +451,83 @@ def run_spec_verify(torch, gdn, wl, dev, rounds=3, warmup=1):
     return res
 
 
+# ------------------------------------------------------------ ReplaySSM --
+def run_replayssm(torch, gdn, wl, dev, rounds=5, warmup=1):
+    """ReplaySSM speculative round on the KDA decode pool (69 layers, 1024 slots,
+    12 heads, K = V = 128, bf16 state, per-channel decay) with the pages'
+    16-position ring, batch 256.  Each round verifies a 4-token draft chain per
+    request in every layer (outputs + ring, no state written), then commits 1..4
+    accepted tokens per request in every layer (exact fold), with tracking every
+    256 tokens into ping-pong track slots."""
+    cfg = wl.KDA_DECODE
+    L, N, H, D, B, T, P = cfg.layers, cfg.slots, cfg.heads, cfg.head_k, 256, 4, 16
+    C = H * 3 * D
+    g = torch.Generator(device=dev)
+    g.manual_seed(107)
+    ssm = torch.empty(L, N, H, D, D, dtype=torch.bfloat16, device=dev).normal_(0.0, 0.25, generator=g)
+    conv = torch.empty(L, N, 3, C, dtype=torch.bfloat16, device=dev).normal_(0.0, 1.0, generator=g)
+    pool = gdn.state_pool_create(ssm, conv, torch.zeros(1, dtype=torch.int32, device=dev))
+    ring = gdn.ReplayRing(pool, P, gdn.ALPHA_PER_CHANNEL)
+    gc = wl.generator(107)
+    perm = (torch.randperm(N - 1, generator=gc) + 1).to(torch.int32)
+    slots = perm[:B].to(dev)
+    track = perm[B:3 * B].view(B, 2).contiguous().to(dev)
+    accepted = torch.randint(1, T + 1, (B,), generator=gc, dtype=torch.int32).to(dev)
+    before = torch.randint(256, 8192, (B,), generator=gc, dtype=torch.int32).to(dev)
+    inp = {k: v.to(dev) for k, v in wl.projected_inputs(gc, B * T, H, D, D, gdn.ALPHA_PER_CHANNEL).items()}
+    x = inp["x"].view(B, T, C)
+    alpha, beta = inp["alpha"].view(B, T, H, D), inp["beta"].view(B, T, H)
+    w = wl.conv_weights(gc, C).to(dev)
+    out = torch.empty(B, T, H, D, dtype=torch.bfloat16, device=dev)
+    nxt = torch.zeros(B, dtype=torch.int32, device=dev)
+
+    def verify():
+        for l in range(L):
+            gdn.replayssm_verify(pool, ring, l, slots, x, w, alpha, beta, out)
+
+    def commit():
+        for l in range(L):
+            gdn.replayssm_commit(pool, ring, l, slots, accepted, seq_len_before=before,
+                                 track_interval=256, track_slots=track, next_track_idx=nxt)
+
+    for _ in range(warmup):
+        verify()
+        commit()
+    torch.cuda.synchronize()
+    ev = [event_pair() + event_pair() for _ in range(rounds)]
+    for a, b, c, d in ev:
+        a.record()
+        verify()
+        b.record()
+        c.record()
+        commit()
+        d.record()
+    torch.cuda.synchronize()
+    tv = sorted(a.elapsed_time(b) for a, b, _, _ in ev)[rounds // 2] / 1e3
+    tc = sorted(c.elapsed_time(d) for _, _, c, d in ev)[rounds // 2] / 1e3
+    assert int(pool.err_word.item()) == 0
+    state, rows = H * D * D * 2, 3 * C * 2
+    ring_pos = H * D * 2 * 2 + H * D * 4 + H * 4 + C * 2          # rawk, rawv, g, beta, xrow
+    v_bytes = B * (state + rows + T * (C * 2 + H * D * 4 + H * 4 + ring_pos + H * D * 2)) + C * 8
+    n_acc = int(accepted.sum())
+    c_bytes = B * 2 * (state + rows) + n_acc * ring_pos
+    crossed = int(((before + accepted) // 256 - before // 256).clamp(max=2).sum())
+    c_bytes += crossed * (state + rows)
+    res = {"workload": "ReplaySSM round: KDA pool (69 layers, 1024 slots, 12 heads, K=V=128, bf16 "
+                       "state), 16-position ring, 256 requests, 4-token draft chain, 1..4 accepted, "
+                       "track every 256",
+           "verify_ms_per_layer": tv / L * 1e3, "commit_ms_per_layer": tc / L * 1e3,
+           "round_ms": (tv + tc) * 1e3, "draft_tokens_per_s": B * T / (tv + tc),
+           "verify_GB_per_s": v_bytes * L / tv / 1e9, "verify_hbm_frac": v_bytes * L / tv / 1e9 / HBM_PEAK_GBS,
+           "commit_GB_per_s": c_bytes * L / tc / 1e9, "commit_hbm_frac": c_bytes * L / tc / 1e9 / HBM_PEAK_GBS,
+           "verify_bytes_per_launch": v_bytes, "commit_bytes_per_launch": c_bytes,
+           "ring_GB": sum(t.numel() * t.element_size() for t in (ring.rawk, ring.rawv, ring.g, ring.beta,
+                                                                    ring.xrow)) / 1e9}
+    del pool, ssm, conv, ring
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------ cpu baseline --
 def cpu_baseline(wl, seconds=10.0):
     import numpy as np
@@ -482,7 +560,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--extra", default="kda_prefill,restore,kda_decode_tracking,warm_prefill,"
-                    "spec_verify", help="comma-separated secondary workloads to run")
+                    "spec_verify,replayssm", help="comma-separated secondary workloads to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -504,7 +582,8 @@ def main():
             "restore": ("restore", run_restore),
             "kda_decode_tracking": ("KDA decode with tracking (69 layers)", run_kda_decode_tracking),
             "warm_prefill": ("prefix-hit restore + warm prefill (24 layers)", run_warm_prefill),
-            "spec_verify": ("speculative verify + commit (32 layers)", run_spec_verify)}
+            "spec_verify": ("speculative verify + commit (32 layers)", run_spec_verify),
+            "replayssm": ("ReplaySSM verify + exact-fold commit (69 layers)", run_replayssm)}
     chosen = [] if args.no_extra else [n for n in args.extra.split(",") if n]
     for name in chosen:
         if name not in runs:

@@ -22,6 +22,8 @@
 namespace gdn {
 namespace {
 
+constexpr int kGroup = 8;  // tokens staged in shared memory at a time
+
 template <int D, typename TS>
 struct ReplayShape {
   static constexpr int VEC = StateVec<TS>::N;
@@ -68,7 +70,6 @@ __global__ __launch_bounds__((ReplayShape<D, TS>::THREADS)) void replay_verify_k
   static_assert(ITEMS <= SH::THREADS, "one conv item per thread");
   using CV = ConvVec<CW>;
   typedef typename CV::raw CR;
-  constexpr int NAL = kAlphaMode == GDN_ALPHA_PER_CHANNEL ? VEC : 1;
 
   const int h = blockIdx.x, b = blockIdx.y;
   const int T = a.draft, H = heads, P = a.ring.positions;
@@ -122,100 +123,113 @@ __global__ __launch_bounds__((ReplayShape<D, TS>::THREADS)) void replay_verify_k
   float *rb = a.ring.beta + rrow;
   uint16_t *rx = a.ring.xrow + (int64_t(a.layer) * slots + slot) * P * C;
 
-  __shared__ __attribute__((aligned(16))) float sy[2][3 * D];  // q | k | v, double buffered
+  // Tokens go in groups of up to kGroup: the conv of every token of a group
+  // (which needs no state) runs first and lands in shared memory with the
+  // group's decays and betas, then one barrier, then the state updates follow
+  // each other with nothing between them but the wave's own reductions.
+  constexpr int NA = kAlphaMode == GDN_ALPHA_PER_CHANNEL ? D : 1;
+  __shared__ __attribute__((aligned(16))) float sy[kGroup][3 * D];  // q | k | v per token
+  __shared__ float sa[kGroup][NA];
+  __shared__ float sb[kGroup];
 
-  auto load_x = [&](int t) { return *reinterpret_cast<const CR *>(a.x + (tok0 + t) * C + ch); };
-  CR xv = load_x(0);
-
-  for (int t = 0; t < T; ++t) {
-    const int64_t tok = tok0 + t;
-    float *y = sy[t & 1];
+  for (int t0 = 0; t0 < T; t0 += kGroup) {
+    const int tn = T - t0 < kGroup ? T - t0 : kGroup;
+    // ---- phase 1: conv, ring records, decays and betas of the group ---------
+    CR xs[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j)
+      if (j < tn) xs[j] = *reinterpret_cast<const CR *>(a.x + (tok0 + t0 + j) * C + ch);
+    for (int i = threadIdx.x; i < tn * NA; i += SH::THREADS) {
+      const int j = i / NA, c = i % NA;
+      const float v = a.alpha[((tok0 + t0 + j) * H + h) * NA + c];
+      sa[j][c] = v;
+      rg[(t0 + j) * NA + c] = v;
+    }
+    if (int(threadIdx.x) < tn) {
+      const float v = a.beta[(tok0 + t0 + threadIdx.x) * H + h];
+      sb[threadIdx.x] = v;
+      rb[t0 + threadIdx.x] = v;
+    }
     if (conv_lane) {
-      float yv[CW];
 #pragma unroll
-      for (int e = 0; e < CW; ++e) {
-        const int sh = (e & 1) ? 16 : 0;
-        auto pick = [&](const CR &v) {
-          return __uint_as_float(((CV::word(v, e >> 1) >> sh) & 0xffffu) << 16);
-        };
-        const u32x4 &w = wv[e >> 1];
-        const int wb = (e & 1) * 2;
-        float acc = __uint_as_float(w[wb] << 16) * pick(w0);
-        acc = fmaf(__uint_as_float(w[wb] & 0xffff0000u), pick(w1), acc);
-        acc = fmaf(__uint_as_float(w[wb + 1] << 16), pick(w2), acc);
-        acc = fmaf(__uint_as_float(w[wb + 1] & 0xffff0000u), pick(xv), acc);
-        if (a.flags & GDN_F_CONV_SILU) acc = acc / (1.f + __expf(-acc));
-        yv[e] = acc;
-        y[pt * D + jc + e] = acc;
+      for (int j = 0; j < kGroup; ++j) {
+        if (j >= tn) break;
+        const int t = t0 + j;
+        float yv[CW];
+#pragma unroll
+        for (int e = 0; e < CW; ++e) {
+          const int sh = (e & 1) ? 16 : 0;
+          auto pick = [&](const CR &v) {
+            return __uint_as_float(((CV::word(v, e >> 1) >> sh) & 0xffffu) << 16);
+          };
+          const u32x4 &w = wv[e >> 1];
+          const int wb = (e & 1) * 2;
+          float acc = __uint_as_float(w[wb] << 16) * pick(w0);
+          acc = fmaf(__uint_as_float(w[wb] & 0xffff0000u), pick(w1), acc);
+          acc = fmaf(__uint_as_float(w[wb + 1] << 16), pick(w2), acc);
+          acc = fmaf(__uint_as_float(w[wb + 1] & 0xffff0000u), pick(xs[j]), acc);
+          if (a.flags & GDN_F_CONV_SILU) acc = acc / (1.f + __expf(-acc));
+          yv[e] = acc;
+          sy[j][pt * D + jc + e] = acc;
+        }
+        // the ring: k and v as they leave the conv (bf16), and the conv input row
+        if (pt == 1) *reinterpret_cast<decltype(PackCW<CW>::pack(yv)) *>(rk + t * D + jc) = PackCW<CW>::pack(yv);
+        if (pt == 2) *reinterpret_cast<decltype(PackCW<CW>::pack(yv)) *>(rv + t * D + jc) = PackCW<CW>::pack(yv);
+        *reinterpret_cast<CR *>(rx + int64_t(t) * C + ch) = xs[j];
+        w0 = w1;
+        w1 = w2;
+        w2 = xs[j];
       }
-      // the ring: k and v as they leave the conv (bf16), and the conv input row
-      if (pt == 1) *reinterpret_cast<decltype(PackCW<CW>::pack(yv)) *>(rk + t * D + jc) = PackCW<CW>::pack(yv);
-      if (pt == 2) *reinterpret_cast<decltype(PackCW<CW>::pack(yv)) *>(rv + t * D + jc) = PackCW<CW>::pack(yv);
-      *reinterpret_cast<CR *>(rx + int64_t(t) * C + ch) = xv;
     }
-    if (kAlphaMode == GDN_ALPHA_PER_CHANNEL) {
-      for (int i = threadIdx.x; i < D; i += SH::THREADS) rg[t * D + i] = a.alpha[(tok * H + h) * D + i];
-    } else if (threadIdx.x == 0) {
-      rg[t] = a.alpha[tok * H + h];
-    }
-    if (threadIdx.x == 0) rb[t] = a.beta[tok * H + h];
-    float al[NAL];
-    if (kAlphaMode == GDN_ALPHA_PER_CHANNEL) {
-      const float *ap = a.alpha + (tok * H + h) * D + col0;
-#pragma unroll
-      for (int e = 0; e < NAL; ++e) al[e] = ap[e];
-    } else {
-      al[0] = a.alpha[tok * H + h];
-    }
-    const float beta = a.beta[tok * H + h];
-    // the window of the next token, and its x, ahead of the barrier
-    w0 = w1;
-    w1 = w2;
-    w2 = xv;
-    xv = load_x(t + 1 < T ? t + 1 : t);
-    __syncthreads();  // y complete; the other buffer is free again for token t + 1
+    __syncthreads();
 
-    const float *sq = y, *sk = y + D, *sv = y + 2 * D;
-    float kinv = 1.f, qinv = 1.f;
-    if (a.flags & GDN_F_L2NORM_K) {
-      float ss = 0.f;
-      for (int j = lane; j < D; j += 64) ss = fmaf(sk[j], sk[j], ss);
-      kinv = 1.f / sqrtf(wave_sum(ss) + 1e-6f);
-    }
-    if (a.flags & GDN_F_L2NORM_Q) {
-      float ss = 0.f;
-      for (int j = lane; j < D; j += 64) ss = fmaf(sq[j], sq[j], ss);
-      qinv = 1.f / sqrtf(wave_sum(ss) + 1e-6f);
-    }
-    float kq = 0.f;
-    for (int j = lane; j < D; j += 64) kq = fmaf(sk[j] * kinv, sq[j] * qinv, kq);
-    kq = wave_sum(kq);
-    float kk[VEC], qq[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      kk[e] = sk[col0 + e] * kinv;
-      qq[e] = sq[col0 + e] * qinv;
-    }
-    uint16_t *out = a.out + (tok * H + h) * D;
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int r = r0 + it * RPI + row_in_group;
-      float pu = 0.f, pq = 0.f;
+    // ---- phase 2: the group's state updates, back to back -------------------
+    for (int j = 0; j < tn; ++j) {
+      const float *sq = sy[j], *sk = sy[j] + D, *sv = sy[j] + 2 * D;
+      float kinv = 1.f, qinv = 1.f;
+      if (a.flags & GDN_F_L2NORM_K) {
+        float ss = 0.f;
+        for (int c = lane; c < D; c += 64) ss = fmaf(sk[c], sk[c], ss);
+        kinv = 1.f / sqrtf(wave_sum(ss) + 1e-6f);
+      }
+      if (a.flags & GDN_F_L2NORM_Q) {
+        float ss = 0.f;
+        for (int c = lane; c < D; c += 64) ss = fmaf(sq[c], sq[c], ss);
+        qinv = 1.f / sqrtf(wave_sum(ss) + 1e-6f);
+      }
+      float kq = 0.f;
+      for (int c = lane; c < D; c += 64) kq = fmaf(sk[c] * kinv, sq[c] * qinv, kq);
+      kq = wave_sum(kq);
+      float kk[VEC], qq[VEC], al[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        s[it][e] *= al[NAL == 1 ? 0 : e];
-        pu = fmaf(s[it][e], kk[e], pu);
-        pq = fmaf(s[it][e], qq[e], pq);
+        kk[e] = sk[col0 + e] * kinv;
+        qq[e] = sq[col0 + e] * qinv;
+        al[e] = sa[j][NA == 1 ? 0 : col0 + e];
       }
-      pu = group_sum<LPR>(pu);
-      pq = group_sum<LPR>(pq);
-      if (SH::FULL || r < r0 + ROWS) {
-        const float d = beta * (sv[r] - pu);
+      const float beta = sb[j];
+      uint16_t *out = a.out + ((tok0 + t0 + j) * H + h) * D;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) s[it][e] = fmaf(d, kk[e], s[it][e]);
-        if ((lane % LPR) == 0) out[r] = f32_to_bf16(a.scale * fmaf(d, kq, pq));
+      for (int it = 0; it < ITERS; ++it) {
+        const int r = r0 + it * RPI + row_in_group;
+        float pu = 0.f, pq = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          s[it][e] *= al[e];
+          pu = fmaf(s[it][e], kk[e], pu);
+          pq = fmaf(s[it][e], qq[e], pq);
+        }
+        pu = group_sum<LPR>(pu);
+        pq = group_sum<LPR>(pq);
+        if (SH::FULL || r < r0 + ROWS) {
+          const float d = beta * (sv[r] - pu);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) s[it][e] = fmaf(d, kk[e], s[it][e]);
+          if ((lane % LPR) == 0) out[r] = f32_to_bf16(a.scale * fmaf(d, kq, pq));
+        }
       }
     }
+    __syncthreads();  // the group's shared inputs are read; the next group may overwrite them
   }
 }
 
