@@ -72,6 +72,20 @@ _lib.gdn_verify_tree.argtypes = [
 _lib.gdn_accept_scatter.argtypes = [
     _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
 _lib.replayssm_ring_bytes.argtypes = [_vp, _i32, _i32, ct.POINTER(_sz)]
+_i64, _u64 = ct.c_int64, ct.c_uint64
+_lib.ckpt_chain_hashes.argtypes = [_vp, _i64, _i32, _i64, _u64, _vp, _i64, ct.POINTER(_i64)]
+_lib.ckpt_index_create.argtypes = [_i32, ct.POINTER(_vp)]
+_lib.ckpt_index_destroy.argtypes = [_vp]
+_lib.ckpt_index_destroy.restype = None
+_lib.ckpt_index_size.argtypes = [_vp]
+_lib.ckpt_index_size.restype = _i32
+_lib.ckpt_index_contains.argtypes = [_vp, _u64]
+_lib.ckpt_index_contains.restype = _i32
+_lib.ckpt_index_match.argtypes = [_vp, _vp, _i64, _i64, _i32, ct.POINTER(_i64), ct.POINTER(_i32),
+                                  ct.POINTER(_u64)]
+_lib.ckpt_index_release.argtypes = [_vp, _u64]
+_lib.ckpt_index_insert.argtypes = [_vp, _u64, _i32, ct.POINTER(_i32), ct.POINTER(_i32)]
+_lib.ckpt_plan_restores.argtypes = [_vp, _i32, _vp, _vp, _i32, _vp, ct.POINTER(RestoreOp), _vp, _vp]
 _lib.replayssm_verify.argtypes = [
     _vp, ct.POINTER(RingDesc), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _f32, _u32, _vp, _vp]
 _lib.replayssm_commit.argtypes = [
@@ -79,7 +93,8 @@ _lib.replayssm_commit.argtypes = [
 for _f in ("state_pool_bytes", "state_pool_create", "conv_gdn_prefill_chunked",
            "gdn_prefill_workspace_bytes", "gdn_decode_step", "track_snapshot", "restore_slots",
            "gdn_verify_tree", "gdn_accept_scatter", "replayssm_ring_bytes", "replayssm_verify",
-           "replayssm_commit"):
+           "replayssm_commit", "ckpt_chain_hashes", "ckpt_index_create", "ckpt_index_match",
+           "ckpt_index_release", "ckpt_index_insert", "ckpt_plan_restores"):
     getattr(_lib, _f).restype = ct.c_int
 
 
@@ -353,3 +368,80 @@ def replayssm_commit(pool: StatePool, ring: ReplayRing, layer, slot_table, accep
     _check(_lib.replayssm_commit(pool.handle, ct.byref(d), layer, B, _ptr(slot_table), _ptr(accepted),
                                  flags, _ptr(seq_len_before), track_interval, _ptr(track_slots),
                                  _ptr(next_track_idx), _stream(stream)))
+
+
+# ------------------------------------------------------- checkpoint index --
+CKPT_STORED, CKPT_PRESENT, CKPT_FULL = 0, 1, 2
+
+
+def ckpt_chain_hashes(tokens, stride, first_chunk=0, prev_key=0):
+    """Chained keys of the whole chunks first_chunk.. of an int32 token sequence
+    (numpy array or list); returns a numpy uint64 array."""
+    import numpy as np
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    cap = max(t.shape[0] // stride - first_chunk, 0) if stride > 0 else 0  # the library rejects stride < 1
+    keys = np.zeros(max(cap, 1), dtype=np.uint64)
+    n = ct.c_int64()
+    _check(_lib.ckpt_chain_hashes(t.ctypes.data, t.shape[0], stride, first_chunk, prev_key,
+                                  keys.ctypes.data, cap, ct.byref(n)))
+    return keys[:n.value]
+
+
+class CheckpointIndex:
+    """The host checkpoint index (include/gdn_ckpt.h)."""
+
+    def __init__(self, capacity):
+        h = _vp()
+        _check(_lib.ckpt_index_create(capacity, ct.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        try:
+            if self.handle:
+                _lib.ckpt_index_destroy(self.handle)
+                self.handle = None
+        except Exception:
+            pass
+
+    def __len__(self):
+        return _lib.ckpt_index_size(self.handle)
+
+    def contains(self, key):
+        return bool(_lib.ckpt_index_contains(self.handle, int(key)))
+
+    def match(self, keys, n_tokens, stride):
+        """(reach_tokens, slot, key); (0, -1, None) on a miss."""
+        import numpy as np
+        k = np.ascontiguousarray(keys, dtype=np.uint64)
+        reach, slot, key = ct.c_int64(), ct.c_int32(), ct.c_uint64()
+        _check(_lib.ckpt_index_match(self.handle, k.ctypes.data if k.size else None, k.size, n_tokens,
+                                     stride, ct.byref(reach), ct.byref(slot), ct.byref(key)))
+        return (reach.value, slot.value, key.value) if slot.value >= 0 else (0, -1, None)
+
+    def release(self, key):
+        _check(_lib.ckpt_index_release(self.handle, int(key)))
+
+    def insert(self, key, slot):
+        """('stored' | 'present' | 'full', slot_back)."""
+        out, back = ct.c_int32(), ct.c_int32()
+        _check(_lib.ckpt_index_insert(self.handle, int(key), slot, ct.byref(out), ct.byref(back)))
+        return ("stored", "present", "full")[out.value], back.value
+
+    def plan_restores(self, token_lists, stride, live_slots):
+        """Hash, match and pin for a batch; returns (ops, reach, hit_keys) where ops
+        are (linear_state_id, restore_requested, restore_src_slot_id) tuples."""
+        import numpy as np
+        n = len(token_lists)
+        cu = np.zeros(n + 1, dtype=np.int64)
+        for i, t in enumerate(token_lists):
+            cu[i + 1] = cu[i] + len(t)
+        toks = np.ascontiguousarray(np.concatenate([np.asarray(t, dtype=np.int32) for t in token_lists])
+                                    if n else np.zeros(1, dtype=np.int32))
+        live = np.ascontiguousarray(live_slots, dtype=np.int32)
+        ops = (RestoreOp * max(n, 1))()
+        reach = np.zeros(max(n, 1), dtype=np.int64)
+        keys = np.zeros(max(n, 1), dtype=np.uint64)
+        _check(_lib.ckpt_plan_restores(self.handle, n, toks.ctypes.data, cu.ctypes.data, stride,
+                                       live.ctypes.data, ops, reach.ctypes.data, keys.ctypes.data))
+        return ([(ops[i].linear_state_id, ops[i].restore_requested, ops[i].restore_src_slot_id)
+                 for i in range(n)], reach[:n], keys[:n])

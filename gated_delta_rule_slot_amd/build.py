@@ -17,6 +17,10 @@ LIB = os.path.join(HERE, "libgdnslot.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.hip", "slot_copy.hip", "decode.hip", "prefill.hip", "verify.hip", "replay.hip"]
+HOST_SOURCES = ["ckpt_index.cpp"]  # host-only C++ (the checkpoint index), built with g++
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra",
+              "-I", INCLUDE, "-I", CSRC]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -40,10 +44,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _compile_host(src: str, verbose: bool) -> str:
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+    cmd = [CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"{CXX} failed on {src}:\n{r.stderr}")
+    if verbose and r.stderr.strip():
+        print(r.stderr, flush=True)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=4) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        objs += list(ex.map(lambda s: _compile_host(s, verbose), HOST_SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

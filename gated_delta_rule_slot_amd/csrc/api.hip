@@ -7,25 +7,33 @@
 #include <new>
 
 #include "common.hpp"
+#include "errors.hpp"
 
 #define GDN_API extern "C" __attribute__((visibility("default")))
 
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
 
-gdn_status fail(gdn_status s, const char *fmt, ...) {
+namespace gdn {
+gdn_status set_error(gdn_status s, const char *fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof g_err, fmt, ap);
   va_end(ap);
   return s;
 }
-
-gdn_status ok() {
+gdn_status clear_error() {
   g_err[0] = '\0';
   return GDN_OK;
 }
+}  // namespace gdn
+
+namespace {
+
+#define fail(...) gdn::set_error(__VA_ARGS__)
+
+gdn_status ok() { return gdn::clear_error(); }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

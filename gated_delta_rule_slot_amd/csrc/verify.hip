@@ -52,7 +52,7 @@ struct VerifyShape {
 
 template <int D, typename TS, int kAlphaMode>
 __global__ __launch_bounds__((VerifyShape<D, TS>::THREADS))
-__attribute__((amdgpu_waves_per_eu(4))) void gdn_verify_kernel(
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 1))) void gdn_verify_kernel(
     const TS *__restrict__ ssm, const uint16_t *__restrict__ conv, int32_t *err, int slots,
     int heads, VerifyArgs a) {
   using SV = StateVec<TS>;

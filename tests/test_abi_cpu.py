@@ -15,7 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "gdn_slot.h")).read()
+    text = "".join(open(os.path.join(ROOT, "include", f)).read()
+                   for f in sorted(os.listdir(os.path.join(ROOT, "include"))) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
 
@@ -26,7 +27,9 @@ def test_library_exports_every_declared_function():
             "conv_gdn_prefill_chunked", "gdn_prefill_workspace_bytes", "gdn_decode_step",
             "track_snapshot", "restore_slots", "gdn_verify_tree",
             "gdn_accept_scatter", "replayssm_ring_bytes", "replayssm_verify",
-            "replayssm_commit"} <= set(names)
+            "replayssm_commit", "ckpt_chain_hashes", "ckpt_index_create", "ckpt_index_destroy",
+            "ckpt_index_size", "ckpt_index_contains", "ckpt_index_match", "ckpt_index_release",
+            "ckpt_index_insert", "ckpt_plan_restores"} <= set(names)
     lib = ct.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
