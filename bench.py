@@ -264,12 +264,16 @@ def run_kda_decode_tracking(torch, gdn, wl, dev, steps=16, warmup=2):
 
 # ------------------------------------------------ prefix hit + warm prefill --
 def run_warm_prefill(torch, gdn, wl, dev, ws_cap=8 << 30):
+    import numpy as np
     """64 requests of 13600 tokens in 8 prefix groups over 24 GDN layers (32 heads,
-    fp32 pool of 81 slots: 64 live + 8 groups x 2 checkpoints).  A request whose
-    shared prefix P reaches c = 6144 * min(2, P // 6144) > 0 restores the group's
-    checkpoint at c into its live slot across all layers, then every request is
-    prefilled from c to 13600 (cold when c = 0).  Checkpoint contents are random
-    (they stand for the seed runs); one x buffer serves every layer."""
+    fp32 pool of 81 slots: 64 live + 8 groups x 2 checkpoints).  Each group's seed
+    run left checkpoints at 6144 and 12288 tokens of the group's token sequence,
+    stored in the host checkpoint index under their chained keys; a request shares
+    the first P ~ U[0, 13600) tokens of its group's sequence.  The index plans the
+    restores (deepest checkpoint strictly below the final token, so c = 6144 *
+    min(2, P // 6144)), restore_slots copies them across all layers, then every
+    request is prefilled from c to 13600 (cold on a miss).  Checkpoint contents
+    are random (they stand for the seed runs); one x buffer serves every layer."""
     cfg = wl.WARM_PREFILL
     L, N, H, D, B, T_full = cfg.layers, cfg.slots, cfg.heads, cfg.head_k, 64, 13600
     C = H * 3 * D
@@ -284,9 +288,23 @@ def run_warm_prefill(torch, gdn, wl, dev, ws_cap=8 << 30):
     gc = wl.generator(cfg.seed)
     group = torch.randint(0, 8, (B,), generator=gc).tolist()
     prefix = torch.randint(0, T_full, (B,), generator=gc).tolist()
-    depth = [6144 * min(2, p // 6144) for p in prefix]
-    ops = [(1 + i, 1 if depth[i] > 0 else 0, 65 + 2 * group[i] + (depth[i] // 6144 - 1))
-           for i in range(B)]
+    # token sequences: the groups' seed sequences and the requests sharing P tokens of theirs
+    seeds = torch.randint(0, 150000, (8, T_full), generator=gc, dtype=torch.int32).numpy()
+    reqs = []
+    for i in range(B):
+        tail = torch.randint(150000, 160000, (T_full - prefix[i],), generator=gc, dtype=torch.int32).numpy()
+        reqs.append(np.concatenate([seeds[group[i]][:prefix[i]], tail]))
+    stride = 6144
+    index = gdn.CheckpointIndex(64)
+    for gi in range(8):
+        keys = gdn.ckpt_chain_hashes(seeds[gi][:2 * stride], stride)
+        for c, k in enumerate(keys):
+            assert index.insert(int(k), 65 + 2 * gi + c) == ("stored", -1)
+    t0 = time.perf_counter()
+    ops, reach, hit_keys = index.plan_restores(reqs, stride, list(range(1, B + 1)))
+    t_plan = time.perf_counter() - t0
+    depth = [int(r) for r in reach]
+    assert depth == [stride * min(2, p // stride) for p in prefix]
     lens = [T_full - c for c in depth]
     T = sum(lens)
     cu = wl.cu_seqlens(lens).to(dev)
@@ -315,10 +333,13 @@ def run_warm_prefill(torch, gdn, wl, dev, ws_cap=8 << 30):
                                      max(lens), start_len=start, workspace=ws)
     b.record()
     torch.cuda.synchronize()
+    for k, c in zip(hit_keys, depth):
+        if c:
+            index.release(int(k))   # the restore copies have run
     assert int(pool.err_word.item()) == 0
     t_restore = a.elapsed_time(m) / 1e3
     t_prefill = m.elapsed_time(b) / 1e3
-    n_restored = sum(1 for o in ops if o[1])
+    n_restored = sum(1 for o in ops if o[2] >= 1)
     restore_bytes = 2 * n_restored * L * (H * D * D * 4 + 3 * C * 2)
     flops = T * L * H * 140.6e3
     del pool, ssm, conv, x, out, ws
@@ -326,6 +347,8 @@ def run_warm_prefill(torch, gdn, wl, dev, ws_cap=8 << 30):
     return {"workload": "prefix-hit restore + warm prefill: 64 requests x 13600 tokens, 8 prefix groups, "
                         "24 GDN layers, 32 heads, K=V=128, fp32 pool of 81 slots",
             "restored_requests": n_restored, "restore_ms": t_restore * 1e3,
+            "index_plan_ms": t_plan * 1e3,
+            "index_plan_us_per_request": t_plan / B * 1e6,
             "restore_GB_per_s": restore_bytes / t_restore / 1e9,
             "prefill_tokens": T, "prefill_ms": t_prefill * 1e3,
             "prefill_tokens_per_s": T / t_prefill,
