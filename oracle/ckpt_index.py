@@ -24,6 +24,12 @@ as possible: a dict from key to entry, a Python list for the recency order.
   recently used entry whose reference count is 0 and returns its slot; if every
   entry is pinned the insert is refused.
 * release: reference count - 1 once the restore copied from the slot.
+* finish (page "SGLang Mamba Radix Cache 深度解析", cache_finished_req and
+  free_mamba_cache in extra_buffer mode): the track slot other(next) holds the
+  last tracked boundary and goes to the index under that boundary's key, no
+  copy; the live slot and track slot next are freed, and so is the kept slot
+  when the index does not take it (key already held, or every entry pinned),
+  together with any slot an insert evicts.
 """
 from __future__ import annotations
 
@@ -105,3 +111,20 @@ class CheckpointIndex:
         self.entries[key] = [slot, 0]
         self.order.append(key)
         return "stored", evicted
+
+
+def finish_request(index, key, live_slot, track_slots, next_track_idx):
+    """Slots the caller frees when a request finishes (see the module notes);
+    key None means no boundary was tracked, so every slot is freed."""
+    keep = track_slots[1 - (next_track_idx & 1)]
+    freed = [live_slot, track_slots[next_track_idx & 1]]
+    if key is None:
+        freed.append(keep)
+    else:
+        status, back = index.insert(key, keep)
+        if status == "stored":
+            if back >= 0:
+                freed.append(back)
+        else:
+            freed.append(back)
+    return [s for s in freed if s > 0]

@@ -122,3 +122,15 @@ def test_prefix_walkthrough_from_the_page(golden_dir):
             idx.insert(save_key, next(slots))
     assert got[:7] == spec["prefix"][:7]
     assert got[7] == 256 and spec["prefix"][7] == 512
+
+
+def test_finish_keeps_the_other_track_slot_as_the_page_shows():
+    """extra_buffer mode: track slots [B, C] with next = 1 -> slot B (index 0) goes
+    to the cache, C and the live slot A are released; without a tracked boundary
+    everything is released; a key already held sends the kept slot back too."""
+    A, Bs, Cs = 3, 7, 9
+    idx = ci.CheckpointIndex(4)
+    assert ci.finish_request(idx, 111, A, [Bs, Cs], 1) == [A, Cs]
+    assert idx.entries[111][0] == Bs
+    assert ci.finish_request(idx, None, A, [Bs, Cs], 0) == [A, Bs, Cs]
+    assert ci.finish_request(idx, 111, A, [5, 6], 0) == [A, 5, 6]
