@@ -86,6 +86,8 @@ _lib.ckpt_index_match.argtypes = [_vp, _vp, _i64, _i64, _i32, ct.POINTER(_i64), 
 _lib.ckpt_index_release.argtypes = [_vp, _u64]
 _lib.ckpt_index_insert.argtypes = [_vp, _u64, _i32, ct.POINTER(_i32), ct.POINTER(_i32)]
 _lib.ckpt_plan_restores.argtypes = [_vp, _i32, _vp, _vp, _i32, _vp, ct.POINTER(RestoreOp), _vp, _vp]
+_lib.ckpt_finish_request.argtypes = [_vp, _i32, _u64, _i32, ct.POINTER(_i32), _i32, ct.POINTER(_i32),
+                                     ct.POINTER(_i32)]
 _lib.replayssm_verify.argtypes = [
     _vp, ct.POINTER(RingDesc), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _f32, _u32, _vp, _vp]
 _lib.replayssm_commit.argtypes = [
@@ -94,7 +96,7 @@ for _f in ("state_pool_bytes", "state_pool_create", "conv_gdn_prefill_chunked",
            "gdn_prefill_workspace_bytes", "gdn_decode_step", "track_snapshot", "restore_slots",
            "gdn_verify_tree", "gdn_accept_scatter", "replayssm_ring_bytes", "replayssm_verify",
            "replayssm_commit", "ckpt_chain_hashes", "ckpt_index_create", "ckpt_index_match",
-           "ckpt_index_release", "ckpt_index_insert", "ckpt_plan_restores"):
+           "ckpt_index_release", "ckpt_index_insert", "ckpt_plan_restores", "ckpt_finish_request"):
     getattr(_lib, _f).restype = ct.c_int
 
 
@@ -445,3 +447,12 @@ class CheckpointIndex:
                                        live.ctypes.data, ops, reach.ctypes.data, keys.ctypes.data))
         return ([(ops[i].linear_state_id, ops[i].restore_requested, ops[i].restore_src_slot_id)
                  for i in range(n)], reach[:n], keys[:n])
+
+    def finish_request(self, key, live_slot, track_slots, next_track_idx):
+        """Hand the tracked boundary's slot to the index; returns the slots to free
+        (key None: nothing was tracked)."""
+        tr = (ct.c_int32 * 2)(*[int(v) for v in track_slots])
+        freed, n = (ct.c_int32 * 4)(), ct.c_int32()
+        _check(_lib.ckpt_finish_request(self.handle, 0 if key is None else 1, 0 if key is None else int(key),
+                                        int(live_slot), tr, int(next_track_idx), freed, ct.byref(n)))
+        return [freed[i] for i in range(n.value)]

@@ -256,3 +256,28 @@ GDN_API gdn_status ckpt_plan_restores(gdn_ckpt_index_t idx, int32_t n_req, const
   }
   return gdn::clear_error();
 }
+
+GDN_API gdn_status ckpt_finish_request(gdn_ckpt_index_t idx, int32_t has_key, uint64_t key,
+                                       int32_t live_slot, const int32_t *track_slots,
+                                       int32_t next_track_idx, int32_t *freed, int32_t *n_freed) {
+  if (!idx || !track_slots || !freed || !n_freed)
+    return gdn::set_error(GDN_ERR_ARG, "a required pointer is NULL");
+  const int32_t cur = next_track_idx & 1;
+  const int32_t keep = track_slots[1 - cur];
+  int32_t n = 0;
+  auto give = [&](int32_t s) {
+    if (s > 0) freed[n++] = s;
+  };
+  give(live_slot);
+  give(track_slots[cur]);
+  if (!has_key) {
+    give(keep);
+  } else {
+    int32_t outcome = 0, back = -1;
+    const gdn_status st = ckpt_index_insert(idx, key, keep, &outcome, &back);
+    if (st != GDN_OK) return st;
+    give(back);  // an evicted slot, or the kept slot when the index did not take it
+  }
+  *n_freed = n;
+  return gdn::clear_error();
+}

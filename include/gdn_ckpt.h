@@ -98,6 +98,20 @@ gdn_status ckpt_plan_restores(gdn_ckpt_index_t idx, int32_t n_req, const int32_t
                               const int64_t *cu_tokens, int32_t stride, const int32_t *live_slots,
                               gdn_restore_op *ops, int64_t *reach, uint64_t *hit_keys);
 
+/* A request finishes (page "SGLang Mamba Radix Cache 深度解析", cache_finished_req
+ * with the ping-pong track slots): the track slot other(next) =
+ * track_slots[1 - (next_track_idx & 1)] holds the state of the last tracked
+ * boundary and is handed to the index under that boundary's recorded key,
+ * without a copy; the live slot and track_slots[next_track_idx & 1] are
+ * released.  has_key = 0 means no boundary was tracked and every slot is
+ * released.  freed (host int32 [4]) receives the slots the caller returns to
+ * its free list, *n_freed their count: the live slot, the other track slot,
+ * the kept slot when the index does not take it (key already held, or every
+ * entry pinned), and a slot the insert evicted.  Ids <= 0 are left out. */
+gdn_status ckpt_finish_request(gdn_ckpt_index_t idx, int32_t has_key, uint64_t key,
+                               int32_t live_slot, const int32_t *track_slots,
+                               int32_t next_track_idx, int32_t *freed, int32_t *n_freed);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
             "gdn_accept_scatter", "replayssm_ring_bytes", "replayssm_verify",
             "replayssm_commit", "ckpt_chain_hashes", "ckpt_index_create", "ckpt_index_destroy",
             "ckpt_index_size", "ckpt_index_contains", "ckpt_index_match", "ckpt_index_release",
-            "ckpt_index_insert", "ckpt_plan_restores"} <= set(names)
+            "ckpt_index_insert", "ckpt_plan_restores", "ckpt_finish_request"} <= set(names)
     lib = ct.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

@@ -128,3 +128,18 @@ def test_prefix_walkthrough_through_the_library(golden_dir):
         if save_key is not None:
             idx.insert(save_key, next(slots))
     assert got[:7] == spec["prefix"][:7] and got[7] == 256
+
+
+def test_finish_request_matches_the_oracle():
+    rng = np.random.default_rng(11)
+    cpp, ref = gdn.CheckpointIndex(5), ci.CheckpointIndex(5)
+    for step in range(300):
+        key = None if rng.random() < 0.2 else int(rng.integers(1, 12))
+        live = int(rng.integers(0, 40))
+        track = [int(rng.integers(0, 40)), int(rng.integers(0, 40))]
+        nxt = int(rng.integers(0, 2))
+        if rng.random() < 0.3 and len(ref):
+            k = next(iter(ref.entries))   # pin one entry now and then
+            assert cpp.match(np.array([k], dtype=np.uint64), 2, 1) == ref.match([k], 2, 1)
+        assert cpp.finish_request(key, live, track, nxt) == ci.finish_request(ref, key, live, track, nxt), step
+        assert len(cpp) == len(ref)
