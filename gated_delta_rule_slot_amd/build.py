@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdnslot.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.hip", "slot_copy.hip", "decode.hip", "prefill.hip", "verify.hip", "replay.hip"]
+SOURCES = ["api.hip", "slot_copy.hip", "decode.hip", "prefill.hip", "prefill_fused.hip", "verify.hip",
+           "replay.hip"]
 HOST_SOURCES = ["ckpt_index.cpp"]  # host-only C++ (the checkpoint index), built with g++
 CXX = os.environ.get("CXX", "g++")
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra",

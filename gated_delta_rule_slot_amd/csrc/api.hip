@@ -35,6 +35,11 @@ namespace {
 
 gdn_status ok() { return gdn::clear_error(); }
 
+// (request, head) units from which the prefill runs in one kernel by default: a
+// workgroup per unit then keeps most compute units busy, while fewer units run
+// faster on the two-kernel path, which spreads each request over its chunks.
+constexpr int64_t kOneKernelMinUnits = 128;
+
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 gdn_status check_shape(const gdn_pool_desc *d) {
@@ -139,8 +144,17 @@ GDN_API gdn_status conv_gdn_prefill_chunked(
   if (total_tokens > 0 && (!x || !out)) return fail(GDN_ERR_ARG, "x or out is NULL");
   if (alpha_mode != GDN_ALPHA_PER_HEAD && alpha_mode != GDN_ALPHA_PER_CHANNEL)
     return fail(GDN_ERR_ARG, "alpha_mode %d unknown", alpha_mode);
-  if (flags & ~uint32_t(GDN_F_L2NORM_K | GDN_F_L2NORM_Q | GDN_F_CONV_SILU))
+  if (flags & ~uint32_t(GDN_F_L2NORM_K | GDN_F_L2NORM_Q | GDN_F_CONV_SILU | GDN_F_PREFILL_ONE_KERNEL |
+                        GDN_F_PREFILL_TWO_KERNEL))
     return fail(GDN_ERR_ARG, "unknown flag bits 0x%x", flags);
+  if ((flags & GDN_F_PREFILL_ONE_KERNEL) && (flags & GDN_F_PREFILL_TWO_KERNEL))
+    return fail(GDN_ERR_ARG, "GDN_F_PREFILL_ONE_KERNEL and GDN_F_PREFILL_TWO_KERNEL both set");
+  const bool one_ok = alpha_mode == GDN_ALPHA_PER_HEAD && pool->d.head_k == 128;
+  if ((flags & GDN_F_PREFILL_ONE_KERNEL) && !one_ok)
+    return fail(GDN_ERR_UNSUPPORTED, "the one-kernel prefill serves a decay per head at head dim 128");
+  const bool one_kernel = (flags & GDN_F_PREFILL_ONE_KERNEL) ||
+                          (one_ok && !(flags & GDN_F_PREFILL_TWO_KERNEL) &&
+                           int64_t(batch) * pool->d.heads >= kOneKernelMinUnits);
   if (snap_interval < 0 || (snap_interval % gdn::kChunk) != 0)
     return fail(GDN_ERR_ARG, "snap_interval %d must be 0 or a positive multiple of 64",
                 snap_interval);
@@ -161,6 +175,9 @@ GDN_API gdn_status conv_gdn_prefill_chunked(
                      alpha,       alpha_mode,     beta,          scale,      flags,
                      out,         snap_interval,  track_slots,   next_track_idx,
                      workspace,   workspace_bytes};
+  if (one_kernel)
+    return launched(gdn::launch_prefill_fused(pool, a, static_cast<hipStream_t>(stream)),
+                    "conv_gdn_prefill_chunked launch (one kernel)");
   return launched(gdn::launch_prefill(pool, a, static_cast<hipStream_t>(stream)),
                   "conv_gdn_prefill_chunked launch");
 }

@@ -85,6 +85,27 @@ struct PrefillArgs {
   size_t workspace_bytes;
 };
 hipError_t launch_prefill(const gdn_pool *p, const PrefillArgs &a, hipStream_t s);
+hipError_t launch_prefill_fused(const gdn_pool *p, const PrefillArgs &a, hipStream_t s);
+
+// Extent of request b in a prefill call: first token, length, front padding of
+// its first 64-token chunk (chunks are aligned to absolute positions) and chunk
+// count.  ok is false when cu_seqlens or start_len is inconsistent.
+struct ReqGeom {
+  int bos, len, off, nch;
+  bool ok;
+};
+
+__device__ __forceinline__ ReqGeom req_geom(const PrefillArgs &a, int b) {
+  ReqGeom g;
+  g.bos = a.cu_seqlens[b];
+  const int eos = a.cu_seqlens[b + 1];
+  g.len = eos - g.bos;
+  const int sl = a.start_len ? a.start_len[b] : 0;
+  g.ok = g.bos >= 0 && g.len >= 0 && eos <= a.total_tokens && g.len <= a.max_seqlen && sl >= 0;
+  g.off = sl & 63;
+  g.nch = (g.ok && g.len > 0) ? (g.off + g.len + 63) / 64 : 0;
+  return g;
+}
 
 // Draft trees: nodes per request are limited so that a workgroup can hold the
 // parent list in shared memory.

@@ -1,0 +1,97 @@
+// mfma.hpp -- bf16 MFMA building blocks shared by the prefill kernels.
+//
+// Products that need about fp32 accuracy run as three bf16 MFMAs on a hi/lo split
+// of each operand (a*b ~ a_hi b_hi + a_hi b_lo + a_lo b_hi), which keeps about 16
+// significant bits with fp32 range.  CDNA4 has no single-precision-class MFMA
+// with a higher rate than this.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// An MFMA 16x16x32 operand gives lane l the k indices 8*(l/16) + e, e < 8.  Where
+// an operand is built from two 16x16 accumulator tiles (which give lane l the
+// rows 4*(l/16) + j, j < 4), its 32 k values are taken in the order
+//     pk(g, e) = 4g + e (e < 4, first tile),  16 + 4g + (e - 4) (e >= 4, second tile)
+// for g = l/16; both operands of a product use the same order, so the sum over k
+// is unchanged.
+__device__ __forceinline__ constexpr int pk(int g, int e) { return e < 4 ? 4 * g + e : 12 + 4 * g + e; }
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct Split {
+  bf16x8 hi, lo;
+};
+__device__ __forceinline__ Split split8(const float *v) {
+  Split s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = static_cast<__bf16>(v[e]);
+    s.hi[e] = h;
+    s.lo[e] = static_cast<__bf16>(v[e] - static_cast<float>(h));
+  }
+  return s;
+}
+__device__ __forceinline__ Split split44(const f32x4 &x, const f32x4 &y) {
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = x[j];
+    v[4 + j] = y[j];
+  }
+  return split8(v);
+}
+// a*b ~ a_hi b_hi + a_hi b_lo + a_lo b_hi (the lo*lo term is ~2^-16 relative)
+__device__ __forceinline__ f32x4 mfma3(const Split &a, const Split &b, f32x4 c) {
+  c = mfma_bf16(a.lo, b.hi, c);
+  c = mfma_bf16(a.hi, b.lo, c);
+  c = mfma_bf16(a.hi, b.hi, c);
+  return c;
+}
+
+// k = 16 products: lane l holds k = 4(l/16) + e of row (A) / column (B) l % 16,
+// which is exactly how a lane holds four rows of a 16x16 accumulator tile
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+struct Split4 {
+  s16x4 hi, lo;
+};
+__device__ __forceinline__ Split4 split4s(const f32x4 &v) {
+  bf16x4 h, l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const __bf16 hv = static_cast<__bf16>(v[j]);
+    h[j] = hv;
+    l[j] = static_cast<__bf16>(v[j] - static_cast<float>(hv));
+  }
+  return Split4{__builtin_bit_cast(s16x4, h), __builtin_bit_cast(s16x4, l)};
+}
+__device__ __forceinline__ f32x4 mfma3k16(const Split4 &a, const Split4 &b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ float bf16_elem(const u32x4 &v, int e) {
+  const uint32_t w = v[e >> 1];
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
+// 2^x on the hardware unit; a result below 2^-126 comes out as zero, which only
+// drops decay products that are negligible next to the unit-scale terms they join
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ void st4(float *p, const f32x4 &v) { *reinterpret_cast<f32x4 *>(p) = v; }
+
+}  // namespace gdn

@@ -82,6 +82,13 @@ enum { GDN_ALPHA_PER_HEAD = 0, GDN_ALPHA_PER_CHANNEL = 1 };
 
 /* flags */
 enum { GDN_F_L2NORM_K = 1u, GDN_F_L2NORM_Q = 2u, GDN_F_CONV_SILU = 4u };
+/* prefill path (conv_gdn_prefill_chunked only; with neither bit the library
+ * chooses): ONE_KERNEL runs each (request, head) start to end in one workgroup with
+ * the state on chip and needs no workspace beyond the minimum; it serves a decay per
+ * head (GDN_ALPHA_PER_HEAD) at head dim 128 and suits batches of many requests.
+ * TWO_KERNEL prepares every chunk in parallel and then scans them; it serves every
+ * shape and suits a few long requests. */
+enum { GDN_F_PREFILL_ONE_KERNEL = 8u, GDN_F_PREFILL_TWO_KERNEL = 16u };
 
 /* bits a kernel may set in the pool's error word (sticky; the caller clears it) */
 enum {
@@ -180,6 +187,11 @@ gdn_status gdn_prefill_workspace_bytes(gdn_pool_t pool, int32_t batch, int32_t m
  *             mamba_cache_chunk_size defaults to 64).
  * workspace   device scratch of workspace_bytes bytes, 256-byte aligned, owned by the
  *             caller and not read across calls (see gdn_prefill_workspace_bytes)
+ * flags       GDN_F_L2NORM_K | GDN_F_L2NORM_Q | GDN_F_CONV_SILU, and at most one of
+ *             GDN_F_PREFILL_ONE_KERNEL / GDN_F_PREFILL_TWO_KERNEL (ONE_KERNEL on a
+ *             shape it does not serve returns GDN_ERR_UNSUPPORTED).  Without either,
+ *             the one-kernel path runs when it serves the shape and batch * heads >= 128.
+ *             Both paths compute the same thing to the stated tolerance.
  * The live slot receives the state after the last token.  Requests of length 0
  * leave a warm slot unchanged and zero a cold one. */
 gdn_status conv_gdn_prefill_chunked(gdn_pool_t pool, int32_t layer, int32_t batch,

@@ -102,6 +102,19 @@ def test_calls_reject_bad_arguments_before_launch():
             h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0, 1, fake,
             0, None, None, fake, 16, None) == -1
         assert "workspace" in B.last_error()
+        # prefill path bits: both at once, and the one-kernel path on a decay per
+        # channel (it serves a decay per head only)
+        assert B._lib.conv_gdn_prefill_chunked(
+            h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0,
+            1 | B.PREFILL_ONE_KERNEL | B.PREFILL_TWO_KERNEL, fake, 0, None, None, fake, 1 << 30,
+            None) == -1
+        assert B._lib.conv_gdn_prefill_chunked(
+            h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 1, fake, 1.0,
+            1 | B.PREFILL_ONE_KERNEL, fake, 0, None, None, fake, 1 << 30, None) == -3
+        assert "one-kernel" in B.last_error()
+        assert B._lib.conv_gdn_prefill_chunked(
+            h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0, 1 | 32, fake,
+            0, None, None, fake, 1 << 30, None) == -1
         # layer range for copies
         assert B._lib.track_snapshot(h, 0, 2, 1, fake, fake, None) == -2
         # draft trees: node count range, required buffers, alignment of node buffers

@@ -18,8 +18,9 @@ pytestmark = pytest.mark.gpu
 
 class Case:
     def __init__(self, seed, H, D, lens, bf16=False, amode=1, slots=None, N=None, L=1,
-                 warm=None, start=None, flags=1, scale=1.0, snap=0):
+                 warm=None, start=None, flags=1, scale=1.0, snap=0, path=0):
         g = wl.generator(seed)
+        self.path = path  # GDN_F_PREFILL_* bit passed to the library only
         B = len(lens)
         self.H, self.D, self.lens, self.amode, self.flags, self.scale = H, D, lens, amode, flags, scale
         self.L = L
@@ -50,7 +51,7 @@ class Case:
             pool, self.layer, self.cu.cuda(), self.slots.cuda(), self.warm.cuda(),
             self.inp["x"].cuda(), self.w.cuda(), self.inp["alpha"].cuda(), self.amode,
             self.inp["beta"].cuda(), out, maxlen, start_len=self.start.cuda(), scale=self.scale,
-            flags=self.flags, snap_interval=self.snap, track_slots=self.track.cuda(),
+            flags=self.flags | self.path, snap_interval=self.snap, track_slots=self.track.cuda(),
             next_track_idx=self.nxt.cuda(), workspace=ws)
         torch.cuda.synchronize()
         return pool, out[:T]
@@ -127,6 +128,67 @@ def test_prefill_parity(name, kw):
     assert int(pool.err_word.item()) == 0
 
 
+ONE, TWO = 8, 16  # GDN_F_PREFILL_ONE_KERNEL, GDN_F_PREFILL_TWO_KERNEL
+
+GDN_CASES = [
+    ("fp32 ragged warm/cold, scale", dict(seed=11, H=3, D=128, lens=[1, 63, 64, 65, 130, 200],
+                                          amode=0, warm=[1, 0, 1, 1, 0, 1], scale=0.5)),
+    ("bf16 snapshots, unaligned start", dict(seed=12, H=4, D=128, lens=[300, 70, 2, 129],
+                                             bf16=True, amode=0, snap=64,
+                                             start=[64, 37, 126, 0], warm=[1, 1, 1, 0])),
+    ("fp32 silu + q norm", dict(seed=13, H=5, D=128, lens=[190, 64, 17], amode=0, flags=7)),
+    ("empty and bad slots", dict(seed=14, H=2, D=128, lens=[0, 40, 0, 33, 5],
+                                 slots=[3, 0, 4, 5, 20], warm=[1, 1, 0, 1, 1], N=20, amode=0)),
+    ("snapshots every 128 across several chunks", dict(seed=15, H=2, D=128, lens=[640, 333],
+                                                       amode=0, snap=128, start=[0, 192],
+                                                       warm=[0, 1])),
+]
+
+
+@pytest.mark.parametrize("path", [ONE, TWO], ids=["one-kernel", "two-kernel"])
+@pytest.mark.parametrize("name,kw", GDN_CASES, ids=[c[0] for c in GDN_CASES])
+def test_prefill_gdn_paths_parity(name, kw, path):
+    """Decay per head at head dim 128: each prefill path against the oracle."""
+    print(f"prefill GDN parity ({'one' if path == ONE else 'two'}-kernel): {name}", flush=True)
+    case = Case(path=path, **kw)
+    pool, out = case.run_gpu()
+    ref, o_ref, e = case.run_oracle()
+    check(case, pool, out, ref, o_ref)
+    assert int(pool.err_word.item()) == e
+
+
+def test_prefill_one_kernel_extreme_decay():
+    """Decays of 1e-3, 1e-20 and exactly 0 on the one-kernel path: finite and
+    matching (every decay factor is applied as a number <= 1)."""
+    print("prefill one-kernel extreme decay", flush=True)
+    case = Case(seed=16, H=3, D=128, lens=[150, 64, 100], amode=0, path=ONE)
+    case.inp["alpha"][:, 0] = 1e-3
+    case.inp["alpha"][40:90, 1] = 1e-20
+    case.inp["alpha"][200:210, 2] = 0.0
+    pool, out = case.run_gpu()
+    ref, o_ref, e = case.run_oracle()
+    check(case, pool, out, ref, o_ref)
+
+
+def test_prefill_one_kernel_default_choice_and_agreement():
+    """A batch of many GDN requests takes the one-kernel path by default; its
+    result equals the forced one-kernel run bit for bit and agrees with the
+    two-kernel path within the tolerance."""
+    print("prefill path choice", flush=True)
+    kw = dict(seed=17, H=16, D=128, lens=[64, 100, 37, 200, 1, 64, 129, 90], amode=0,
+              snap=64, warm=[1, 0, 1, 1, 0, 1, 1, 1])
+    d_pool, d_out = Case(**kw).run_gpu()            # 8 x 16 = 128 units: one kernel
+    o_pool, o_out = Case(path=ONE, **kw).run_gpu()
+    t_pool, t_out = Case(path=TWO, **kw).run_gpu()
+    assert torch.equal(d_out, o_out) and torch.equal(d_pool.ssm, o_pool.ssm)
+    assert torch.equal(d_pool.conv, t_pool.conv)
+    T, H, D = d_out.shape
+    a = widen(bf16_np(o_out)).reshape(T, H, D).transpose(1, 0, 2)
+    b = widen(bf16_np(t_out)).reshape(T, H, D).transpose(1, 0, 2)
+    assert worst_unit_rel_l2(a, b, 1) <= REL_L2_TOL
+    assert worst_unit_rel_l2(device_ssm_values(o_pool.ssm)[0], device_ssm_values(t_pool.ssm)[0], 2) <= REL_L2_TOL
+
+
 def test_prefill_small_workspace_windows_match_single_pass():
     """A workspace that holds one chunk per request forces many windows; the
     fp32 carry between windows makes the result identical bit for bit."""
@@ -156,13 +218,14 @@ def test_prefill_full_kda_workload():
     check(case, pool, out, ref, o_ref)
 
 
-def test_prefill_warm_gdn_subset():
+@pytest.mark.parametrize("path", [ONE, TWO], ids=["one-kernel", "two-kernel"])
+def test_prefill_warm_gdn_subset(path):
     """32 heads, K=V=128, scalar decay, fp32 pool, warm starts at a 6144
     boundary followed by ragged remainders (a sample of the prefix-hit workload)."""
-    print("prefill parity: warm GDN sample", flush=True)
+    print(f"prefill parity: warm GDN sample, path {path}", flush=True)
     cfg = wl.WARM_PREFILL
     case = Case(seed=cfg.seed, H=cfg.heads, D=cfg.head_k, lens=[1312, 700, 2048], amode=0,
-                start=[12288, 6144, 6144], warm=[1, 1, 1], N=12, snap=6144)
+                start=[12288, 6144, 6144], warm=[1, 1, 1], N=12, snap=6144, path=path)
     pool, out = case.run_gpu()
     ref, o_ref, e = case.run_oracle()
     check(case, pool, out, ref, o_ref)
