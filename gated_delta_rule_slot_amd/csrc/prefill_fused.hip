@@ -8,8 +8,7 @@
 // configuration: chunk size 64).  With G(t, i) = prod_{i < tau <= t} a_tau and
 // g_t = G(t, -1) inside a chunk whose entry state is S0:
 //     A[t][i] = G(t,i) k_t.k_i (i < t),      M[t][i] = G(t,i) q_t.k_i (i <= t)
-//     T  = (I + Diag(b) A)^-1
-//     Dl = T Diag(b) (V - Diag(g) K S0^T)                 (rows d_t)
+//     (I + Diag(b) A) Dl = Diag(b) (V - Diag(g) K S0^T)    (rows d_t)
 //     O  = Diag(g) Q S0^T + M Dl
 //     S_end = g_63 S0 + Dl^T Diag(G(63, .)) K
 // (the chunked form the oracle's tests check against the sequential one, with the
@@ -24,18 +23,20 @@
 //   P1  conv + norms of q and k (an item is 8 channels x 4 tokens) written as
 //       bf16 hi/lo MFMA fragments: K and Q (rows = tokens) and K^T (rows =
 //       channels); raw v rows staged; log2 decays (cumulated) and b (wave 0).
-//   P2  every wave forms its V values from the staged rows.  Waves 0-3: the
-//       diagonal block m = w of Diag(b) A and its inverse by forward
-//       substitution.  Waves 4-7: the M fragments and the blocks of Diag(b) A
-//       below the diagonal blocks, then their own K S0^T and Q S0^T.
-//   P3  waves 0-2: the blocks of T below the diagonal, one block column each;
-//       wave 3: the diagonal blocks; then waves 0-3: their K S0^T and Q S0^T.
-//   P4  every wave: Dl, O (stored as bf16) and the state update of its rows; a
-//       snapshot when the chunk ends on a boundary.
+//   P2  waves 0-3: the diagonal 16x16 block m = w of N = Diag(b) A and the
+//       inverse D_m of I + N_mm by forward substitution; waves 4-7: the M
+//       fragments and the blocks of N below the diagonal blocks.  Then every
+//       wave: K S0^T and Q S0^T for its rows, its V values from the staged rows,
+//       and Y = Diag(b) (V - Diag(g) K S0^T).
+//   P3  every wave: Dl for its rows by block forward substitution,
+//       Dl_m = D_m (Y_m - sum_{k<m} N_mk Dl_k), then O (staged in LDS and
+//       written out as whole rows during the next chunk) and the state update;
+//       a snapshot when the chunk ends on a boundary.
 // Every contraction runs on bf16 MFMA in the three-product hi/lo split of
 // mfma.hpp.  Accumulators enter the next product without a transpose (the k order
 // pk), and fragments in LDS are stored in operand order.
 #include "common.hpp"
+#include "lanes.hpp"
 #include "mfma.hpp"
 
 namespace gdn {
@@ -50,18 +51,23 @@ constexpr int kFThreads = 512;
 constexpr int kKN = 0;                    // K  [tb 4][ks 4][plane 2]
 constexpr int kQN = kKN + 32 * 1024;      // Q  [tb 4][ks 4][plane 2]
 constexpr int kKT = kQN + 32 * 1024;      // K^T [cb 8][ks 2][plane 2]
-constexpr int kTF = kKT + 32 * 1024;      // T  [pair 6][plane 2], pairs (tb, ks), ks <= tb/2
-constexpr int kMF = kTF + 12 * 1024;      // M  [pair 6][plane 2]
-constexpr int kLM = kMF + 12 * 1024;      // Diag(b) A blocks (m, j <= m), fp32 [10][16][kBP]
+constexpr int kMF = kKT + 32 * 1024;      // M  [pair 6][plane 2], pairs (tb, ks), ks <= tb/2
+// k = 16 A-operand fragments, split once where they are made: lane l holds row
+// l % 16, columns 4(l/16)..+3 of a 16x16 block as hi[4] | lo[4] bf16 (16 bytes)
+constexpr int kNF = kMF + 12 * 1024;      // -N_mk, blocks below the diagonal, [6][64][16 B]
+constexpr int kDF = kNF + 6 * 1024;       // D_m = (I + N_mm)^-1, [4][64][16 B]
+constexpr int kLD = kDF + 4 * 1024;       // diagonal blocks N_mm, then D_m, fp32 [4][16][kBP]
 constexpr int kBP = 20;                   // fp32 pitch of a 16x16 block row
-constexpr int kDI = kLM + 10 * 16 * kBP * 4;  // diagonal inverses, row-major [4][16][kBP]
-constexpr int kDT = kDI + 4 * 16 * kBP * 4;   // the same, transposed
-constexpr int kLB = kDT + 4 * 16 * kBP * 4;   // log2 decays L[64], then b[64]
+constexpr int kLB = kLD + 4 * 16 * kBP * 4;   // log2 decays L[64], then b[64]
 // raw v rows [67][256 B]: row i is request position p0 - 3 + i; its 16-byte
 // chunks are XOR-swizzled by 2((i >> 2) & 3), so that the four lane groups of a
 // wave, which read rows 4 apart, hit different banks
 constexpr int kXV = kLB + 128 * 4;
-constexpr int kLdsBytes = kXV + 67 * 256;
+// a chunk's outputs, bf16 [64][kOP bytes]: written in the last phase of a chunk,
+// sent out in the first phase of the next
+constexpr int kOS = kXV + 67 * 256;
+constexpr int kOP = 264;
+constexpr int kLdsBytes = kOS + 64 * kOP;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int xv_off(int row, int byte) {
@@ -69,7 +75,25 @@ __device__ __forceinline__ int xv_off(int row, int byte) {
 }
 
 __device__ __forceinline__ int pair_idx(int tb, int ks) { return tb < 2 ? tb : 2 * tb - 2 + ks; }
-__device__ __forceinline__ int lm_idx(int m, int j) { return m * (m + 1) / 2 + j; }
+
+// Operand lane l of a K or Q fragment idx (= tb * 4 + ks) is stored in slot
+// l ^ (idx & 3), and of a K^T fragment idx (= cb * 2 + ks) in slot l ^ (cb & 7).
+// The writers fill several fragments at once with lanes that would otherwise
+// share banks; the XOR spreads them, and a reader's 8-lane groups still cover
+// 8 distinct 16-byte slots.
+__device__ __forceinline__ int kn_slot(int idx, int l) { return l ^ (idx & 3); }
+__device__ __forceinline__ int kt_slot(int idx, int l) { return l ^ ((idx >> 1) & 7); }
+__device__ __forceinline__ int nf_idx(int m, int k) { return m * (m - 1) / 2 + k; }  // m > k
+
+__device__ __forceinline__ void split4_put(char *lds, int off, int lane, const f32x4 &v) {
+  const Split4 sp = split4s(v);
+  *reinterpret_cast<s16x4 *>(lds + off + lane * 16) = sp.hi;
+  *reinterpret_cast<s16x4 *>(lds + off + lane * 16 + 8) = sp.lo;
+}
+__device__ __forceinline__ Split4 split4_get(const char *lds, int off, int lane) {
+  return Split4{*reinterpret_cast<const s16x4 *>(lds + off + lane * 16),
+                *reinterpret_cast<const s16x4 *>(lds + off + lane * 16 + 8)};
+}
 
 __device__ __forceinline__ Split frag_lds(const char *lds, int off, int idx, int lane) {
   Split s;
@@ -91,22 +115,13 @@ __device__ __forceinline__ void frag_put4(char *lds, int off, int idx, int lanep
   *reinterpret_cast<bf16x4 *>(lds + off + (2 * idx + 1) * 1024 + lanep * 16 + 2 * e0) = l;
 }
 
-// one value of one fragment lane, both planes
-__device__ __forceinline__ void frag_put1(char *lds, int off, int idx, int lanep, int e, float v) {
-  const __bf16 hv = static_cast<__bf16>(v);
-  *reinterpret_cast<__bf16 *>(lds + off + (2 * idx) * 1024 + lanep * 16 + 2 * e) = hv;
-  *reinterpret_cast<__bf16 *>(lds + off + (2 * idx + 1) * 1024 + lanep * 16 + 2 * e) =
-      static_cast<__bf16>(v - static_cast<float>(hv));
-}
-
-// A 16x16 accumulator tile C[16m + 4g + j][16k + r] (lane = r + 16g) of a matrix
-// used as the A operand of a k = 32 product over its columns: element (row 4g + j,
-// column 16(k&1) + r) of pair (m, k>>1) lives in lane 4g + j + 16(r>>2), slot
-// (r&3) + 4(k&1).
-__device__ __forceinline__ void tile_to_afrag(char *lds, int off, int m, int k, int lane, const f32x4 &c) {
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) frag_put1(lds, off, pair_idx(m, k >> 1), 4 * g + j + 16 * (r >> 2), (r & 3) + 4 * (k & 1), c[j]);
+// Workgroup barrier that orders LDS accesses only: global loads issued before it
+// stay in flight (a full __syncthreads would wait for them), which lets the next
+// chunk's inputs load across the barriers of the current one.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -137,29 +152,6 @@ struct FArgs {
   int32_t *err;
   int slots, heads;
 };
-
-// One column k of T below the diagonal: T_mk = -D_m sum_{k <= j < m} N_mj T_jk with
-// N = Diag(b) A and D_m the inverse of the diagonal block, by k = 16 products;
-// each block of T enters the next as a B operand straight from its accumulator.
-template <int K>
-__device__ __forceinline__ void t_column(char *lds, int lane) {
-  const int r = lane & 15, g = lane >> 4;
-  const float *LM = reinterpret_cast<const float *>(lds + kLM);
-  const float *DI = reinterpret_cast<const float *>(lds + kDI);
-  const float *DT = reinterpret_cast<const float *>(lds + kDT);
-  Split4 tb[4];
-  tb[K] = split4s(ld4(DT + (K * 16 + r) * kBP + 4 * g));  // T_KK = D_K as a B operand
-#pragma unroll
-  for (int m = K + 1; m < 4; ++m) {
-    f32x4 p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = K; j < m; ++j) p = mfma3k16(split4s(ld4(LM + (lm_idx(m, j) * 16 + r) * kBP + 4 * g)), tb[j], p);
-    f32x4 t = mfma3k16(split4s(ld4(DI + (m * 16 + r) * kBP + 4 * g)), split4s(p), f32x4{0.f, 0.f, 0.f, 0.f});
-    t = -t;
-    if (m < 3) tb[m] = split4s(t);
-    tile_to_afrag(lds, kTF, m, K, lane, t);
-  }
-}
 
 template <typename TS>
 __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
@@ -194,18 +186,26 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
   TS *Slive = ssm + ((int64_t(a.layer) * fa.slots + slot) * H + h) * int64_t(D) * D;
   uint16_t *conv_live = fa.conv + (int64_t(a.layer) * fa.slots + slot) * kConvRows * C;
 
-  // 8 channels at request position q: the input row, the slot's conv rows before
-  // the call (warm start), or zero
-  auto row_vec = [&](int q, int64_t ch) -> u32x4 {
-    if (q >= 0 && q < rg.len) return *reinterpret_cast<const u32x4 *>(a.x + int64_t(rg.bos + q) * C + ch);
-    if (q < 0 && q >= -3 && warm) return *reinterpret_cast<const u32x4 *>(conv_live + int64_t(3 + q) * C + ch);
-    return u32x4{0u, 0u, 0u, 0u};
+  // 8 channels (from channel ch) of the input row at request position q.  The
+  // request's rows are a buffer resource, and a load whose offset lies outside
+  // its range (q < 0 or q >= len) returns zero, so no load is clamped, masked or
+  // branched around.  (The one-kernel path is only taken when len * C * 2 bytes
+  // fits a signed int.)
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.x) + int64_t(rg.bos) * C, 0, rg.len * int(C) * 2, 0x00020000);
+  auto row_x = [&](int q, int ch) -> u32x4 {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, (q * int(C) + ch) * 2, 0, 0));
+  };
+  // the same, with positions -3..-1 taken from the slot's conv rows on a warm start
+  auto row_vec = [&](int q, int ch) -> u32x4 {
+    if (q < 0 && q >= -3 && warm) return *reinterpret_cast<const u32x4 *>(conv_live + (3 + q) * C + ch);
+    return row_x(q, ch);
   };
   // the 3 conv rows of head h after `done` tokens: 144 items of 8 channels
-  auto conv_item = [&](int i, int done, int64_t &ch, int &row) -> u32x4 {
+  auto conv_item = [&](int i, int done, int &ch, int &row) -> u32x4 {
     row = i / 48;
     const int oc = i % 48;
-    ch = int64_t(oc >> 4) * H * D + int64_t(h) * D + 8 * (oc & 15);
+    ch = (oc >> 4) * H * D + h * D + 8 * (oc & 15);
     return row_vec(done - 3 + row, ch);
   };
 
@@ -256,8 +256,52 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
     snap_lo = (sl + rg.len) / a.snap_interval - sl / a.snap_interval - 2;
   }
 
-  Split yop[2];
-  f32x4 OQ[4];
+  f32x4 Y[4], OQ[4];  // per chunk: Diag(b) (V - Diag(g) K S0^T) and Diag(g) Q S0^T
+
+  // The staged outputs of the chunk at position p0 go out as 16-byte rows pieces
+  // (rows outside the request fall outside the resource and are dropped).
+  const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
+      a.out + (int64_t(rg.bos) * H + h) * D, 0, rg.len * H * D * 2, 0x00020000);
+  auto flush_out = [&](int t, int p0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int it = t + u * kFThreads, row = it >> 4, pc = it & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + kOS + row * kOP + 16 * pc);
+      __builtin_amdgcn_raw_buffer_store_b128(v, ores, ((p0 + row) * H * D + 8 * pc) * 2, 0, 0);
+    }
+  };
+
+  // Global inputs of a chunk: 7 rows of the thread's conv item, its 3 staged v
+  // chunks, and (one token per lane) the decay and b.  They are loaded one chunk
+  // ahead, during the previous chunk's last phase; nothing waits for them before
+  // the next chunk uses them.  Rows at positions -3..-1 (a warm start's conv
+  // rows) are patched in when the chunk is used.
+  u32x4 xr[7], sv[3];
+  float av, bv;
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(a.alpha) + int64_t(rg.bos) * H + h, 0, rg.len * H * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(a.beta) + int64_t(rg.bos) * H + h, 0, rg.len * H * 4, 0x00020000);
+  auto load_chunk = [&](int t, int p0) {
+    const int co = t & 15, tq = (t & 255) >> 4;
+    const int ch0 = (w >> 2) * H * D + h * D + 8 * co;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) xr[i] = row_x(p0 + 4 * tq - 3 + i, ch0);
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {  // 67 staged rows x 16 chunks of 16 bytes
+      const int it = min(t + u * kFThreads, 67 * 16 - 1);
+      sv[u] = row_x(p0 - 3 + (it >> 4), 2 * H * D + h * D + 8 * (it & 15));
+    }
+    const int toff = (p0 + (t & 63)) * H * 4;  // outside [0, len) reads zero
+    av = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ares, toff, 0, 0));
+    bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bres, toff, 0, 0));
+  };
+  load_chunk(tid, -rg.off);
+  u32x4 iw[4];  // taps of the conv item's 8 channels
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    iw[i] = *reinterpret_cast<const u32x4 *>(
+        a.conv_w + (int64_t(w >> 2) * H * D + int64_t(h) * D + 8 * (tid & 15) + 2 * i) * 4);
 
 #pragma unroll 1
   for (int c = 0; c < rg.nch; ++c) {
@@ -269,10 +313,9 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
     const int lane = tid_c & 63, r = lane & 15, g = lane >> 4, vcol = 16 * w + r;  // (shadow the call's)
     // conv item: channels 8co..8co+7 of part w / 4 (q, k), tokens 4tq..4tq+3
     const int co = tid_c & 15, tq = (tid_c & 255) >> 4;
-    const int64_t ich0 = int64_t(w >> 2) * H * D + int64_t(h) * D + 8 * co;
 
-    // Y = Diag(b) (V - Diag(g) K S0^T) as a B operand over the tokens, and
-    // Diag(g) Q S0^T, for this wave's rows; V comes from the staged raw rows
+    // Y = Diag(b) (V - Diag(g) K S0^T) and Diag(g) Q S0^T for this wave's rows;
+    // V comes from the staged raw rows
     auto ks0_products = [&](int p0) {
       f32x4 X1[4], XQ[4];
   #pragma unroll
@@ -280,16 +323,22 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
         X1[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
         XQ[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      // fragments of step i = ks * 4 + tb are read one step ahead of their products
+      Split kf[2], qf[2], sop;
+      kf[0] = frag_lds(lds, kKN, 0, kn_slot(0, lane));
+      qf[0] = frag_lds(lds, kQN, 0, kn_slot(0, lane));
   #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const Split sop = split44(S[2 * ks], S[2 * ks + 1]);
-  #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          X1[tb] = mfma3(frag_lds(lds, kKN, tb * 4 + ks, lane), sop, X1[tb]);
-          XQ[tb] = mfma3(frag_lds(lds, kQN, tb * 4 + ks, lane), sop, XQ[tb]);
+      for (int i = 0; i < 16; ++i) {
+        const int ks = i >> 2, tb = i & 3;
+        if (i + 1 < 16) {
+          const int n = ((i + 1) & 3) * 4 + ((i + 1) >> 2);
+          kf[(i + 1) & 1] = frag_lds(lds, kKN, n, kn_slot(n, lane));
+          qf[(i + 1) & 1] = frag_lds(lds, kQN, n, kn_slot(n, lane));
         }
+        if (tb == 0) sop = split44(S[2 * ks], S[2 * ks + 1]);
+        X1[tb] = mfma3(kf[i & 1], sop, X1[tb]);
+        XQ[tb] = mfma3(qf[i & 1], sop, XQ[tb]);
       }
-      f32x4 Y[4];
   #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
   #pragma unroll
@@ -307,40 +356,39 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
           OQ[tb][j] = gt * XQ[tb][j];
         }
       }
-      yop[0] = split44(Y[0], Y[1]);
-      yop[1] = split44(Y[2], Y[3]);
     };
 
 
     // ================= P1: conv, norms, fragments; staged v rows; decays =========
-    if (w == 0) {
-      const int pos = p0 + lane;
-      const bool valid = pos >= 0 && pos < rg.len;
-      float la = 0.f, bt = 0.f;
-      if (valid) {
-        const int64_t ti = int64_t(rg.bos + pos) * H + h;
-        la = fmaxf(__log2f(a.alpha[ti]), -512.f);  // a == 0: full decay
-        bt = a.beta[ti];
+    if (c > 0) flush_out(tid_c, p0 - 64);  // the previous chunk's outputs
+    if (p0 < 3 && warm) {  // rows at positions -3..-1 come from the slot's conv rows
+#pragma unroll
+      for (int i = 0; i < 7; ++i) xr[i] = row_vec(p0 + 4 * tq - 3 + i, (w >> 2) * H * D + h * D + 8 * co);
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int it = min(tid_c + u * kFThreads, 67 * 16 - 1);
+        sv[u] = row_vec(p0 - 3 + (it >> 4), 2 * H * D + h * D + 8 * (it & 15));
       }
+    }
+    const int dpos = p0 + lane;  // decays and b: wave 0, one token per lane
+    if (w == 0) {
+      const bool valid = dpos >= 0 && dpos < rg.len;
+      float la = valid ? fmaxf(__log2f(av), -512.f) : 0.f;  // a == 0: full decay
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
         const float u = __shfl_up(la, d, 64);
         if (lane >= d) la += u;
       }
       LB[lane] = la;
-      LB[64 + lane] = bt;
+      LB[64 + lane] = valid ? bv : 0.f;
     }
-    for (int it = tid; it < 67 * 16; it += kFThreads) {
-      const int row = it >> 4, oc = it & 15;
-      const u32x4 v = row_vec(p0 - 3 + row, 2 * int64_t(H) * D + int64_t(h) * D + 8 * oc);
-      *reinterpret_cast<u32x4 *>(lds + xv_off(row, 16 * oc)) = v;
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int it = tid_c + u * kFThreads;
+      if (it < 67 * 16)
+        *reinterpret_cast<u32x4 *>(lds + xv_off(it >> 4, 16 * (it & 15))) = sv[u];
     }
     {
-      u32x4 xr[7], iw[4];
-#pragma unroll
-      for (int i = 0; i < 7; ++i) xr[i] = row_vec(p0 + 4 * tq - 3 + i, ich0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) iw[i] = *reinterpret_cast<const u32x4 *>(a.conv_w + (ich0 + 2 * i) * 4);
       float y[4][8];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -359,8 +407,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
           float ss = 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) ss = fmaf(y[rr][e], y[rr][e], ss);
-#pragma unroll
-          for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+          ss = group_sum<16>(ss);
           const float inv = 1.f / sqrtf(ss + 1e-6f);
 #pragma unroll
           for (int e = 0; e < 8; ++e) y[rr][e] *= inv;
@@ -374,29 +421,50 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
         const int t = 4 * tq + rr;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
-          frag_put4(lds, fo, (t >> 4) * 4 + (co >> 2), (t & 15) + 16 * (2 * (co & 1) + hf), 4 * ((co >> 1) & 1),
-                    &y[rr][4 * hf]);
+          frag_put4(lds, fo, (t >> 4) * 4 + (co >> 2), kn_slot(co >> 2, (t & 15) + 16 * (2 * (co & 1) + hf)),
+                    4 * ((co >> 1) & 1), &y[rr][4 * hf]);
       }
       if (w >= 4) {  // K^T: rows = channels, tokens along k in the same order
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int ch = 8 * co + e;
           const float col[4] = {y[0][e], y[1][e], y[2][e], y[3][e]};
-          frag_put4(lds, kKT, (ch >> 4) * 2 + (tq >> 3), (ch & 15) + 16 * (tq & 3), 4 * ((tq >> 2) & 1), col);
+          frag_put4(lds, kKT, (ch >> 4) * 2 + (tq >> 3), kt_slot((ch >> 4) * 2, (ch & 15) + 16 * (tq & 3)),
+                    4 * ((tq >> 2) & 1), col);
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ================= P2 =======================================================
-    float *LM = reinterpret_cast<float *>(lds + kLM);
+    // a transposed M tile (lane holds M[16m+r][16k+4g+j]): decay mask, then this
+    // lane's own slot run of the M fragment
+    auto put_m = [&](int m, int k, const f32x4 &cc) {
+      const int t = 16 * m + r;
+      const float lt = LB[t];
+      float mv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 16 * k + 4 * g + j;
+        mv[j] = i <= t ? fexp2(lt - LB[i]) * cc[j] : 0.f;
+      }
+      frag_put4(lds, kMF, pair_idx(m, k >> 1), lane, 4 * (k & 1), mv);
+      if (m == k && !(m & 1)) {  // block (m, m+1) above the diagonal is zero
+        const float z[4] = {0.f, 0.f, 0.f, 0.f};
+        frag_put4(lds, kMF, pair_idx(m, m >> 1), lane, 4, z);
+      }
+    };
     if (w < 4) {
       // diagonal block m of N = Diag(b) A: lane holds k_{16m+4g+j} . k_{16m+r}
       const int m = w;
-      f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 c2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) cc = mfma3(frag_lds(lds, kKN, m * 4 + ks, lane), frag_lds(lds, kKN, m * 4 + ks, lane), cc);
-      float *blk = LM + lm_idx(m, m) * 16 * kBP;
+      for (int ks = 0; ks < 4; ++ks) {
+        const Split kf = frag_lds(lds, kKN, m * 4 + ks, kn_slot(m * 4 + ks, lane));
+        c2[ks & 1] = mfma3(kf, kf, c2[ks & 1]);
+      }
+      const f32x4 cc = c2[0] + c2[1];
+      float *blk = reinterpret_cast<float *>(lds + kLD) + m * 16 * kBP;
       const float li = LB[16 * m + r];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -413,93 +481,85 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
         for (int i = 0; i < t; ++i) v = fmaf(-blk[t * kBP + i], x[i], v);
         x[t] = v;
       }
+      // D_m over N_mm, then split once into its operand fragment
+      wave_lds_sync();
       if (g == 0) {
-        float *di = reinterpret_cast<float *>(lds + kDI) + m * 16 * kBP;
-        float *dt = reinterpret_cast<float *>(lds + kDT) + m * 16 * kBP;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) di[t * kBP + r] = x[t];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st4(dt + r * kBP + 4 * q, f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]});
+        for (int t = 0; t < 16; ++t) blk[t * kBP + r] = x[t];
       }
+      wave_lds_sync();
+      split4_put(lds, kDF + m * 1024, lane, ld4(blk + r * kBP + 4 * g));
+      // and the diagonal M tile (m, m)
+      f32x4 cm[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        cm[ks & 1] = mfma3(frag_lds(lds, kKN, m * 4 + ks, kn_slot(m * 4 + ks, lane)),
+                           frag_lds(lds, kQN, m * 4 + ks, kn_slot(m * 4 + ks, lane)), cm[ks & 1]);
+      put_m(m, m, cm[0] + cm[1]);
     } else {
-      // four tiles per wave: M blocks (m >= k) and the blocks of N below the diagonal
-      // entry (one byte per tile, wave 4 in the low bytes): type (0 = M, 1 = N) << 4
-      // | m << 2 | k.  Wave 4: M00 M10 M11 N10; 5: M20 M21 M22 N20; 6: M30 M31 N21
-      // N30; 7: M32 M33 N31 N32
-      constexpr uint64_t kTilesLo = 0x180a090814050400ull, kTilesHi = 0x1e1d0f0e1c190d0cull;
-      const uint64_t tiles = w < 6 ? kTilesLo : kTilesHi;
+      // three tiles per wave: the M blocks below the diagonal and the N blocks.
+      // Entry (one byte per tile, wave 4 first): type (0 = M, 1 = N) << 4 | m << 2 | k.
+      // Wave 4: M10 M20 N10; 5: M21 M30 N20; 6: M31 N21 N30; 7: M32 N31 N32
+      constexpr uint64_t kTilesLo = 0x190d180c09140804ull, kTilesHi = 0x1e1d0e1cull;
+      auto tile_entry = [&](int q) {
+        const int i = (w - 4) * 3 + q;
+        return int(((i < 8 ? kTilesLo >> (8 * i) : kTilesHi >> (8 * (i - 8)))) & 0xff);
+      };
+      // two tiles, then one: products first (independent accumulators), then stores
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = int((tiles >> (8 * (((w - 4) & 1) * 4 + q))) & 0xff);
+      for (int q0 = 0; q0 < 3; q0 += 2) {
+      f32x4 cc[3];
+#pragma unroll
+      for (int q = q0; q < min(q0 + 2, 3); ++q) cc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int q = q0; q < min(q0 + 2, 3); ++q) {
+          const int e = tile_entry(q);
+          const int m = (e >> 2) & 3, k = e & 3;
+          // transposed tiles: lane holds (k_{16k+4g+j} . q_{16m+r}) = M[16m+r][16k+4g+j]
+          // or (k_{16k+4g+j} . k_{16m+r}) = A[16m+r][16k+4g+j], i.e. row r and columns
+          // 4g..4g+3 of the block: this lane's own operand slots
+          const int ia = k * 4 + ks, ib = m * 4 + ks;
+          cc[q] = mfma3(frag_lds(lds, kKN, ia, kn_slot(ia, lane)),
+                        frag_lds(lds, (e >> 4) ? kKN : kQN, ib, kn_slot(ib, lane)), cc[q]);
+        }
+      }
+#pragma unroll
+      for (int q = q0; q < min(q0 + 2, 3); ++q) {
+        const int e = tile_entry(q);
         const int m = (e >> 2) & 3, k = e & 3;
-        f32x4 cc = {0.f, 0.f, 0.f, 0.f};
         if ((e >> 4) == 0) {
-          // transposed M tile: lane holds k_{16k+4g+j} . q_{16m+r} = M[16m+r][16k+4g+j],
-          // which is this lane's own slot run of the M fragment
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            cc = mfma3(frag_lds(lds, kKN, k * 4 + ks, lane), frag_lds(lds, kQN, m * 4 + ks, lane), cc);
+          put_m(m, k, cc[q]);
+        } else {  // -N_mk = -b_t G(t, i) A[t][i]
           const int t = 16 * m + r;
-          const float lt = LB[t];
-          float mv[4];
+          const float lt = LB[t], bt = LB[64 + t];
+          f32x4 nv;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = 16 * k + 4 * g + j;
-            mv[j] = i <= t ? fexp2(lt - LB[i]) * cc[j] : 0.f;
-          }
-          frag_put4(lds, kMF, pair_idx(m, k >> 1), lane, 4 * (k & 1), mv);
-          if (m == k && !(m & 1)) {  // block (m, m+1) above the diagonal is zero
-            const float z[4] = {0.f, 0.f, 0.f, 0.f};
-            frag_put4(lds, kMF, pair_idx(m, m >> 1), lane, 4, z);
-          }
-        } else {
-          // block (m, k) of N below the diagonal: lane holds k_{16m+4g+j} . k_{16k+r}
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            cc = mfma3(frag_lds(lds, kKN, m * 4 + ks, lane), frag_lds(lds, kKN, k * 4 + ks, lane), cc);
-          float *blk = LM + lm_idx(m, k) * 16 * kBP;
-          const float li = LB[16 * k + r];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int t = 16 * m + 4 * g + j;
-            blk[(4 * g + j) * kBP + r] = LB[64 + t] * fexp2(LB[t] - li) * cc[j];
-          }
+          for (int j = 0; j < 4; ++j) nv[j] = -bt * fexp2(lt - LB[16 * k + 4 * g + j]) * cc[q][j];
+          split4_put(lds, kNF + nf_idx(m, k) * 1024, lane, nv);
         }
       }
-      ks0_products(p0);
-    }
-    __syncthreads();
-
-    // ================= P3: T ====================================================
-    if (w < 4) {
-      if (w == 0) t_column<0>(lds, lane);
-      else if (w == 1) t_column<1>(lds, lane);
-      else if (w == 2) t_column<2>(lds, lane);
-      else {
-        // diagonal blocks of T are the inverses; blocks (0,1) and (2,3) are zero
-        const float *DI = reinterpret_cast<const float *>(lds + kDI);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          f32x4 d;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) d[j] = DI[(m * 16 + 4 * g + j) * kBP + r];
-          tile_to_afrag(lds, kTF, m, m, lane, d);
-        }
-        const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        frag_put4(lds, kTF, pair_idx(0, 0), lane, 4, z);
-        frag_put4(lds, kTF, pair_idx(2, 1), lane, 4, z);
       }
-      ks0_products(p0);
     }
-    __syncthreads();
+    ks0_products(p0);  // every wave, two per SIMD
+    lds_barrier();
 
-    // ================= P4: Dl, O, state update ==================================
+    // ================= P3: Dl, O, state update ==================================
+    load_chunk(tid_c, p0 + 64);  // the next chunk's inputs (clamped on the last)
+    // (I + N) Dl = Y by blocks: Dl_m = D_m (Y_m - sum_{k<m} N_mk Dl_k); each block of
+    // Dl enters the next products as a k = 16 B operand straight from its accumulator
     f32x4 Dl[4];
+    {
+      Split4 db[3];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      Dl[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < 4; ++m) {
+        f32x4 acc = Y[m];
 #pragma unroll
-      for (int ks = 0; ks <= (tb >> 1); ++ks) Dl[tb] = mfma3(frag_lds(lds, kTF, pair_idx(tb, ks), lane), yop[ks], Dl[tb]);
+        for (int k = 0; k < m; ++k) acc = mfma3k16(split4_get(lds, kNF + nf_idx(m, k) * 1024, lane), db[k], acc);
+        Dl[m] = mfma3k16(split4_get(lds, kDF + m * 1024, lane), split4s(acc), f32x4{0.f, 0.f, 0.f, 0.f});
+        if (m < 3) db[m] = split4s(Dl[m]);
+      }
     }
     const float L63 = LB[63];
     Split dop[2], dgop[2];
@@ -518,10 +578,8 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
 #pragma unroll
       for (int ks = 0; ks <= (tb >> 1); ++ks) o = mfma3(frag_lds(lds, kMF, pair_idx(tb, ks), lane), dop[ks], o);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int pos = p0 + 16 * tb + 4 * g + j;
-        if (pos >= 0 && pos < rg.len) a.out[(int64_t(rg.bos + pos) * H + h) * D + vcol] = f32_to_bf16(a.scale * o[j]);
-      }
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint16_t *>(lds + kOS + (16 * tb + 4 * g + j) * kOP + 2 * vcol) = f32_to_bf16(a.scale * o[j]);
     }
     // S^T = g_63 S0^T + K^T Diag(G(63, .)) Dl
     const float g63 = fexp2(L63);
@@ -529,7 +587,8 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
     for (int kb = 0; kb < 8; ++kb) {
       S[kb] *= g63;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) S[kb] = mfma3(frag_lds(lds, kKT, kb * 2 + ks, lane), dgop[ks], S[kb]);
+      for (int ks = 0; ks < 2; ++ks)
+        S[kb] = mfma3(frag_lds(lds, kKT, kb * 2 + ks, kt_slot(kb * 2 + ks, lane)), dgop[ks], S[kb]);
     }
 
     // snapshot at a boundary that ends this chunk
@@ -547,23 +606,22 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
           for (int kb = 0; kb < 8; ++kb) store_s4(Sd + int64_t(vcol) * D + 16 * kb + 4 * g, S[kb]);
           uint16_t *cd = fa.conv + (int64_t(a.layer) * fa.slots + dst) * kConvRows * C;
           if (tid < 144) {
-            int64_t ch;
-            int row;
+            int ch, row;
             const u32x4 v = conv_item(tid, done, ch, row);
             *reinterpret_cast<u32x4 *>(cd + row * C + ch) = v;
           }
         }
       }
     }
-    __syncthreads();  // the next chunk overwrites every fragment
+    lds_barrier();  // the next chunk overwrites every fragment
   }
 
   // ---- end of the request: live slot -------------------------------------------
+  flush_out(tid, 64 * (rg.nch - 1) - rg.off);
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) store_s4(Slive + int64_t(vcol) * D + 16 * kb + 4 * g, S[kb]);
   // read every new conv row before writing any: the old rows may be inputs
-  int64_t ch = 0;
-  int row = 0;
+  int ch = 0, row = 0;
   u32x4 nv = {0u, 0u, 0u, 0u};
   if (tid < 144) nv = conv_item(tid, rg.len, ch, row);
   __syncthreads();

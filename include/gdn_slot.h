@@ -85,7 +85,8 @@ enum { GDN_F_L2NORM_K = 1u, GDN_F_L2NORM_Q = 2u, GDN_F_CONV_SILU = 4u };
 /* prefill path (conv_gdn_prefill_chunked only; with neither bit the library
  * chooses): ONE_KERNEL runs each (request, head) start to end in one workgroup with
  * the state on chip and needs no workspace beyond the minimum; it serves a decay per
- * head (GDN_ALPHA_PER_HEAD) at head dim 128 and suits batches of many requests.
+ * head (GDN_ALPHA_PER_HEAD) at head dim 128 with max_seqlen * channels * 2 < 2^31,
+ * and suits batches of many requests.
  * TWO_KERNEL prepares every chunk in parallel and then scans them; it serves every
  * shape and suits a few long requests. */
 enum { GDN_F_PREFILL_ONE_KERNEL = 8u, GDN_F_PREFILL_TWO_KERNEL = 16u };
