@@ -273,7 +273,9 @@ def run_warm_prefill(torch, gdn, wl, dev, ws_cap=8 << 30):
     restores (deepest checkpoint strictly below the final token, so c = 6144 *
     min(2, P // 6144)), restore_slots copies them across all layers, then every
     request is prefilled from c to 13600 (cold on a miss).  Checkpoint contents
-    are random (they stand for the seed runs); one x buffer serves every layer."""
+    are random (they stand for the seed runs); one x buffer serves every layer.
+    The library's default path runs (64 x 32 (request, head) units: the one-kernel
+    prefill); the same 24 layers on the two-kernel path are timed beside it."""
     cfg = wl.WARM_PREFILL
     L, N, H, D, B, T_full = cfg.layers, cfg.slots, cfg.heads, cfg.head_k, 64, 13600
     C = H * 3 * D
@@ -339,9 +341,24 @@ def run_warm_prefill(torch, gdn, wl, dev, ws_cap=8 << 30):
     assert int(pool.err_word.item()) == 0
     t_restore = a.elapsed_time(m) / 1e3
     t_prefill = m.elapsed_time(b) / 1e3
+    # the same layers on the two-kernel path (continuing from the states just written)
+    c0, c1 = event_pair()
+    c0.record()
+    for l in range(L):
+        gdn.conv_gdn_prefill_chunked(pool, l, cu, slots, has, x, w, alpha, cfg.alpha_mode, beta, out,
+                                     max(lens), start_len=start, workspace=ws,
+                                     flags=gdn.L2NORM_K | gdn.PREFILL_TWO_KERNEL)
+    c1.record()
+    torch.cuda.synchronize()
+    t_two = c0.elapsed_time(c1) / 1e3
     n_restored = sum(1 for o in ops if o[2] >= 1)
     restore_bytes = 2 * n_restored * L * (H * D * D * 4 + 3 * C * 2)
     flops = T * L * H * 140.6e3
+    # HBM bytes of the prefill: per (token, layer) x, decay, b and out; per
+    # (request, layer) the fp32 state and the conv rows read (warm) and written
+    n_warm = sum(hist)
+    pbytes = T * L * (C * 2 + H * 4 * 2 + H * D * 2) + \
+        L * (B + n_warm) * (H * D * D * 4 + 3 * C * 2) + L * C * 8
     del pool, ssm, conv, x, out, ws
     torch.cuda.empty_cache()
     return {"workload": "prefix-hit restore + warm prefill: 64 requests x 13600 tokens, 8 prefix groups, "
@@ -350,10 +367,15 @@ def run_warm_prefill(torch, gdn, wl, dev, ws_cap=8 << 30):
             "index_plan_ms": t_plan * 1e3,
             "index_plan_us_per_request": t_plan / B * 1e6,
             "restore_GB_per_s": restore_bytes / t_restore / 1e9,
+            "prefill_path": "one kernel (library default for 2048 (request, head) units)",
             "prefill_tokens": T, "prefill_ms": t_prefill * 1e3,
             "prefill_tokens_per_s": T / t_prefill,
+            "prefill_GB_per_s": pbytes / t_prefill / 1e9,
+            "prefill_hbm_frac": pbytes / t_prefill / 1e9 / HBM_PEAK_GBS,
             "prefill_mfma_util_vs_bf16_peak": flops / t_prefill / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "workspace_bytes": ws_cap}
+            "prefill_algorithmic_bytes": pbytes,
+            "two_kernel_prefill_ms": t_two * 1e3,
+            "workspace_bytes_two_kernel": ws_cap}
 
 
 # ----------------------------------------------------------------- restore --
