@@ -91,8 +91,8 @@ struct KArgs {
   int32_t *err;
   int slots, heads;
   int c0, w, vt_count;
-  char *ws;            // workspace base
-  size_t carry_bytes;  // fp32 state carry at the start of the workspace
+  char *ws;            // workspace base: the fp32 state carry, then record windows
+  size_t rec_off;      // byte offset of this launch's record window
 };
 
 // a fragment pair (hi, lo) of a record
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
   if (!rg.ok || slot <= 0 || slot >= ka.slots || c >= rg.nch) return;
   const bool warm = a.has_initial_state[b] != 0;
   const int64_t C = int64_t(H) * 3 * D;
-  char *rec = ka.ws + ka.carry_bytes + (size_t(b * ka.w + cl) * H + h) * RC::BYTES;
+  char *rec = ka.ws + ka.rec_off + (size_t(b * ka.w + cl) * H + h) * RC::BYTES;
   const int p0 = 64 * c - rg.off;  // request position of local token 0
 
   // ---- phase 1: causal conv + norms (waves 0..11), log2 decays + beta (12..15) ----
@@ -980,7 +980,7 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
   // channel tiles (G(63,.)K, g_63)
   auto rec_rsrc = [&](int cc) {
     return __builtin_amdgcn_make_buffer_rsrc(
-        ka.ws + ka.carry_bytes + (size_t(b * ka.w + (cc - ka.c0)) * H + h) * RC::BYTES, 0, int(RC::BYTES),
+        ka.ws + ka.rec_off + (size_t(b * ka.w + (cc - ka.c0)) * H + h) * RC::BYTES, 0, int(RC::BYTES),
         0x00020000);
   };
   const int voff = lane * 16;
@@ -1186,38 +1186,56 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
 
 // ================================================================ dispatch ==
 template <int D>
+hipError_t launch_prep(const KArgs &ka, hipStream_t s) {
+  const dim3 grid(ka.a.batch * ka.w, ka.heads);
+  if (ka.a.alpha_mode == GDN_ALPHA_PER_CHANNEL)
+    hipLaunchKernelGGL((prefill_prep_kernel<D, GDN_ALPHA_PER_CHANNEL>), grid, dim3(kPrepThreads), 0, s, ka);
+  else
+    hipLaunchKernelGGL((prefill_prep_kernel<D, GDN_ALPHA_PER_HEAD>), grid, dim3(kPrepThreads), 0, s, ka);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_scan(const KArgs &ka, bool bf, hipStream_t s) {
+  const dim3 grid(unsigned(ka.a.batch) * ka.heads * ka.vt_count), block(64 * Rec<D>::NKS);
+  if (bf) hipLaunchKernelGGL((prefill_scan_kernel<D, uint16_t>), grid, block, 0, s, ka);
+  else hipLaunchKernelGGL((prefill_scan_kernel<D, float>), grid, block, 0, s, ka);
+  return hipGetLastError();
+}
+
+#define GDN_TRY(x)                        \
+  do {                                    \
+    const hipError_t e_ = (x);            \
+    if (e_ != hipSuccess) return e_;      \
+  } while (0)
+
+template <int D>
 hipError_t launch_d(const gdn_pool *p, const PrefillArgs &a, hipStream_t s) {
   const int B = a.batch, H = p->d.heads;
   const size_t rec = Rec<D>::BYTES;
   const size_t carry = (size_t(B) * H * D * D * 4 + 255) / 256 * 256;
   const int nch_max = a.start_len ? (a.max_seqlen + 126) / 64 : (a.max_seqlen + 63) / 64;
-  size_t avail = (a.workspace_bytes - carry) / (size_t(B) * H * rec);
-  int w = int(avail < size_t(nch_max) ? avail : size_t(nch_max));
-  if (w < 1) w = 1;
+  const size_t avail = (a.workspace_bytes - carry) / (size_t(B) * H * rec);  // chunks per window
   constexpr int VT = D / 16;  // one scan workgroup per 16 rows of V
   KArgs ka{a, p->d.ssm_base, static_cast<uint16_t *>(p->d.conv_base), p->d.err_word,
-           p->d.slots, H, 0, w, VT, static_cast<char *>(a.workspace), carry};
+           p->d.slots, H, 0, 1, VT, static_cast<char *>(a.workspace), carry};
   const bool bf = p->d.ssm_dtype == GDN_BF16;
+
+  // Windows on the caller's stream: as many chunks per window as the workspace
+  // holds (all of them when it is large enough).
+  int w = int(avail < size_t(nch_max) ? avail : size_t(nch_max));
+  if (w < 1) w = 1;
+  ka.w = w;
   const int rounds = nch_max > 0 ? (nch_max + w - 1) / w : 1;
   for (int rnd = 0; rnd < rounds; ++rnd) {
     ka.c0 = rnd * w;
-    if (nch_max > 0) {
-      dim3 grid(B * w, H);
-      if (a.alpha_mode == GDN_ALPHA_PER_CHANNEL)
-        hipLaunchKernelGGL((prefill_prep_kernel<D, GDN_ALPHA_PER_CHANNEL>), grid, dim3(kPrepThreads), 0, s, ka);
-      else
-        hipLaunchKernelGGL((prefill_prep_kernel<D, GDN_ALPHA_PER_HEAD>), grid, dim3(kPrepThreads), 0, s, ka);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    const dim3 grid(unsigned(B) * H * VT), block(64 * Rec<D>::NKS);
-    if (bf) hipLaunchKernelGGL((prefill_scan_kernel<D, uint16_t>), grid, block, 0, s, ka);
-    else hipLaunchKernelGGL((prefill_scan_kernel<D, float>), grid, block, 0, s, ka);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (nch_max > 0) GDN_TRY(launch_prep<D>(ka, s));
+    GDN_TRY(launch_scan<D>(ka, bf, s));
   }
   return hipSuccess;
 }
+
+#undef GDN_TRY
 
 }  // namespace
 

@@ -206,6 +206,22 @@ def test_prefill_small_workspace_windows_match_single_pass():
     check(case, p2, o2, ref, o_ref)
 
 
+def test_prefill_long_request_windows_match_single_pass():
+    """A request of 25+ chunks, per-channel decay, bf16 pool, snapshots: one window
+    for all chunks against one chunk per window (minimum workspace).  The fp32
+    carry between windows makes both bit-identical, snapshots included."""
+    print("prefill long-request windows", flush=True)
+    import gated_delta_rule_slot_amd as gdn
+    case = Case(seed=18, H=3, D=128, lens=[1500, 700, 0, 64], amode=1, bf16=True, snap=64,
+                start=[0, 128, 0, 64], warm=[0, 1, 1, 1], path=TWO)
+    p1, o1 = case.run_gpu()
+    p2, o2 = case.run_gpu(workspace_bytes=gdn.gdn_prefill_workspace_bytes(p1, 4, 64))
+    assert torch.equal(o1, o2)
+    assert torch.equal(p1.ssm, p2.ssm) and torch.equal(p1.conv, p2.conv)
+    ref, o_ref, e = case.run_oracle()
+    check(case, p1, o1, ref, o_ref)
+
+
 def test_prefill_full_kda_workload():
     """12 heads, K=V=128, one request of 6144 tokens, per-channel decay, bf16
     pool, snapshot at every 64-token boundary: checked in full."""
