@@ -27,15 +27,18 @@ namespace {
 // after the single barrier every wave has what it needs, writes back its own
 // slice of the conv rows (all old rows were read before the barrier) and runs
 // its rows to completion on its own (norms are recomputed per wave).
-// Rows per wave: kIters 16-byte vectors per lane.  Measured on MI355X for this
-// in-place read-modify-write stream: 8 beat 4 (1024-thread workgroups) and 16.
-constexpr int kIters = 8;
+// Rows per wave: 16-byte vectors per lane.  Measured on MI355X for this in-place
+// read-modify-write stream: fp32 state, 8 beat 4 (1024-thread workgroups) and 16;
+// bf16 state (KDA pool, 12 heads), 4 (8-wave workgroups, 71 VGPRs) beat 8 by 2.5%
+// and 16 by 5%.
+template <typename TS>
+constexpr int kIters = sizeof(TS) == 4 ? 8 : 4;
 template <int D, typename TS>
 struct DecodeShape {
   static constexpr int VEC = StateVec<TS>::N;
   static constexpr int LPR = D / VEC;                         // lanes per row
   static constexpr int RPI = 64 / LPR;                        // rows per load instruction
-  static constexpr int ROWS = RPI * kIters < D ? RPI * kIters : D;  // state rows per wave
+  static constexpr int ROWS = RPI * kIters<TS> < D ? RPI * kIters<TS> : D;  // state rows per wave
   static constexpr int THREADS = 64 * (D / ROWS);
   // fp32 state: 8-wave workgroups; capping registers at 6 waves per SIMD (80 VGPRs,
   // no spills) fits a third workgroup per CU, i.e. more state loads in flight
