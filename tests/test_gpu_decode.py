@@ -124,6 +124,29 @@ def test_decode_tracking_snapshots():
             assert torch.equal(pool.conv[0, t], pool.conv[0, int(slots[i])])
 
 
+def test_decode_full_size_kda_tracking_config():
+    """One layer of the 69-layer KDA decode in its launch configuration: 12 heads,
+    K=V=128, bf16 pool of 1024 slots, batch 256, per-channel decay, tracking every
+    256 tokens into ping-pong track slots with lengths ~ U[256, 8192) (about one
+    request in 256 reaches a boundary; some are forced to), checked in full."""
+    cfg = wl.KDA_DECODE
+    print("decode parity: full KDA decode-with-tracking layer", flush=True)
+    B, N = 256, cfg.slots
+    ssm, conv, w, inp, slots = _setup(cfg.seed, 1, N, cfg.heads, cfg.head_k, True, B, cfg.alpha_mode)
+    g = wl.generator(cfg.seed + 1)
+    free = [s for s in range(1, N) if s not in set(slots.tolist())]
+    track = torch.tensor(free[:2 * B], dtype=torch.int32).reshape(B, 2)
+    nxt = torch.randint(0, 2, (B,), generator=g, dtype=torch.int32)
+    seq = torch.randint(256, 8192, (B,), generator=g, dtype=torch.int32)
+    seq[::16] = 256 * torch.randint(1, 32, (B // 16,), generator=g, dtype=torch.int32)
+    pool, out, ref, o_ref, e = _run_both(ssm, conv, w, inp, slots, cfg.alpha_mode, seq_len_after=seq,
+                                         interval=256, track=track, nxt=nxt)
+    hit = [int(track[i, int(nxt[i])]) for i in range(B) if seq[i] % 256 == 0]
+    assert len(hit) >= 16
+    _assert_parity(pool, out, ref, o_ref, 0, slots.numpy(), extra_written=hit)
+    assert e == 0 and int(pool.err_word.item()) == 0
+
+
 def test_decode_skips_reserved_and_bad_slots():
     print("decode slot skipping", flush=True)
     H, D, B, N = 2, 64, 4, 16
