@@ -29,18 +29,35 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, f32
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Two floats rounded to bf16 (nearest even) by one v_cvt_pk_bf16_f32, a in the low half.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2v));
+}
+// hi = bf16(x), lo = bf16(x - hi) for a pair, as packed words (two conversions, two
+// exact widenings and two subtractions; converting one value at a time would need
+// a third instruction per pair to pack the halves)
+struct Split2 {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ Split2 split2(float a, float b) {
+  const uint32_t hi = cvt_pk_bf16(a, b);
+  return Split2{hi, cvt_pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u))};
+}
+
 struct Split {
   bf16x8 hi, lo;
 };
 __device__ __forceinline__ Split split8(const float *v) {
-  Split s;
+  u32x4 h, l;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 h = static_cast<__bf16>(v[e]);
-    s.hi[e] = h;
-    s.lo[e] = static_cast<__bf16>(v[e] - static_cast<float>(h));
+  for (int p = 0; p < 4; ++p) {
+    const Split2 q = split2(v[2 * p], v[2 * p + 1]);
+    h[p] = q.hi;
+    l[p] = q.lo;
   }
-  return s;
+  return Split{__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, l)};
 }
 __device__ __forceinline__ Split split44(const f32x4 &x, const f32x4 &y) {
   float v[8];
@@ -66,14 +83,8 @@ struct Split4 {
   s16x4 hi, lo;
 };
 __device__ __forceinline__ Split4 split4s(const f32x4 &v) {
-  bf16x4 h, l;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const __bf16 hv = static_cast<__bf16>(v[j]);
-    h[j] = hv;
-    l[j] = static_cast<__bf16>(v[j] - static_cast<float>(hv));
-  }
-  return Split4{__builtin_bit_cast(s16x4, h), __builtin_bit_cast(s16x4, l)};
+  const Split2 a = split2(v[0], v[1]), b = split2(v[2], v[3]);
+  return Split4{__builtin_bit_cast(s16x4, u32x2{a.hi, b.hi}), __builtin_bit_cast(s16x4, u32x2{a.lo, b.lo})};
 }
 __device__ __forceinline__ f32x4 mfma3k16(const Split4 &a, const Split4 &b, f32x4 c) {
   c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, c, 0, 0, 0);

@@ -437,11 +437,10 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
       }
       st4(fA + t * TP + 16 * pn + 4 * g4, av);
       bf16x4 mh, ml;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const __bf16 hv = static_cast<__bf16>(mv[j]);
-        mh[j] = hv;
-        ml[j] = static_cast<__bf16>(mv[j] - static_cast<float>(hv));
+      {
+        const Split2 a = split2(mv[0], mv[1]), b = split2(mv[2], mv[3]);
+        mh = __builtin_bit_cast(bf16x4, u32x2{a.hi, b.hi});
+        ml = __builtin_bit_cast(bf16x4, u32x2{a.lo, b.lo});
       }
       char *mf = rec + RC::MF + size_t(2 * (2 * pm + (pn >> 1))) * 1024 + lane * 16 + (pn & 1) * 8;
       *reinterpret_cast<bf16x4 *>(mf) = mh;
@@ -642,11 +641,10 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
     }
     st4(sA + t * TP + 16 * n + 4 * g4, av);
     bf16x4 mh, ml;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const __bf16 hv = static_cast<__bf16>(mv[j]);
-      mh[j] = hv;
-      ml[j] = static_cast<__bf16>(mv[j] - static_cast<float>(hv));
+    {
+      const Split2 a = split2(mv[0], mv[1]), b = split2(mv[2], mv[3]);
+      mh = __builtin_bit_cast(bf16x4, u32x2{a.hi, b.hi});
+      ml = __builtin_bit_cast(bf16x4, u32x2{a.lo, b.lo});
     }
     char *mf = rec + RC::MF + size_t(2 * (2 * m + (n >> 1))) * 1024 + lane * 16 + (n & 1) * 8;
     *reinterpret_cast<bf16x4 *>(mf) = mh;
@@ -871,12 +869,9 @@ __device__ __forceinline__ f32x4 f4_buf(__amdgpu_buffer_rsrc_t r, int voff, int 
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, byte_off, 0));
 }
 __device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const __bf16 h = static_cast<__bf16>(v[j]);
-    hi[j] = h;
-    lo[j] = static_cast<__bf16>(v[j] - static_cast<float>(h));
-  }
+  const Split2 a = split2(v[0], v[1]), b = split2(v[2], v[3]);
+  hi = __builtin_bit_cast(bf16x4, u32x2{a.hi, b.hi});
+  lo = __builtin_bit_cast(bf16x4, u32x2{a.lo, b.lo});
 }
 
 template <int D, typename TS>

@@ -104,15 +104,10 @@ __device__ __forceinline__ Split frag_lds(const char *lds, int off, int idx, int
 
 // 4 consecutive values of one fragment lane, both planes
 __device__ __forceinline__ void frag_put4(char *lds, int off, int idx, int lanep, int e0, const float *v) {
-  bf16x4 h, l;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const __bf16 hv = static_cast<__bf16>(v[j]);
-    h[j] = hv;
-    l[j] = static_cast<__bf16>(v[j] - static_cast<float>(hv));
-  }
-  *reinterpret_cast<bf16x4 *>(lds + off + (2 * idx) * 1024 + lanep * 16 + 2 * e0) = h;
-  *reinterpret_cast<bf16x4 *>(lds + off + (2 * idx + 1) * 1024 + lanep * 16 + 2 * e0) = l;
+  const Split2 a = split2(v[0], v[1]), b = split2(v[2], v[3]);
+  const u32x2 h = {a.hi, b.hi}, l = {a.lo, b.lo};
+  *reinterpret_cast<u32x2 *>(lds + off + (2 * idx) * 1024 + lanep * 16 + 2 * e0) = h;
+  *reinterpret_cast<u32x2 *>(lds + off + (2 * idx + 1) * 1024 + lanep * 16 + 2 * e0) = l;
 }
 
 // Workgroup barrier that orders LDS accesses only: global loads issued before it
