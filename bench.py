@@ -193,7 +193,8 @@ def run_kda_prefill(torch, gdn, wl, dev, reps=5):
             "tokens_per_s": T / t, "ms": t * 1e3,
             "mfma_util_vs_bf16_peak": flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "hbm_frac": byts / t / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": byts,
-            "algorithmic_flops": flops}
+            "algorithmic_flops": flops,
+            "cu_parallelism_ceiling": "serial scan over 96 chunks on 12 heads x 8 value tiles = 96 of 256 CUs"}
 
 
 # ------------------------------------------------- KDA decode with tracking --
