@@ -189,6 +189,48 @@ def test_prefill_one_kernel_default_choice_and_agreement():
     assert worst_unit_rel_l2(device_ssm_values(o_pool.ssm)[0], device_ssm_values(t_pool.ssm)[0], 2) <= REL_L2_TOL
 
 
+@pytest.mark.parametrize("path", [ONE, TWO], ids=["one-kernel", "two-kernel"])
+def test_prefill_request_over_max_seqlen_is_skipped(path):
+    """A request longer than max_seqlen sets error bit 4 and is skipped (its slot
+    and output rows untouched); the others equal the oracle run without it."""
+    import gated_delta_rule_slot_amd as gdn
+    print(f"prefill bad seqlens, path {path}", flush=True)
+    case = Case(seed=19, H=4, D=128, lens=[100, 300, 64], amode=0, warm=[1, 1, 0], path=path)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pool = gdn.state_pool_create(case.ssm.cuda(), case.conv.cuda(), err)
+    T = int(case.cu[-1])
+    out = torch.full((T, case.H, case.D), -7.0, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(pool, 3, 300), dtype=torch.uint8, device="cuda")
+    gdn.conv_gdn_prefill_chunked(pool, 0, case.cu.cuda(), case.slots.cuda(), case.warm.cuda(),
+                                 case.inp["x"].cuda(), case.w.cuda(), case.inp["alpha"].cuda(), 0,
+                                 case.inp["beta"].cuda(), out, 200, start_len=case.start.cuda(),
+                                 flags=1 | path, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 4
+    keep = [0, 2]
+    rows = torch.cat([torch.arange(0, 100), torch.arange(400, 464)])
+    ref = pool_to_oracle(case.ssm, case.conv)
+    o_ref, e = oracle.prefill(
+        ref, 0, wl.cu_seqlens([100, 64]).numpy(), case.slots[keep].numpy(),
+        wl.bf16_bits(case.inp["x"][rows]), wl.bf16_bits(case.w), case.inp["alpha"][rows].numpy(), 0,
+        case.inp["beta"][rows].numpy(), has_initial_state=case.warm[keep].numpy())
+    assert e == 0
+    got = widen(bf16_np(out[rows.cuda()])).reshape(-1, case.H, case.D)
+    want = widen(o_ref).reshape(-1, case.H, case.D)
+    eo = max(worst_unit_rel_l2(got[:100].transpose(1, 0, 2), want[:100].transpose(1, 0, 2), 1),
+             worst_unit_rel_l2(got[100:].transpose(1, 0, 2), want[100:].transpose(1, 0, 2), 1))
+    assert eo <= REL_L2_TOL, eo
+    skipped = bf16_np(out[100:400])
+    assert np.all(skipped == bf16_np(torch.full((1,), -7.0, dtype=torch.bfloat16))[0])
+    s_bad = int(case.slots[1])
+    gs = device_ssm_values(pool.ssm)
+    assert np.array_equal(gs[0, s_bad], case.ssm.double().numpy()[0, s_bad])
+    assert torch.equal(pool.conv[0, s_bad].cpu(), case.conv[0, s_bad])
+    sk = [int(case.slots[i]) for i in keep]
+    assert worst_unit_rel_l2(gs[0, sk], ssm_values(ref)[0, sk], 2) <= REL_L2_TOL
+    assert np.array_equal(bf16_np(pool.conv[0, sk]), ref.conv()[0, sk])
+
+
 def test_prefill_small_workspace_windows_match_single_pass():
     """A workspace that holds one chunk per request forces many windows; the
     fp32 carry between windows makes the result identical bit for bit."""
