@@ -593,10 +593,17 @@ def cpu_baseline(wl, seconds=10.0):
         oracle.decode_step(pool, 0, slots, x, w, a, cfg.alpha_mode, b, precision="f32")
         steps += 1
     t = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": B * steps / t, "unit": "tokens/s", "cores": oracle.num_threads("f32"),
             "kind": "oracle",
             "sample": f"{steps} GDN decode steps (128 requests x 32 heads, K=V=128, fp32) "
-                      f"of the fp32 oracle in {t:.1f} s"}
+                      f"of the fp32 oracle in {t:.1f} s",
+            "cpu": f"{model}; {os.cpu_count()} logical CPUs visible"}
 
 
 def main():
