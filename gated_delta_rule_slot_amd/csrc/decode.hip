@@ -66,7 +66,18 @@ __attribute__((amdgpu_waves_per_eu(DecodeShape<D, TS>::WAVES_PER_EU))) void gdn_
   using CV = ConvVec<CW>;
   static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "row layout");
 
-  const int h = blockIdx.x, b = blockIdx.y;
+  // workgroup -> (request, head), with consecutive heads kept on one XCD: the
+  // workgroups of a launch are dealt to the 8 XCDs in turn (XCD x runs w = x, x+8,
+  // ...), so each XCD is given its own contiguous run of (request, head) pairs,
+  // whose state blocks are adjacent in the pool.  Measured on MI355X: 2% faster for
+  // the bf16 state (32 KB per head), 0.5% for fp32.
+  const int nwg = heads * a.batch;
+  int w = blockIdx.x;
+  {
+    const int q = nwg >> 3, rm = nwg & 7, x = w & 7, i = w >> 3;
+    w = (x < rm ? x * (q + 1) : rm * (q + 1) + (x - rm) * q) + i;
+  }
+  const int h = w % heads, b = w / heads;
   const int lane = threadIdx.x & 63, part = threadIdx.x >> 6;
   const int H = heads;
   const int64_t C = int64_t(H) * 3 * D;
@@ -224,7 +235,7 @@ __attribute__((amdgpu_waves_per_eu(DecodeShape<D, TS>::WAVES_PER_EU))) void gdn_
 template <int D, typename TS>
 hipError_t launch_d(const gdn_pool *p, const DecodeArgs &a, hipStream_t s) {
   constexpr int THREADS = DecodeShape<D, TS>::THREADS;
-  dim3 grid(p->d.heads, a.batch);
+  dim3 grid(p->d.heads * a.batch);
   if (a.alpha_mode == GDN_ALPHA_PER_CHANNEL)
     hipLaunchKernelGGL((gdn_decode_kernel<D, TS, GDN_ALPHA_PER_CHANNEL>), grid, dim3(THREADS), 0, s,
                        static_cast<TS *>(p->d.ssm_base), static_cast<uint16_t *>(p->d.conv_base),
