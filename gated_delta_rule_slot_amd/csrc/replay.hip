@@ -10,14 +10,16 @@
 // with the track-interval check during the replay).  The ring also keeps each
 // position's conv input row, so the commit can advance the conv state.
 //
-// Both kernels use the decode kernel's lane layout (one workgroup per (request,
-// head), a lane owns 16-byte pieces of K-contiguous state rows, row sums with
-// DPP and row swaps) and keep the state in fp32 registers across the tokens:
-// the verify reads the live state once and stores no state at all; the commit
-// reads it once, folds every accepted token, and stores it once (and at a
-// snapshot).
+// The commit, and the verify of drafts longer than 8 tokens, use the decode
+// kernel's lane layout (one workgroup per (request, head), a lane owns 16-byte
+// pieces of K-contiguous state rows, row sums with DPP and row swaps) and keep
+// the state in fp32 registers across the tokens: the verify reads the live state
+// once and stores no state at all; the commit reads it once, folds every
+// accepted token, and stores it once (and at a snapshot).  Drafts of up to 8
+// tokens are verified in closed form on MFMA (see below).
 #include "common.hpp"
 #include "lanes.hpp"
+#include "mfma.hpp"
 
 namespace gdn {
 namespace {
@@ -393,6 +395,324 @@ __global__ __launch_bounds__((ReplayShape<D, TS>::THREADS)) void replay_commit_k
   store_to(slot);
 }
 
+// ------------------------------------------------------- verify on MFMA ----
+// A draft of T <= 8 tokens needs no per-token pass over the state.  With
+// Gam_t = prod_{s <= t} a_s and P(i, t) = prod_{i < s <= t} a_s (per channel), the
+// state after token t is S0 Diag(Gam_t) + sum_{i <= t} d_i (k_i . P(i, t))^T, so
+//     u_t = S0 (Gam_t . k_t) + sum_{i < t} A[t][i] d_i,    A[t][i] = sum_c k_i P(i, t) k_t
+//     d_t = b_t (v_t - u_t)
+//     o_t = scale (S0 (Gam_t . q_t) + sum_{i <= t} M[t][i] d_i),  M[t][i] = sum_c k_i P(i, t) q_t
+// (k and q after their normalisation).  The 2T products with S0 are one
+// [D x D] x [D x 2T] contraction per head on bf16 MFMA: the state as stored is
+// the A operand (a bf16 state exactly; an fp32 state split hi/lo), the columns
+// Gam_t . k_t and Gam_t . q_t are split hi/lo, so every product keeps about 16
+// significant bits.  The T x T coefficients A and M come from per-channel sums,
+// and each state row then solves its own T-step triangular recurrence for d.
+// Measured on MI355X (KDA pool, 12 heads, batch 256): 4 tokens 53.9 -> 33 us,
+// 8 tokens 87 -> 48 us, 1 token 28.6 -> 25 us against the token-by-token kernel;
+// at 16 tokens the token-by-token kernel was faster, so longer drafts run there.
+template <int D>
+struct MmaShape {
+  static constexpr int RB = D / 16;               // 16-row blocks of the state
+  static constexpr int KS = D / 32;               // 32-channel k slabs
+  static constexpr int WAVES = RB < 4 ? RB : 4;
+  static constexpr int RBW = RB / WAVES;          // row blocks per wave
+  static constexpr int ROWS = 16 * RBW;           // state rows per wave
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int CL = D < 64 ? D : 64;      // lanes holding channels in the per-channel steps
+  static constexpr int CPL = D / CL;              // channels per such lane
+};
+
+template <int D, typename TS, int kAlphaMode, int TMAX>
+__global__ __launch_bounds__((MmaShape<D>::THREADS)) void replay_verify_mma_kernel(
+    const TS *__restrict__ ssm, const uint16_t *__restrict__ conv, int32_t *err, int slots,
+    int heads, ReplayArgs a) {
+  using SH = MmaShape<D>;
+  constexpr int RBW = SH::RBW, KS = SH::KS, ROWS = SH::ROWS, CL = SH::CL, CPL = SH::CPL;
+  constexpr int NCOL = 2 * TMAX, NT = (NCOL + 15) / 16;  // columns: Gam.k of every token, then Gam.q
+  constexpr int HALF = D / 2;                            // two-channel conv items per part (q, k, v)
+  constexpr int ITEMS = 3 * HALF;
+  constexpr bool PERCH = kAlphaMode == GDN_ALPHA_PER_CHANNEL;
+  constexpr int NA = PERCH ? D : 1;
+  constexpr int PIECES = sizeof(TS) / 2;                 // 16-byte loads per 8 state values
+  static_assert(D % 32 == 0 && ITEMS <= SH::THREADS && SH::WAVES >= 2, "shape");
+  static_assert(HALF <= 64 && 64 % HALF == 0, "a part's conv items lie within one wave");
+
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int T = a.draft, H = heads, P = a.ring.positions;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t C = int64_t(H) * 3 * D;
+  const int slot = a.slot_table[b];
+  const int rw0 = wv * ROWS;  // first state row of this wave
+  const int64_t tok0 = int64_t(b) * T;
+
+  if (slot <= 0 || slot >= slots) {
+    for (int t = 0; t < T; ++t)
+      if (lane < ROWS) a.out[((tok0 + t) * H + h) * D + rw0 + lane] = 0;
+    if (slot >= slots && err && h == 0 && threadIdx.x == 0) atomicOr(err, GDN_ERRW_BAD_SLOT);
+    return;
+  }
+
+  // ---- loads: the small inputs of phase 1 first, then the state ------------
+  // Loads complete in issue order, so phase 1 (conv, decays, betas) and phase 2
+  // run while the state blocks are still streaming in.
+  constexpr int AL = (TMAX * NA + SH::THREADS - 1) / SH::THREADS;  // decays per thread
+  float av[AL];
+#pragma unroll
+  for (int k = 0; k < AL; ++k) {
+    const int i = int(threadIdx.x) + k * SH::THREADS;
+    av[k] = i < T * NA ? a.alpha[((tok0 + i / NA) * H + h) * NA + i % NA] : 0.f;
+  }
+  const float bv = int(threadIdx.x) < T ? a.beta[(tok0 + threadIdx.x) * H + h] : 0.f;
+  const bool conv_lane = int(threadIdx.x) < ITEMS;
+  const int item = conv_lane ? int(threadIdx.x) : 0;
+  const int pt = item / HALF, jc = (item % HALF) * 2;
+  const int64_t ch = int64_t(pt) * H * D + int64_t(h) * D + jc;
+  const uint16_t *crow = conv + (int64_t(a.layer) * slots + slot) * kConvRows * C;
+  uint32_t w0 = *reinterpret_cast<const uint32_t *>(crow + ch);
+  uint32_t w1 = *reinterpret_cast<const uint32_t *>(crow + C + ch);
+  uint32_t w2 = *reinterpret_cast<const uint32_t *>(crow + 2 * C + ch);
+  const u32x4 wt = *reinterpret_cast<const u32x4 *>(a.conv_w + ch * 4);  // taps of channels jc, jc+1
+  uint32_t xs[TMAX];
+#pragma unroll
+  for (int j = 0; j < TMAX; ++j)
+    if (j < T) xs[j] = *reinterpret_cast<const uint32_t *>(a.x + (tok0 + j) * C + ch);
+
+  // the live state as MFMA A operands: row block rb, slab ks: lane l holds row
+  // rw0 + 16 rb + l % 16, channels 32 ks + 8 (l / 16) + e, e < 8
+  const TS *S0 = ssm + ((int64_t(a.layer) * slots + slot) * H + h) * int64_t(D) * D;
+  const int fr = lane & 15, fg = lane >> 4;
+  u32x4 st[RBW][KS][PIECES];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(S0 + int64_t(rw0 + 16 * rb + fr) * D + 32 * ks + 8 * fg);
+#pragma unroll
+      for (int q = 0; q < PIECES; ++q) st[rb][ks][q] = __builtin_nontemporal_load(src + q);
+    }
+
+  const int64_t rrow = ((int64_t(a.layer) * slots + slot) * H + h) * P;  // ring row of position 0
+  uint16_t *rk = a.ring.rawk + rrow * D;
+  uint16_t *rv = a.ring.rawv + rrow * D;
+  float *rg = a.ring.g + rrow * NA;
+  float *rbt = a.ring.beta + rrow;
+  uint16_t *rx = a.ring.xrow + (int64_t(a.layer) * slots + slot) * P * C;
+
+  __shared__ __attribute__((aligned(16))) float sy[TMAX][3 * D];  // q | k | v per token
+  __shared__ float sal[TMAX][NA];
+  __shared__ float sbe[TMAX];
+  __shared__ float sinv[TMAX][2];  // 1 / |q|, 1 / |k| (1 where the norm is off)
+  __shared__ __attribute__((aligned(16))) u32x4 sB[NT][KS][2][64]; // B operands, hi | lo
+  __shared__ float sC[D][NCOL + 1];
+  __shared__ float sA[TMAX][TMAX], sM[TMAX][TMAX];
+
+  // ---- phase 1: conv of every token, ring records, decays and betas ---------
+#pragma unroll
+  for (int k = 0; k < AL; ++k) {
+    const int i = int(threadIdx.x) + k * SH::THREADS;
+    if (i < T * NA) sal[i / NA][i % NA] = av[k];
+  }
+  if (int(threadIdx.x) < T) sbe[threadIdx.x] = bv;
+#pragma unroll
+  for (int j = 0; j < TMAX; ++j) {
+    if (j >= T) break;
+    float y[2] = {0.f, 0.f};
+    if (conv_lane) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int sh = e ? 16 : 0;
+        auto pick = [&](uint32_t v) { return __uint_as_float(((v >> sh) & 0xffffu) << 16); };
+        float acc = __uint_as_float(wt[2 * e] << 16) * pick(w0);
+        acc = fmaf(__uint_as_float(wt[2 * e] & 0xffff0000u), pick(w1), acc);
+        acc = fmaf(__uint_as_float(wt[2 * e + 1] << 16), pick(w2), acc);
+        acc = fmaf(__uint_as_float(wt[2 * e + 1] & 0xffff0000u), pick(xs[j]), acc);
+        if (a.flags & GDN_F_CONV_SILU) acc = acc / (1.f + __expf(-acc));
+        y[e] = acc;
+        sy[j][pt * D + jc + e] = acc;
+      }
+      w0 = w1;
+      w1 = w2;
+      w2 = xs[j];
+    }
+    // inverse norms of q and k (a part's items are HALF adjacent lanes of one wave)
+    float ss = conv_lane && pt < 2 ? fmaf(y[0], y[0], y[1] * y[1]) : 0.f;
+    ss = group_sum<HALF>(ss);
+    if (conv_lane && pt < 2 && (item % HALF) == 0) {
+      const bool on = (a.flags & (pt == 0 ? GDN_F_L2NORM_Q : GDN_F_L2NORM_K)) != 0;
+      sinv[j][pt] = on ? 1.f / sqrtf(ss + 1e-6f) : 1.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: B operands and the T x T coefficients ------------------------
+  // B operands: thread c < D takes channel c.  Column t is Gam_t . k_t, column
+  // TMAX + t is Gam_t . q_t (zero for t >= T); channel c sits in slab c / 32 at lane
+  // 16 ((c / 8) % 4) + column % 16, element c % 8.
+  if (int(threadIdx.x) < D) {
+    const int c = threadIdx.x;
+    const int ks = c >> 5, g = (c >> 3) & 3, e = c & 7;
+    float gam = 1.f;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      float xk = 0.f, xq = 0.f;
+      if (t < T) {
+        gam *= sal[t][PERCH ? c : 0];
+        xk = gam * (sy[t][D + c] * sinv[t][1]);
+        xq = gam * (sy[t][c] * sinv[t][0]);
+      }
+      const Split2 sp = split2(xk, xq);
+      const int nk = t, nq = TMAX + t;
+      reinterpret_cast<uint16_t *>(&sB[nk / 16][ks][0][16 * g + nk % 16])[e] = uint16_t(sp.hi);
+      reinterpret_cast<uint16_t *>(&sB[nk / 16][ks][1][16 * g + nk % 16])[e] = uint16_t(sp.lo);
+      reinterpret_cast<uint16_t *>(&sB[nq / 16][ks][0][16 * g + nq % 16])[e] = uint16_t(sp.hi >> 16);
+      reinterpret_cast<uint16_t *>(&sB[nq / 16][ks][1][16 * g + nq % 16])[e] = uint16_t(sp.lo >> 16);
+    }
+  }
+  // columns 2 TMAX .. 15 of the last tile (TMAX = 4) are zero
+  if constexpr (NT * 16 > NCOL) {
+    if (wv == SH::WAVES - 1) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        if ((lane & 15) >= NCOL % 16) sB[NT - 1][ks][0][lane] = sB[NT - 1][ks][1][lane] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // A[t][i] (i < t) and M[t][i] (i <= t): the 32 lanes of group i (thread 32 i + l)
+  // take channels l, l + 32, ... (D / 32 of them; adjacent lanes read adjacent
+  // words), carry P(i, t) along t and sum each t's products over the group; the
+  // norm factors multiply the sums.
+  constexpr int CB = D / 32;
+  static_assert(TMAX % 2 == 0, "whole waves of coefficient groups (uniform trip counts)");
+  for (int u = threadIdx.x; u < 32 * TMAX; u += SH::THREADS) {
+    const int i = u >> 5, cl = u & 31;
+    const bool row = i < T;
+    float ki[CB], pr[CB];
+#pragma unroll
+    for (int m = 0; m < CB; ++m) {
+      ki[m] = row ? sy[i][D + cl + 32 * m] : 0.f;
+      pr[m] = 1.f;
+    }
+    const float kin = row ? sinv[i][1] : 0.f;
+    for (int t = 0; t < T; ++t) {  // T is uniform: every lane takes part in the sums
+      float pa = 0.f, pm = 0.f;
+#pragma unroll
+      for (int m = 0; m < CB; ++m) {
+        const int c = cl + 32 * m;
+        if (t > i) pr[m] *= sal[t][PERCH ? c : 0];
+        const float w = t >= i ? ki[m] * pr[m] : 0.f;
+        pa = fmaf(w, sy[t][D + c], pa);
+        pm = fmaf(w, sy[t][c], pm);
+      }
+      pa = group_sum<32>(pa);
+      pm = group_sum<32>(pm);
+      if (row && t >= i && cl == 0) {
+        sA[t][i] = pa * kin * sinv[t][1];
+        sM[t][i] = pm * kin * sinv[t][0];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: S0 times the 2 TMAX columns on MFMA -------------------------
+  f32x4 acc[RBW][NT];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[rb][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    Split bop[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      bop[nt].hi = __builtin_bit_cast(bf16x8, sB[nt][ks][0][lane]);
+      bop[nt].lo = __builtin_bit_cast(bf16x8, sB[nt][ks][1][lane]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      if constexpr (PIECES == 1) {  // bf16 state: exact as an operand
+        const bf16x8 av = __builtin_bit_cast(bf16x8, st[rb][ks][0]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[rb][nt] = mfma_bf16(av, bop[nt].lo, acc[rb][nt]);
+          acc[rb][nt] = mfma_bf16(av, bop[nt].hi, acc[rb][nt]);
+        }
+      } else {  // fp32 state: split hi/lo
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = __uint_as_float(st[rb][ks][0][e]);
+          v[4 + e] = __uint_as_float(st[rb][ks][1][e]);
+        }
+        const Split av = split8(v);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[rb][nt] = mfma3(av, bop[nt], acc[rb][nt]);
+      }
+    }
+  }
+  // accumulator tile (rb, nt): lane l holds column 16 nt + l % 16, rows 4 (l / 16) + j
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = 16 * nt + fr;
+      if (n < NCOL) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sC[rw0 + 16 * rb + 4 * fg + j][n] = acc[rb][nt][j];
+      }
+    }
+  __syncthreads();
+
+  // ---- the ring (stored only now: loads and stores retire in one order, so a
+  // store ahead of the MFMA phase would make it wait for the whole state) ----
+  //   k and v as they leave the conv (bf16), the conv input rows, decays, betas
+#pragma unroll
+  for (int j = 0; j < TMAX; ++j) {
+    if (j >= T) break;
+    if (conv_lane) {
+      if (pt == 1) *reinterpret_cast<uint32_t *>(rk + j * D + jc) = pack_bf16x2(sy[j][D + jc], sy[j][D + jc + 1]);
+      if (pt == 2) *reinterpret_cast<uint32_t *>(rv + j * D + jc) = pack_bf16x2(sy[j][2 * D + jc], sy[j][2 * D + jc + 1]);
+      *reinterpret_cast<uint32_t *>(rx + int64_t(j) * C + ch) = xs[j];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < AL; ++k) {
+    const int i = int(threadIdx.x) + k * SH::THREADS;
+    if (i < T * NA) rg[i] = av[k];
+  }
+  if (int(threadIdx.x) < T) rbt[threadIdx.x] = bv;
+
+  // ---- phase 4: each state row's T-step recurrence, outputs ----------------
+  if (lane < ROWS) {
+    const int r = rw0 + lane;
+    float d[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t >= T) break;
+      float u = sC[r][t];
+#pragma unroll
+      for (int i = 0; i < t; ++i) u = fmaf(sA[t][i], d[i], u);
+      d[t] = sbe[t] * (sy[t][2 * D + r] - u);
+      float o = sC[r][TMAX + t];
+#pragma unroll
+      for (int i = 0; i <= t; ++i) o = fmaf(sM[t][i], d[i], o);
+      a.out[((tok0 + t) * H + h) * D + r] = f32_to_bf16(a.scale * o);
+    }
+  }
+}
+
+template <int D, typename TS, int TMAX>
+void launch_verify_mma(const gdn_pool *p, const ReplayArgs &a, hipStream_t s) {
+  const dim3 grid(p->d.heads, a.batch), block(MmaShape<D>::THREADS);
+  const TS *ssm = static_cast<const TS *>(p->d.ssm_base);
+  const uint16_t *conv = static_cast<const uint16_t *>(p->d.conv_base);
+  if (a.ring.alpha_mode == GDN_ALPHA_PER_CHANNEL)
+    hipLaunchKernelGGL((replay_verify_mma_kernel<D, TS, GDN_ALPHA_PER_CHANNEL, TMAX>), grid, block, 0, s, ssm,
+                       conv, p->d.err_word, p->d.slots, p->d.heads, a);
+  else
+    hipLaunchKernelGGL((replay_verify_mma_kernel<D, TS, GDN_ALPHA_PER_HEAD, TMAX>), grid, block, 0, s, ssm, conv,
+                       p->d.err_word, p->d.slots, p->d.heads, a);
+}
+
 template <int D, typename TS, bool kVerify>
 hipError_t launch_r(const gdn_pool *p, const ReplayArgs &a, hipStream_t s) {
   using SH = ReplayShape<D, TS>;
@@ -401,6 +721,13 @@ hipError_t launch_r(const gdn_pool *p, const ReplayArgs &a, hipStream_t s) {
   uint16_t *conv = static_cast<uint16_t *>(p->d.conv_base);
   const bool pc = a.ring.alpha_mode == GDN_ALPHA_PER_CHANNEL;
   if (kVerify) {
+    if constexpr (D >= 32) {  // drafts of up to 8 tokens: the MFMA form
+      if (a.draft <= 8) {
+        if (a.draft <= 4) launch_verify_mma<D, TS, 4>(p, a, s);
+        else launch_verify_mma<D, TS, 8>(p, a, s);
+        return hipGetLastError();
+      }
+    }
     if (pc)
       hipLaunchKernelGGL((replay_verify_kernel<D, TS, GDN_ALPHA_PER_CHANNEL>), grid, dim3(SH::THREADS), 0, s,
                          ssm, conv, p->d.err_word, p->d.slots, p->d.heads, a);

@@ -84,6 +84,54 @@ def test_replay_verify_parity(name, seed, L, N, H, D, bf16, B, T, P, amode):
     assert torch.equal(pool.ssm.cpu(), ssm) and torch.equal(pool.conv.cpu(), conv)
 
 
+# Drafts of up to 8 tokens at head dims 32..128 run the MFMA form of the verify
+# (in two sizes: up to 4 and up to 8 tokens); longer drafts and head dim 16 run
+# the token-by-token kernel.  Both against the same oracle.
+@pytest.mark.parametrize("name,seed,H,D,bf16,B,T,P,amode,flags", [
+    ("D64 bf16 KDA T1", 91, 4, 64, True, 3, 1, 4, 1, 1),
+    ("D128 fp32 GDN T12 q-norm silu (token by token)", 92, 4, 128, False, 4, 12, 16, 0, 7),
+    ("D128 bf16 KDA T16 (token by token)", 93, 12, 128, True, 5, 16, 16, 1, 1),
+    ("D32 fp32 KDA T9 (token by token)", 94, 3, 32, False, 4, 9, 12, 1, 3),
+    ("D128 bf16 KDA T8 q-norm", 95, 6, 128, True, 6, 8, 8, 1, 3),
+    ("D128 fp32 GDN T5 q-norm silu", 90, 4, 128, False, 4, 5, 8, 0, 7),
+    ("D32 fp32 KDA T2 q-norm", 89, 3, 32, False, 4, 2, 4, 1, 3),
+    ("D128 bf16 KDA T24 (token by token)", 96, 4, 128, True, 3, 24, 32, 1, 1),
+    ("D32 fp32 GDN T64 (token by token)", 97, 2, 32, False, 2, 64, 64, 0, 1),
+    ("D16 bf16 KDA T6 (token by token)", 98, 3, 16, True, 4, 6, 8, 1, 1),
+])
+def test_replay_verify_forms(name, seed, H, D, bf16, B, T, P, amode, flags):
+    print(f"replay verify: {name}", flush=True)
+    N = 3 * B + 4
+    g, ssm, conv, w, inp, slots = _setup(seed, 1, N, H, D, bf16, B, T, amode)
+    pool, ring, out, ref, rref, o_ref, e = _verify_both(ssm, conv, w, inp, slots, B, T, P, amode, 0,
+                                                        scale=0.8, flags=flags)
+    eo = worst_unit_rel_l2(widen(bf16_np(out)), widen(o_ref), 3)
+    print(f"  worst unit rel-L2: out {eo:.2e}", flush=True)
+    assert eo <= REL_L2_TOL and e == 0 and int(pool.err_word.item()) == 0
+    _assert_ring(ring, rref, 0, slots.numpy(), T)
+    assert torch.equal(pool.ssm.cpu(), ssm) and torch.equal(pool.conv.cpu(), conv)
+
+
+@pytest.mark.parametrize("D,T", [(128, 4), (128, 8), (128, 12), (16, 3)])
+def test_replay_verify_skips_bad_slots(D, T):
+    """Slot 0 and an id past the pool skip their request (zero outputs, bit 1 for
+    the out-of-range id); the other requests match the oracle."""
+    print(f"replay verify: bad slots, D {D}, T {T}", flush=True)
+    import gated_delta_rule_slot_amd as gdn
+    B, H, N = 5, 4, 20
+    g, ssm, conv, w, inp, slots = _setup(99 + D + T, 1, N, H, D, True, B, T, 1)
+    slots[1] = 0
+    slots[3] = N + 5
+    pool, ring, out, ref, rref, o_ref, e = _verify_both(ssm, conv, w, inp, slots, B, T, T, 1, 0)
+    got = widen(bf16_np(out))
+    assert int(pool.err_word.item()) == gdn.ERRW_BAD_SLOT
+    assert not got[[1, 3]].any()
+    good = [0, 2, 4]
+    eo = worst_unit_rel_l2(got[good], widen(o_ref)[good], 3)
+    print(f"  worst unit rel-L2 (valid requests): {eo:.2e}", flush=True)
+    assert eo <= REL_L2_TOL
+
+
 def _changed(before, after):
     L, N = before.ssm().shape[:2]
     sb = before.ssm_bytes.reshape(L, N, -1) != after.ssm_bytes.reshape(L, N, -1)
