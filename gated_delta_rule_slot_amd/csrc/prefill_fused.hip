@@ -58,11 +58,13 @@ constexpr int kNF = kMF + 12 * 1024;      // -N_mk, blocks below the diagonal, [
 constexpr int kDF = kNF + 6 * 1024;       // D_m = (I + N_mm)^-1, [4][64][16 B]
 constexpr int kLD = kDF + 4 * 1024;       // diagonal blocks N_mm, then D_m, fp32 [4][16][kBP]
 constexpr int kBP = 20;                   // fp32 pitch of a 16x16 block row
-constexpr int kLB = kLD + 4 * 16 * kBP * 4;   // log2 decays L[64], then b[64]
+// per token t of the chunk: log2 decay L_t cumulated from the chunk start, b_t,
+// g_t = 2^L_t and G(63, t) = 2^(L_63 - L_t)
+constexpr int kLB = kLD + 4 * 16 * kBP * 4;
 // raw v rows [67][256 B]: row i is request position p0 - 3 + i; its 16-byte
 // chunks are XOR-swizzled by 2((i >> 2) & 3), so that the four lane groups of a
 // wave, which read rows 4 apart, hit different banks
-constexpr int kXV = kLB + 128 * 4;
+constexpr int kXV = kLB + 256 * 4;
 // a chunk's outputs, bf16 [64][kOP bytes]: written in the last phase of a chunk,
 // sent out in the first phase of the next
 constexpr int kOS = kXV + 67 * 256;
@@ -102,12 +104,29 @@ __device__ __forceinline__ Split frag_lds(const char *lds, int off, int idx, int
   return s;
 }
 
-// 4 consecutive values of one fragment lane, both planes
-__device__ __forceinline__ void frag_put4(char *lds, int off, int idx, int lanep, int e0, const float *v) {
-  const Split2 a = split2(v[0], v[1]), b = split2(v[2], v[3]);
+// a0 * b0 + a1 * b1 + c for bf16 pairs (the products are exact in fp32)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c, false);
+}
+// half h of word x (low half) and of word y (high half): one v_perm_b32
+__device__ __forceinline__ uint32_t halves(uint32_t x, uint32_t y, int h) {
+  return __builtin_amdgcn_perm(y, x, h ? 0x07060302u : 0x05040100u);
+}
+// channel e of two input rows (8 bf16 channels each) as one pair
+__device__ __forceinline__ uint32_t tok_pair(const u32x4 &r0, const u32x4 &r1, int e) {
+  return halves(r0[e >> 1], r1[e >> 1], e & 1);
+}
+
+// 4 consecutive values of one fragment lane, both planes, already split
+__device__ __forceinline__ void frag_put4w(char *lds, int off, int idx, int lanep, int e0, const Split2 &a,
+                                           const Split2 &b) {
   const u32x2 h = {a.hi, b.hi}, l = {a.lo, b.lo};
   *reinterpret_cast<u32x2 *>(lds + off + (2 * idx) * 1024 + lanep * 16 + 2 * e0) = h;
   *reinterpret_cast<u32x2 *>(lds + off + (2 * idx + 1) * 1024 + lanep * 16 + 2 * e0) = l;
+}
+__device__ __forceinline__ void frag_put4(char *lds, int off, int idx, int lanep, int e0, const float *v) {
+  frag_put4w(lds, off, idx, lanep, e0, split2(v[0], v[1]), split2(v[2], v[3]));
 }
 
 // Workgroup barrier that orders LDS accesses only: global loads issued before it
@@ -152,7 +171,7 @@ template <typename TS>
 __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
   constexpr int D = kFD;
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  float *LB = reinterpret_cast<float *>(lds + kLB);  // L[0..63], b[64..127]
+  float *LB = reinterpret_cast<float *>(lds + kLB);  // L, b, g, G(63, .): 64 each
 
   const PrefillArgs &a = fa.a;
   const int H = fa.heads;
@@ -223,14 +242,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
   const bool inorm = (a.flags & (w < 4 ? GDN_F_L2NORM_Q : GDN_F_L2NORM_K)) != 0;
   // taps of this lane's V column
   const int vcol = 16 * w + r;
-  float vw[4];
-  {
-    const u32x2 u = *reinterpret_cast<const u32x2 *>(a.conv_w + (2 * int64_t(H) * D + int64_t(h) * D + vcol) * 4);
-    vw[0] = __uint_as_float(u[0] << 16);
-    vw[1] = __uint_as_float(u[0] & 0xffff0000u);
-    vw[2] = __uint_as_float(u[1] << 16);
-    vw[3] = __uint_as_float(u[1] & 0xffff0000u);
-  }
+  const u32x2 vw = *reinterpret_cast<const u32x2 *>(a.conv_w + (2 * int64_t(H) * D + int64_t(h) * D + vcol) * 4);
 
   // ---- state: lane (r, g) of wave w holds S[16w + r][16kb + 4g + j] in S[kb][j] ----
   f32x4 S[8];
@@ -336,17 +348,22 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
       }
   #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
+        // staged rows t0 .. t0 + 6 of this lane's V column, as pairs of adjacent rows
+        const int t0 = 16 * tb + 4 * g;
+        uint32_t xc[7], xp[6];
+  #pragma unroll
+        for (int q = 0; q < 7; ++q) xc[q] = *reinterpret_cast<const uint16_t *>(lds + xv_off(t0 + q, 2 * vcol));
+  #pragma unroll
+        for (int q = 0; q < 6; ++q) xp[q] = halves(xc[q], xc[q + 1], 0);
   #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int t = 16 * tb + 4 * g + j;
-          float acc = vw[0] * bf16_to_f32(*reinterpret_cast<const uint16_t *>(lds + xv_off(t, 2 * vcol)));
-  #pragma unroll
-          for (int q = 1; q < 4; ++q)
-            acc = fmaf(vw[q], bf16_to_f32(*reinterpret_cast<const uint16_t *>(lds + xv_off(t + q, 2 * vcol))), acc);
+          const int t = t0 + j;
+          float acc = dot2_bf16(vw[0], xp[j], 0.f);
+          acc = dot2_bf16(vw[1], xp[j + 2], acc);
           if (silu) acc = acc / (1.f + __expf(-acc));
           const int pos = p0 + t;
           const float v = (pos >= 0 && pos < rg.len) ? acc : 0.f;
-          const float gt = fexp2(LB[t]);
+          const float gt = LB[128 + t];
           Y[tb][j] = LB[64 + t] * (v - gt * X1[tb][j]);
           OQ[tb][j] = gt * XQ[tb][j];
         }
@@ -376,6 +393,8 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
       }
       LB[lane] = la;
       LB[64 + lane] = valid ? bv : 0.f;
+      LB[128 + lane] = fexp2(la);
+      LB[192 + lane] = fexp2(__shfl(la, 63, 64) - la);
     }
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
@@ -391,10 +410,9 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
         const bool valid = pos >= 0 && pos < rg.len;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          // tap j multiplies position pos - 3 + j
-          float acc = bf16_elem(iw[e >> 1], 4 * (e & 1)) * bf16_elem(xr[rr], e);
-#pragma unroll
-          for (int j = 1; j < 4; ++j) acc = fmaf(bf16_elem(iw[e >> 1], 4 * (e & 1) + j), bf16_elem(xr[rr + j], e), acc);
+          // taps (0, 1) and (2, 3) multiply positions (pos - 3, pos - 2) and (pos - 1, pos)
+          float acc = dot2_bf16(iw[e >> 1][2 * (e & 1)], tok_pair(xr[rr], xr[rr + 1], e), 0.f);
+          acc = dot2_bf16(iw[e >> 1][2 * (e & 1) + 1], tok_pair(xr[rr + 2], xr[rr + 3], e), acc);
           if (silu) acc = acc / (1.f + __expf(-acc));
           y[rr][e] = valid ? acc : 0.f;
         }
@@ -410,22 +428,28 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
       }
       // rows = tokens: element (t, 32ks + p) of fragment (t>>4, ks) sits in lane
       // (t&15) + 16((p&15)>>2), slot (p&3) + 4(p>>4)
+      // each value is split once (pairs of adjacent channels); K^T takes the same
+      // bf16 halves regrouped into pairs of adjacent tokens
       const int fo = w < 4 ? kQN : kKN;
+      Split2 sp[4][4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int t = 4 * tq + rr;
 #pragma unroll
+        for (int p = 0; p < 4; ++p) sp[rr][p] = split2(y[rr][2 * p], y[rr][2 * p + 1]);
+#pragma unroll
         for (int hf = 0; hf < 2; ++hf)
-          frag_put4(lds, fo, (t >> 4) * 4 + (co >> 2), kn_slot(co >> 2, (t & 15) + 16 * (2 * (co & 1) + hf)),
-                    4 * ((co >> 1) & 1), &y[rr][4 * hf]);
+          frag_put4w(lds, fo, (t >> 4) * 4 + (co >> 2), kn_slot(co >> 2, (t & 15) + 16 * (2 * (co & 1) + hf)),
+                     4 * ((co >> 1) & 1), sp[rr][2 * hf], sp[rr][2 * hf + 1]);
       }
       if (w >= 4) {  // K^T: rows = channels, tokens along k in the same order
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int ch = 8 * co + e;
-          const float col[4] = {y[0][e], y[1][e], y[2][e], y[3][e]};
-          frag_put4(lds, kKT, (ch >> 4) * 2 + (tq >> 3), kt_slot((ch >> 4) * 2, (ch & 15) + 16 * (tq & 3)),
-                    4 * ((tq >> 2) & 1), col);
+          const int ch = 8 * co + e, p = e >> 1, hh = e & 1;
+          const Split2 t01{halves(sp[0][p].hi, sp[1][p].hi, hh), halves(sp[0][p].lo, sp[1][p].lo, hh)};
+          const Split2 t23{halves(sp[2][p].hi, sp[3][p].hi, hh), halves(sp[2][p].lo, sp[3][p].lo, hh)};
+          frag_put4w(lds, kKT, (ch >> 4) * 2 + (tq >> 3), kt_slot((ch >> 4) * 2, (ch & 15) + 16 * (tq & 3)),
+                     4 * ((tq >> 2) & 1), t01, t23);
         }
       }
     }
@@ -556,14 +580,13 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
         if (m < 3) db[m] = split4s(Dl[m]);
       }
     }
-    const float L63 = LB[63];
     Split dop[2], dgop[2];
     dop[0] = split44(Dl[0], Dl[1]);
     dop[1] = split44(Dl[2], Dl[3]);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Dl[tb][j] *= fexp2(L63 - LB[16 * tb + 4 * g + j]);  // G(63, t) Dl
+      for (int j = 0; j < 4; ++j) Dl[tb][j] *= LB[192 + 16 * tb + 4 * g + j];  // G(63, t) Dl
     dgop[0] = split44(Dl[0], Dl[1]);
     dgop[1] = split44(Dl[2], Dl[3]);
     // outputs
@@ -577,7 +600,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
         *reinterpret_cast<uint16_t *>(lds + kOS + (16 * tb + 4 * g + j) * kOP + 2 * vcol) = f32_to_bf16(a.scale * o[j]);
     }
     // S^T = g_63 S0^T + K^T Diag(G(63, .)) Dl
-    const float g63 = fexp2(L63);
+    const float g63 = LB[128 + 63];
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
       S[kb] *= g63;
