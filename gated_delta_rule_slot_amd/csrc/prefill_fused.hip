@@ -421,7 +421,9 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) ss = fmaf(y[rr][e], y[rr][e], ss);
           ss = group_sum<16>(ss);
-          const float inv = 1.f / sqrtf(ss + 1e-6f);
+          // v_rsq_f32 (about 1 ulp): a full-precision square root and division here
+          // held the k waves ~1.2k cycles per chunk behind the q waves at the barrier
+          const float inv = __builtin_amdgcn_rsqf(ss + 1e-6f);
 #pragma unroll
           for (int e = 0; e < 8; ++e) y[rr][e] *= inv;
         }
