@@ -44,6 +44,7 @@ namespace {
 
 constexpr int kFD = 128;      // head dim K = V
 constexpr int kFThreads = 512;
+constexpr int kOrderedBatch = 1024;  // batches up to this size are taken longest request first
 
 // ---------------------------------------------------------------- LDS layout --
 // A fragment is one bf16 plane (hi or lo) of one 16x16x32 operand: 64 lanes x 8
@@ -175,8 +176,26 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
 
   const PrefillArgs &a = fa.a;
   const int H = fa.heads;
-  const int b = blockIdx.x / H, h = blockIdx.x % H;
+  const int h = blockIdx.x % H;
   const int tid = threadIdx.x, lane = tid & 63;
+  // Requests are taken longest first (most chunks; ties by index): workgroups
+  // start in index order, so a long request that came late would keep its CU
+  // busy after the others finish.  Every workgroup ranks the batch itself.
+  int b = blockIdx.x / H;
+  if (a.batch <= kOrderedBatch) {
+    __shared__ int s_req;
+    for (int i = tid; i < a.batch; i += kFThreads) {
+      const int ni = req_geom(a, i).nch;
+      int rank = 0;
+      for (int j = 0; j < a.batch; ++j) {
+        const int nj = req_geom(a, j).nch;
+        rank += (nj > ni) | ((nj == ni) & (j < i));
+      }
+      if (rank == b) s_req = i;
+    }
+    __syncthreads();
+    b = s_req;
+  }
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
 
