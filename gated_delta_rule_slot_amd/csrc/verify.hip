@@ -324,7 +324,13 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 1))) void gdn_verify_kernel(
         if (carry) cur[it] = w;
         else if (regroup)
           cur[it] = __builtin_bit_cast(SR, __builtin_amdgcn_raw_buffer_load_b128(nsrc, loff, it * kPieceStep, 0));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), dst, loff, it * kPieceStep, 2);
+        // The piece offset goes into the lane offset, not the scalar offset: a
+        // 16-byte buffer store reads its data registers over several cycles, and
+        // the compiler keeps an overwriting instruction away from them only when
+        // the scalar offset is not a register.  With a register scalar offset the
+        // next instruction was allowed to overwrite the first data register, and
+        // under a full launch some lanes stored that new value.
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), dst, loff + it * kPieceStep, 0, 2);
         // every lane of the row stores the same value: no divergent branch
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(a.scale * fmaf(d, kq, pq)), orow, r * 2, 0, 0);
       }

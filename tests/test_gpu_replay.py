@@ -195,3 +195,58 @@ def test_replay_commit_flags_bad_input():
                          next_track_idx=torch.zeros(B, dtype=torch.int32).cuda())
     torch.cuda.synchronize()
     assert int(pool.err_word.item()) == gdn.ERRW_BAD_SLOT | gdn.ERRW_BAD_TRACK_SLOT
+
+
+def test_replay_full_size_round_sampled():
+    """The benchmark's ReplaySSM launches on one layer of the KDA pool (12 heads,
+    K = V = 128, bf16 state, 1024 slots, per-channel decay): verify of 4-token
+    draft chains for 256 requests into a 16-position ring, then the commit of 1..4
+    accepted tokens with tracking every 256.  The GPU runs the whole launches;
+    three requests (one whose replay crosses a multiple of 256) are checked
+    against the oracle."""
+    import gated_delta_rule_slot_amd as gdn
+    print("replay: full-size round, sampled requests", flush=True)
+    H, D, N, B, T, P, amode = 12, 128, 1024, 256, 4, 16, 1
+    C = H * 3 * D
+    g, ssm, conv, w, inp, _ = _setup(107, 1, N, H, D, True, B, T, amode)
+    ids = wl.distinct_slots(g, 3 * B, N)
+    slots, track = ids[:B].contiguous(), ids[B:].reshape(B, 2).contiguous()
+    accepted = torch.randint(1, T + 1, (B,), generator=g, dtype=torch.int32)
+    before = torch.randint(256, 8192, (B,), generator=g, dtype=torch.int32)
+    nxt = torch.randint(0, 2, (B,), generator=g, dtype=torch.int32)
+    sample = [0, 137, 255]
+    accepted[137], before[137] = 4, 1022   # the replay reaches 1024 at its second token
+    x = inp["x"].reshape(B, T, C).contiguous()
+    a = inp["alpha"].reshape(B, T, H, D).contiguous()
+    bt = inp["beta"].reshape(B, T, H).contiguous()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pool = gdn.state_pool_create(ssm.cuda(), conv.cuda(), err)
+    ring = gdn.ReplayRing(pool, P, amode)
+    out = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    gdn.replayssm_verify(pool, ring, 0, slots.cuda(), x.cuda(), w.cuda(), a.cuda(), bt.cuda(), out)
+    gdn.replayssm_commit(pool, ring, 0, slots.cuda(), accepted.cuda(), seq_len_before=before.cuda(),
+                         track_interval=256, track_slots=track.cuda(), next_track_idx=nxt.cuda())
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+
+    ref = pool_to_oracle(ssm, conv)
+    rref = oracle.Ring(ref, P, amode)
+    o_ref, e = oracle.replay_verify(ref, rref, 0, slots.numpy()[sample], wl.bf16_bits(x)[sample],
+                                    wl.bf16_bits(w), a.numpy()[sample], amode, bt.numpy()[sample])
+    assert e == 0
+    eo = worst_unit_rel_l2(widen(bf16_np(out[sample])), widen(o_ref), 3)
+    ref0 = ref.copy()
+    e2 = oracle.replay_commit(ref, rref, 0, slots.numpy()[sample], accepted.numpy()[sample], amode,
+                              seq_len_before=before.numpy()[sample], track_interval=256,
+                              track_slots=track.numpy()[sample], next_track_idx=nxt.numpy()[sample])
+    assert e2 == 0
+    # the sampled live slots and both of their track slots, on both sides
+    checked = sorted(set(slots.numpy()[sample].tolist()) | set(track.numpy()[sample].ravel().tolist()))
+    want_changed = {n for (_, n) in _changed(ref0, ref)}
+    assert set(slots.numpy()[sample].tolist()) <= want_changed and len(want_changed) >= 4  # + a track slot
+    gpu_ssm = pool.ssm[0, checked].cpu()
+    gpu_conv = bf16_np(pool.conv[0, checked].cpu())
+    es = worst_unit_rel_l2(gpu_ssm.to(torch.float64).numpy(), widen(ref.ssm()[0, checked]), 2)
+    print(f"  worst unit rel-L2: out {eo:.2e}  committed state {es:.2e}", flush=True)
+    assert eo <= REL_L2_TOL and es <= REL_L2_TOL
+    assert np.array_equal(gpu_conv, ref.conv()[0, checked])

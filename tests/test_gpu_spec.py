@@ -230,3 +230,43 @@ def test_accept_scatter_flags_bad_input():
     torch.cuda.synchronize()
     assert int(pool.err_word.item()) == gdn.ERRW_BAD_TRACK_SLOT
     assert torch.equal(pool.ssm[0, s[1]], ns[1, 2])
+
+
+def test_verify_full_size_tree_sampled():
+    """The benchmark's draft-tree verify launch: 32 requests, a 63-node breadth-first
+    tree of topk 4, 32 heads, K = V = 128, bf16 state, decay per head.  The GPU runs
+    the whole launch; two requests are checked against the oracle (requests are
+    independent, so the oracle takes only those)."""
+    import gated_delta_rule_slot_amd as gdn
+    print("verify: full-size tree launch, sampled requests", flush=True)
+    B, T, H, D = 32, 63, 32, 128
+    N, C = 1 + 3 * B, H * 3 * D
+    g, ssm, conv, w, inp, slots = _spec_inputs(106, 1, N, H, D, True, B, T, 0)
+    parent = torch.tensor([bfs_forest(4, T)] * B, dtype=torch.int32)
+    x = inp["x"].reshape(B, T, C).contiguous()
+    a = inp["alpha"].reshape(B, T, H).contiguous()
+    bt = inp["beta"].reshape(B, T, H).contiguous()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pool = gdn.state_pool_create(ssm.cuda(), conv.cuda(), err)
+    out = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    ns = torch.empty((B, T, H, D, D), dtype=torch.bfloat16, device="cuda")
+    nc = torch.empty((B, T, 3, C), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_verify_tree(pool, 0, slots.cuda(), parent.cuda(), x.cuda(), w.cuda(), a.cuda(), 0, bt.cuda(),
+                        out, ns, nc)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    sample = [5, 30]
+    ref = pool_to_oracle(ssm, conv)
+    o_ref, ns_ref, nc_ref, e = oracle.verify_tree(
+        ref, 0, slots.numpy()[sample], parent.numpy()[sample], wl.bf16_bits(x)[sample], wl.bf16_bits(w),
+        a.numpy()[sample], 0, bt.numpy()[sample])
+    assert e == 0
+    eo = worst_unit_rel_l2(widen(bf16_np(out[sample])), widen(o_ref), 3)
+    es = 0.0
+    for i, b in enumerate(sample):  # node by node, to keep the host copies small
+        for n in range(T):
+            got = ns[b, n].cpu().to(torch.float64).numpy()
+            es = max(es, worst_unit_rel_l2(got, widen(ns_ref[i, n]), 1))
+    print(f"  worst unit rel-L2: out {eo:.2e}  node state {es:.2e}", flush=True)
+    assert eo <= REL_L2_TOL and es <= REL_L2_TOL
+    assert np.array_equal(bf16_np(nc[sample]), nc_ref)
