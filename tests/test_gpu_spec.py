@@ -13,8 +13,8 @@ import torch
 
 import oracle
 import workloads as wl
-from tests.helpers import (REL_L2_TOL, bf16_np, device_ssm_values, pool_to_oracle, ssm_values,
-                           widen, worst_unit_rel_l2)
+from tests.helpers import (REL_L2_TOL, bf16_np, device_ssm_values, pool_bytes_equal, pool_to_oracle,
+                           ssm_values, widen, worst_unit_rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -270,3 +270,25 @@ def test_verify_full_size_tree_sampled():
     print(f"  worst unit rel-L2: out {eo:.2e}  node state {es:.2e}", flush=True)
     assert eo <= REL_L2_TOL and es <= REL_L2_TOL
     assert np.array_equal(bf16_np(nc[sample]), nc_ref)
+
+    # the benchmark's commit of that launch (a depth-3 node per request, tracking every
+    # 256; three requests cross a multiple of 256 at depths 1, 2 and 3): the pool must
+    # equal, byte for byte, what the oracle's scatter makes of the GPU's node buffers
+    used = set(slots.tolist())
+    track = torch.tensor([s for s in range(1, N) if s not in used][:2 * B], dtype=torch.int32).reshape(B, 2)
+    accepted = torch.randint(4 + 16, T, (B,), generator=g, dtype=torch.int32)
+    before = torch.randint(256, 8192, (B,), generator=g, dtype=torch.int32)
+    before[0], before[1], before[2] = 255, 510, 1021
+    nxt = torch.zeros(B, dtype=torch.int32)
+    ref2 = pool_to_oracle(pool.ssm, pool.conv)
+    gdn.gdn_accept_scatter(pool, 0, slots.cuda(), parent.cuda(), accepted.cuda(), ns, nc,
+                           seq_len_before=before.cuda(), track_interval=256, track_slots=track.cuda(),
+                           next_track_idx=nxt.cuda())
+    e3 = oracle.accept_scatter(ref2, 0, slots.numpy(), parent.numpy(), accepted.numpy(), bf16_np(ns),
+                               bf16_np(nc), seq_len_before=before.numpy(), track_interval=256,
+                               track_slots=track.numpy(), next_track_idx=nxt.numpy())
+    torch.cuda.synchronize()
+    assert e3 == 0 and int(err.item()) == 0
+    assert pool_bytes_equal(pool.ssm, pool.conv, ref2)
+    # the first crossing of requests 0..2 goes to track slot (next_track_idx + 0) & 1 = 0
+    assert {(0, int(track[i, 0])) for i in range(3)} <= _changed_slots(pool_to_oracle(ssm, conv), ref2)
