@@ -81,3 +81,34 @@ def test_restore_across_many_ops_and_layers():
     torch.cuda.synchronize()
     assert got == want.tolist() == [1] * 300
     assert pool_bytes_equal(pool.ssm, pool.conv, ref)
+
+
+def test_restore_full_size_workload():
+    """The benchmark's restore launch: 35 requests restored across all 24 layers of a
+    32-head, K = V = 128 fp32 pool of 81 slots (2 MiB of state and 72 KiB of conv rows
+    per layer and slot) from 16 checkpoint slots, plus a requested restore without a
+    source, one onto its own slot and one not requested.  Every copied (layer, slot)
+    equals its source byte for byte and every other slot is untouched (checked on the
+    device); the outcomes are the oracle's, whose rules do not depend on the state's
+    size (a one-head pool of the same slot count decides them)."""
+    import gated_delta_rule_slot_amd as gdn
+    print("restore: full-size launch", flush=True)
+    cfg = wl.WARM_PREFILL
+    L, N, H, D = cfg.layers, cfg.slots, cfg.heads, cfg.head_k
+    C = 3 * H * D
+    gd = torch.Generator(device="cuda")
+    gd.manual_seed(91)
+    ssm = torch.empty(L, N, H, D, D, dtype=torch.float32, device="cuda").normal_(generator=gd)
+    conv = torch.empty(L, N, 3, C, dtype=torch.float32, device="cuda").normal_(generator=gd).to(torch.bfloat16)
+    ssm0, conv0 = ssm.clone(), conv.clone()
+    pool = gdn.state_pool_create(ssm, conv, torch.zeros(1, dtype=torch.int32, device="cuda"))
+    ops = [(1 + i, 1, 65 + (i % 16)) for i in range(35)] + [(40, 1, -1), (41, 1, 41), (42, 0, 70)]
+    got = gdn.restore_slots(pool, ops, [0] * len(ops))
+    want = oracle.restore_slots(oracle.Pool(1, N, 1, 16, 16, oracle.SSM_F32), ops,
+                                np.zeros(len(ops), dtype=np.int64))
+    torch.cuda.synchronize()
+    assert got == want.tolist() and got[:35] == [1] * 35 and got[35:] == [0, 1, 0]
+    copied = {d: s for (d, r, s) in ops if r and 0 < s < N and s != d}
+    for n in range(N):
+        s = copied.get(n, n)
+        assert torch.equal(ssm[:, n], ssm0[:, s]) and torch.equal(conv[:, n], conv0[:, s]), n
