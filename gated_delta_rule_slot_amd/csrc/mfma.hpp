@@ -93,6 +93,20 @@ __device__ __forceinline__ f32x4 mfma3k16(const Split4 &a, const Split4 &b, f32x
   return c;
 }
 
+// a0 * b0 + a1 * b1 + c for bf16 pairs (the products are exact in fp32)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c, false);
+}
+// half h of word x (low half) and of word y (high half): one v_perm_b32
+__device__ __forceinline__ uint32_t halves(uint32_t x, uint32_t y, int h) {
+  return __builtin_amdgcn_perm(y, x, h ? 0x07060302u : 0x05040100u);
+}
+// channel e of two input rows (8 bf16 channels each) as one pair
+__device__ __forceinline__ uint32_t tok_pair(const u32x4 &r0, const u32x4 &r1, int e) {
+  return halves(r0[e >> 1], r1[e >> 1], e & 1);
+}
+
 __device__ __forceinline__ float bf16_elem(const u32x4 &v, int e) {
   const uint32_t w = v[e >> 1];
   return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));

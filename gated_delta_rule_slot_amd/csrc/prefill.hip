@@ -49,12 +49,20 @@
 //         2^60); a block whose channels span more than that uses an exact
 //         per-pair evaluation instead.
 #include "common.hpp"
+#include "lanes.hpp"
 #include "mfma.hpp"
 
 namespace gdn {
 namespace {
 
 constexpr int kPrepThreads = 1024;
+
+// min(max(v, 0), hi) for a wave-uniform v, kept in a scalar register: the compiler
+// otherwise forms a vector med3 for the clamp, and a buffer resource built from a
+// vector register costs a readfirstlane loop around every load that uses it.
+__device__ __forceinline__ int uniform_clamp(int v, int hi) {
+  return __builtin_amdgcn_readfirstlane(max(min(v, hi), 0));
+}
 constexpr float kMidRange = 60.f;  // max |log2| of a factor on the diagonal fast path
 // A chunk takes the chunk-reference path when no 16-token block decays any channel
 // by more than 2^-kBlockSpan, so that e^{+-L} stays within 2^(+-4 kBlockSpan).
@@ -181,15 +189,25 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
     u32x4 wr[4], xr[R + 3];
 #pragma unroll
     for (int i = 0; i < 4; ++i) wr[i] = *reinterpret_cast<const u32x4 *>(a.conv_w + (ch0 + 2 * i) * 4);
+    // The chunk's input rows (positions p0 - 3 .. p0 + 63) as a buffer resource based
+    // at its first row inside the request: a row before it (negative offset) or past
+    // the request's end lies outside the resource and reads zero, so no load is
+    // branched around.  A warm start's rows at positions -3..-1 come from the conv
+    // rows of the slot, patched in for the first chunk only.
+    const int qb = max(p0 - 3, 0);
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.x) + (int64_t(rg.bos) + qb) * C, 0, uniform_clamp(rg.len - qb, 67) * int(C) * 2,
+        0x00020000);
 #pragma unroll
-    for (int r = 0; r < R + 3; ++r) {  // positions p0 + t0 - 3 + r
-      const int q = p0 + t0 - 3 + r;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (q >= 0 && q < rg.len)
-        v = *reinterpret_cast<const u32x4 *>(a.x + int64_t(rg.bos + q) * C + ch0);
-      else if (q < 0 && q >= -3 && warm)
-        v = *reinterpret_cast<const u32x4 *>(crow + int64_t(3 + q) * C + ch0);
-      xr[r] = v;
+    for (int r = 0; r < R + 3; ++r)  // positions p0 + t0 - 3 + r
+      xr[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            xres, ((p0 + t0 - 3 + r - qb) * int(C) + int(ch0)) * 2, 0, 0));
+    if (warm && p0 + t0 - 3 < 0) {  // p0 < 0 when the request starts inside the chunk
+#pragma unroll
+      for (int r = 0; r < R + 3; ++r) {
+        const int q = p0 + t0 - 3 + r;
+        if (q < 0 && q >= -3) xr[r] = *reinterpret_cast<const u32x4 *>(crow + int64_t(3 + q) * C + ch0);
+      }
     }
     const bool silu = (a.flags & GDN_F_CONV_SILU) != 0;
     const bool norm = part == 0 ? (a.flags & GDN_F_L2NORM_Q) != 0 : part == 1 ? (a.flags & GDN_F_L2NORM_K) != 0 : false;
@@ -199,92 +217,79 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
       const bool valid = pos >= 0 && pos < rg.len;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        // tap j multiplies position pos - 3 + j
-        float acc = bf16_elem(wr[e >> 1], 4 * (e & 1)) * bf16_elem(xr[r], e);
-#pragma unroll
-        for (int j = 1; j < 4; ++j) acc = fmaf(bf16_elem(wr[e >> 1], 4 * (e & 1) + j), bf16_elem(xr[r + j], e), acc);
+        // taps (0, 1) and (2, 3) multiply positions (pos - 3, pos - 2) and (pos - 1, pos)
+        float acc = dot2_bf16(wr[e >> 1][2 * (e & 1)], tok_pair(xr[r], xr[r + 1], e), 0.f);
+        acc = dot2_bf16(wr[e >> 1][2 * (e & 1) + 1], tok_pair(xr[r + 2], xr[r + 3], e), acc);
         if (silu) acc = acc / (1.f + __expf(-acc));
         y[r][e] = valid ? acc : 0.f;
       }
-      if (norm) {  // wave-uniform: every lane takes part in the shuffles
+      if (norm) {  // wave-uniform: the G lanes of a token set share the sum
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = fmaf(y[r][e], y[r][e], ss);
-#pragma unroll
-        for (int off = G / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-        const float inv = 1.f / sqrtf(ss + 1e-6f);
+        ss = group_sum<G>(ss);
+        const float inv = __builtin_amdgcn_rsqf(ss + 1e-6f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[r][e] *= inv;
       }
     }
   } else if (wave >= 12) {
-    // wave 12 + m handles token block m; lane = (channel octet co, token quad tqb)
-    constexpr int NCO = KD / 8;
-    const int m = wave - 12, co = lane & 15, tqb = lane >> 4;
-    const bool act = co < NCO, chv = act && 8 * co < D;
+    // wave 12 + m handles token block m.  Lane l takes channels l and l + 64 (those
+    // below KD) and cumulates their log2 decays token by token, so no step crosses
+    // lanes.  The block's decay rows are a buffer resource based at its first row
+    // inside the request: rows outside it read zero and are masked below.
+    const int m = wave - 12;
     if (wave == 12) {
       const int pos = p0 + lane;
       sB[lane] = (pos >= 0 && pos < rg.len) ? a.beta[int64_t(rg.bos + pos) * H + h] : 0.f;
     }
-    float cum[4][8];
+    constexpr int NA = AMODE == GDN_ALPHA_PER_CHANNEL ? D : 1;
+    constexpr int CPL = (KD + 63) / 64;
+    const int pb = p0 + 16 * m, pbase = max(pb, 0);
+    const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.alpha) + (int64_t(rg.bos + pbase) * H + h) * NA, 0,
+        uniform_clamp(rg.len - pbase, 16) * H * NA * 4, 0x00020000);
+    // every load is issued before the first use, so the 16 rows are in flight together
+    float av[16][CPL];
 #pragma unroll
-    for (int tok = 0; tok < 4; ++tok) {
-      const int pos = p0 + 16 * m + 4 * tqb + tok;
-      const bool valid = chv && pos >= 0 && pos < rg.len;
-      float av[8];
-      if (AMODE == GDN_ALPHA_PER_CHANNEL) {
-        f32x4 u0 = {1.f, 1.f, 1.f, 1.f}, u1 = u0;
-        if (valid) {
-          const float *ap = a.alpha + (int64_t(rg.bos + pos) * H + h) * D + 8 * co;
-          u0 = ld4(ap);
-          u1 = ld4(ap + 4);
-        }
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          av[j] = u0[j];
-          av[4 + j] = u1[j];
-        }
-      } else {
-        const float s = valid ? a.alpha[int64_t(rg.bos + pos) * H + h] : 1.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) av[e] = s;
+      for (int q = 0; q < CPL; ++q) {
+        const int ch = lane + 64 * q;
+        av[j][q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 ares, ((pb + j - pbase) * H * NA + (NA == 1 || ch >= D ? 0 : ch)) * 4, 0, 0));
       }
+    float cum[CPL], l0[CPL], l7[CPL];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float la = valid ? fmaxf(__log2f(av[e]), -512.f) : 0.f;  // a == 0: full decay
-        cum[tok][e] = tok == 0 ? la : cum[tok - 1][e] + la;
+    for (int q = 0; q < CPL; ++q) cum[q] = l0[q] = l7[q] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int pos = pb + j;
+      const bool vpos = pos >= 0 && pos < rg.len;
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const int ch = lane + 64 * q;
+        const float la = (vpos && ch < D) ? fmaxf(__log2f(av[j][q]), -512.f) : 0.f;  // a == 0: full decay
+        cum[q] += la;
+        if (ch < KD) sL[(16 * m + j) * DP + ch] = cum[q];
+        if (j == 0) l0[q] = cum[q];
+        if (j == 7) l7[q] = cum[q];
       }
     }
-    // cumulative inside the 16-token block: add the sums of the lower token quads
     bool big = false, wide = false;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float tot = cum[3][e];
-      const float v0 = __shfl(tot, co, 64), v1 = __shfl(tot, co + 16, 64), v2 = __shfl(tot, co + 32, 64);
-      const float off = tqb == 0 ? 0.f : tqb == 1 ? v0 : tqb == 2 ? v0 + v1 : (v0 + v1) + v2;
-#pragma unroll
-      for (int tok = 0; tok < 4; ++tok) cum[tok][e] += off;
-      const float l0 = __shfl(cum[0][e], co, 64), l7 = __shfl(cum[3][e], co + 16, 64),
-                  l15 = __shfl(cum[3][e], co + 48, 64);
-      big = big || (act && fmaxf(l0 - l7, l7 - l15) > kMidRange);
-      wide = wide || (act && -l15 > kBlockSpan);
+    for (int q = 0; q < CPL; ++q) {
+      const int ch = lane + 64 * q;
+      if (ch < KD) {
+        big = big || fmaxf(l0[q] - l7[q], l7[q] - cum[q]) > kMidRange;
+        wide = wide || -cum[q] > kBlockSpan;
+        sTot[m * KD + ch] = cum[q];
+      }
     }
     const bool any_big = __ballot(big) != 0, any_wide = __ballot(wide) != 0;
     // bit 0: the blockwise path evaluates this diagonal block exactly;
     // bit 1: the block rules out the chunk-reference path
     if (lane == 0) sWF[m] = (any_big ? 1 : 0) | (any_wide ? 2 : 0);
-    if (act) {
-#pragma unroll
-      for (int tok = 0; tok < 4; ++tok) {
-        const int t = 16 * m + 4 * tqb + tok;
-        st4(sL + t * DP + 8 * co, f32x4{cum[tok][0], cum[tok][1], cum[tok][2], cum[tok][3]});
-        st4(sL + t * DP + 8 * co + 4, f32x4{cum[tok][4], cum[tok][5], cum[tok][6], cum[tok][7]});
-      }
-      if (tqb == 3) {
-        st4(sTot + m * KD + 8 * co, f32x4{cum[3][0], cum[3][1], cum[3][2], cum[3][3]});
-        st4(sTot + m * KD + 8 * co + 4, f32x4{cum[3][4], cum[3][5], cum[3][6], cum[3][7]});
-      }
-    }
   }
   __syncthreads();
 

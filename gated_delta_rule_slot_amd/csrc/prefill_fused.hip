@@ -105,20 +105,6 @@ __device__ __forceinline__ Split frag_lds(const char *lds, int off, int idx, int
   return s;
 }
 
-// a0 * b0 + a1 * b1 + c for bf16 pairs (the products are exact in fp32)
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c, false);
-}
-// half h of word x (low half) and of word y (high half): one v_perm_b32
-__device__ __forceinline__ uint32_t halves(uint32_t x, uint32_t y, int h) {
-  return __builtin_amdgcn_perm(y, x, h ? 0x07060302u : 0x05040100u);
-}
-// channel e of two input rows (8 bf16 channels each) as one pair
-__device__ __forceinline__ uint32_t tok_pair(const u32x4 &r0, const u32x4 &r1, int e) {
-  return halves(r0[e >> 1], r1[e >> 1], e & 1);
-}
-
 // 4 consecutive values of one fragment lane, both planes, already split
 __device__ __forceinline__ void frag_put4w(char *lds, int off, int idx, int lanep, int e0, const Split2 &a,
                                            const Split2 &b) {
