@@ -880,9 +880,9 @@ __device__ __forceinline__ void split4(const f32x4 &v, bf16x4 &hi, bf16x4 &lo) {
 }
 
 template <int D, typename TS>
-__global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs ka) {
+__global__ __launch_bounds__((128 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs ka) {
   using RC = Rec<D>;
-  constexpr int NW = RC::NKS, NT = 64 * NW, NCB = RC::NCB;
+  constexpr int NW = RC::NKS, NT = 128 * NW, NCB = RC::NCB;
   constexpr int TBW = 4 / NW;  // 16-token blocks per wave
   // every wave's two channel tiles exist unless D = 16 (then tile 1 is padding);
   // keeping the guards compile-time leaves the chunk loop without branches, so
@@ -950,13 +950,22 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
   }
   if (ka.c0 >= rg.nch) return;
 
-  // ---- state: lane (r16, g4) of wave w holds S[v0 + r16][16cb + 4g4 + j], cb = 2w + hh
+  // ---- roles: waves 0..NW-1 carry the state recurrence (Δ and the state update);
+  // waves NW..2NW-1 form the outputs (g.Q S0^T + M Δ) and store them.  Both run the
+  // same chunk loop with the same two barriers per chunk: A (the entry state's
+  // operand fragments are in LDS) and B (Δ's fragments are in LDS).  Each LDS
+  // buffer is read before the barrier that precedes its next write, so one copy of
+  // each suffices.
+  const bool state_wave = wave < NW;
+  const int tw = state_wave ? wave : wave - NW;  // this wave's first 16-token block
+
+  // ---- state: lane (r16, g4) of state wave w holds S[v0 + r16][16cb + 4g4 + j], cb = 2w + hh
   f32x4 S[2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int cb = 2 * wave + hh;
     S[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (kAllCb || cb < NCB) {
+    if (state_wave && (kAllCb || cb < NCB)) {
       const int64_t o = int64_t(v0 + r16) * D + 16 * cb + 4 * g4;
       if (ka.c0 > 0) S[hh] = ld4(carry + o);
       else if (warm) S[hh] = load_state4<TS>(Slive + o);
@@ -975,9 +984,16 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
     trk1 = a.track_slots[2 * b + 1];
     snap_lo = (sl + rg.len) / a.snap_interval - sl / a.snap_interval - 2;
   }
+  // the track slot a chunk ending at request position `done` snapshots into, or 0
+  auto snap_dst = [&](int done) {
+    const int n_end = sl + done;
+    const int j = n_end / a.snap_interval - sl / a.snap_interval - 1;
+    if (n_end % a.snap_interval != 0 || j < snap_lo) return 0;
+    return ((nxt + j) & 1) ? trk1 : trk0;
+  };
 
-  // operands of one chunk for this wave: its token blocks (W, g.Q, M, U) and its
-  // channel tiles (G(63,.)K, g_63)
+  // operands of one chunk for this wave: the state waves' token blocks (W, U) and
+  // channel tiles (G(63,.)K, g_63); the output waves' token blocks (g.Q, M)
   auto rec_rsrc = [&](int cc) {
     return __builtin_amdgcn_make_buffer_rsrc(
         ka.ws + ka.rec_off + (size_t(b * ka.w + (cc - ka.c0)) * H + h) * RC::BYTES, 0, int(RC::BYTES),
@@ -989,7 +1005,7 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
   auto load_wu = [&](__amdgpu_buffer_rsrc_t r) {
 #pragma unroll
     for (int u = 0; u < TBW; ++u) {
-      const int tb = wave + NW * u;
+      const int tb = tw + NW * u;
 #pragma unroll
       for (int ks = 0; ks < NW; ++ks) Wn[u][ks] = frag_buf(r, voff, int(RC::WF) + (tb * NW + ks) * 2048);
       Un[u] = f4_buf(r, voff, int(RC::UF) + (tb * NCB + vt) * 1024);
@@ -998,7 +1014,7 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
   auto load_q = [&](__amdgpu_buffer_rsrc_t r) {
 #pragma unroll
     for (int u = 0; u < TBW; ++u) {
-      const int tb = wave + NW * u;
+      const int tb = tw + NW * u;
 #pragma unroll
       for (int ks = 0; ks < NW; ++ks) Qn[u][ks] = frag_buf(r, voff, int(RC::QF) + (tb * NW + ks) * 2048);
     }
@@ -1017,114 +1033,84 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
   auto load_m = [&](__amdgpu_buffer_rsrc_t r) {
 #pragma unroll
     for (int u = 0; u < TBW; ++u) {
-      const int tb = wave + NW * u;
+      const int tb = tw + NW * u;
 #pragma unroll
       for (int ksp = 0; ksp < 2; ++ksp) Mn[u][ksp] = frag_buf(r, voff, int(RC::MF) + (tb * 2 + ksp) * 2048);
     }
   };
-  {
-    // same issue order as inside the loop, so that the wait counts the compiler
-    // derives at the loop head do not force later groups to land early
-    const __amdgpu_buffer_rsrc_t r0 = rec_rsrc(ka.c0);
-    load_wu(r0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_q(r0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_kg(r0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_m(r0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-#pragma unroll 1
-  for (int c = ka.c0; c < cend; ++c) {
-    const __amdgpu_buffer_rsrc_t rnext = rec_rsrc(min(c + 1, cend - 1));  // next chunk's operands
-
-    // this wave's channel slice of the entry state, as an operand, to every wave
-    {
-      const Split sb = split44(S[0], S[1]);
-      sS[wave][0][lane] = sb.hi;
-      sS[wave][1][lane] = sb.lo;
-    }
-    __syncthreads();
-    Split Sf[NW];
+  // the entry state's operand fragments (all channel slices) and Δ's (all tokens)
+  auto read_sf = [&](Split (&Sf)[NW]) {
 #pragma unroll
     for (int ks = 0; ks < NW; ++ks) {
       Sf[ks].hi = sS[ks][0][lane];
       Sf[ks].lo = sS[ks][1][lane];
     }
-
-    // Dl = U - W S0^T for this wave's token blocks (the record keeps -W)
-#pragma unroll
-    for (int u = 0; u < TBW; ++u) {
-      const int tb = wave + NW * u;
-      f32x4 d = Un[u];
-#pragma unroll
-      for (int ks = 0; ks < NW; ++ks) d = mfma3(Wn[u][ks], Sf[ks], d);
-      bf16x4 dh, dl;
-      split4(d, dh, dl);
-      sD[tb >> 1][0][lane][tb & 1] = dh;
-      sD[tb >> 1][1][lane][tb & 1] = dl;
-    }
-    load_wu(rnext);
-    // (g.Q) S0^T for the same blocks
-    f32x4 Oq[TBW];
-#pragma unroll
-    for (int u = 0; u < TBW; ++u) {
-      Oq[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NW; ++ks) Oq[u] = mfma3(Qn[u][ks], Sf[ks], Oq[u]);
-    }
-    load_q(rnext);
-    __syncthreads();
-    Split Db[2];
+  };
+  auto read_db = [&](Split (&Db)[2]) {
 #pragma unroll
     for (int ksp = 0; ksp < 2; ++ksp) {
       Db[ksp].hi = *reinterpret_cast<const bf16x8 *>(&sD[ksp][0][lane][0]);
       Db[ksp].lo = *reinterpret_cast<const bf16x8 *>(&sD[ksp][1][lane][0]);
     }
+  };
 
-    // S = S Diag(g_63) + Dl^T (G(63,.) K) on this wave's channels (kept here: the
-    // g_63 operand is among the latest loads of the previous chunk)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if (kAllCb || 2 * wave + hh < NCB) {
-        S[hh] *= Gn[hh];
-#pragma unroll
-        for (int ksp = 0; ksp < 2; ++ksp) S[hh] = mfma3(Kn[hh][ksp], Db[ksp], S[hh]);
-      }
+  if (state_wave) {
+    {
+      // same issue order as inside the loop, so that the wait counts the compiler
+      // derives at the loop head do not force later groups to land early
+      const __amdgpu_buffer_rsrc_t r0 = rec_rsrc(ka.c0);
+      load_wu(r0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_kg(r0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    load_kg(rnext);
+#pragma unroll 1
+    for (int c = ka.c0; c < cend; ++c) {
+      const __amdgpu_buffer_rsrc_t rnext = rec_rsrc(min(c + 1, cend - 1));  // next chunk's operands
 
-    // O = (g.Q) S0^T + M Dl; the stores go through a buffer resource spanning this
-    // chunk's rows of the request, and a padding token's offset lies outside it,
-    // so the hardware drops that store
-    const int pbase = max(64 * c - rg.off, 0), pend = min(64 * c - rg.off + 64, rg.len);
-    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-        a.out + (int64_t(rg.bos) + pbase) * H * D, 0, (pend - pbase) * H * D * 2, 0x00020000);
-#pragma unroll
-    for (int u = 0; u < TBW; ++u) {
-      const int tb = wave + NW * u;
-      f32x4 o = Oq[u];
-#pragma unroll
-      for (int ksp = 0; ksp < 2; ++ksp) o = mfma3(Mn[u][ksp], Db[ksp], o);  // zero above the diagonal
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int pos = 64 * c - rg.off + 16 * tb + 4 * g4 + j;
-        const int offs = (pos >= pbase && pos < pend) ? (((pos - pbase) * H + h) * D + v0 + r16) * 2 : 0x7fffffff;
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(a.scale * o[j]), orsrc, offs, 0, 0);
+      // this wave's channel slice of the entry state, as an operand, to every wave
+      {
+        const Split sb = split44(S[0], S[1]);
+        sS[wave][0][lane] = sb.hi;
+        sS[wave][1][lane] = sb.lo;
       }
-    }
-    load_m(rnext);
+      __syncthreads();  // A
+      Split Sf[NW];
+      read_sf(Sf);
 
-    // snapshot at a boundary that ends this chunk
-    if (a.snap_interval > 0) {
-      const int done = min(64 * (c + 1) - rg.off, rg.len);
-      const int n_end = sl + done;
-      const int j = n_end / a.snap_interval - sl / a.snap_interval - 1;
-      if (n_end % a.snap_interval == 0 && j >= snap_lo) {
-        const int dst = ((nxt + j) & 1) ? trk1 : trk0;
+      // Dl = U - W S0^T for this wave's token blocks (the record keeps -W)
+#pragma unroll
+      for (int u = 0; u < TBW; ++u) {
+        const int tb = tw + NW * u;
+        f32x4 d = Un[u];
+#pragma unroll
+        for (int ks = 0; ks < NW; ++ks) d = mfma3(Wn[u][ks], Sf[ks], d);
+        bf16x4 dh, dl;
+        split4(d, dh, dl);
+        sD[tb >> 1][0][lane][tb & 1] = dh;
+        sD[tb >> 1][1][lane][tb & 1] = dl;
+      }
+      load_wu(rnext);
+      __syncthreads();  // B
+      Split Db[2];
+      read_db(Db);
+
+      // S = S Diag(g_63) + Dl^T (G(63,.) K) on this wave's channels
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        if (kAllCb || 2 * wave + hh < NCB) {
+          S[hh] *= Gn[hh];
+#pragma unroll
+          for (int ksp = 0; ksp < 2; ++ksp) S[hh] = mfma3(Kn[hh][ksp], Db[ksp], S[hh]);
+        }
+      }
+      load_kg(rnext);
+
+      // snapshot of the state at a boundary that ends this chunk (the output waves
+      // copy the conv rows)
+      if (a.snap_interval > 0) {
+        const int dst = snap_dst(min(64 * (c + 1) - rg.off, rg.len));
         if (dst >= ka.slots) {
           if (ka.err && vt == 0 && tid == 0) atomicOr(ka.err, GDN_ERRW_BAD_TRACK_SLOT);
         } else if (dst > 0) {
@@ -1134,13 +1120,68 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
             const int cb = 2 * wave + hh;
             if (kAllCb || cb < NCB) store_state4(Sdst + int64_t(v0 + r16) * D + 16 * cb + 4 * g4, S[hh]);
           }
-          if (vt == 0) {
-            uint16_t *conv_dst = ka.conv + (int64_t(a.layer) * ka.slots + dst) * kConvRows * C;
-            for (int i = tid; i < 3 * 3 * D; i += NT) {
-              const int row = i / (3 * D), k = i % (3 * D);
-              const int64_t ch = int64_t(k / D) * H * D + int64_t(h) * D + k % D;
-              conv_dst[row * C + ch] = conv_row_value(done - 3 + row, ch);
-            }
+        }
+      }
+    }
+  } else {
+    {
+      const __amdgpu_buffer_rsrc_t r0 = rec_rsrc(ka.c0);
+      load_q(r0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_m(r0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int otid = tid - 64 * NW;  // thread index among the output waves
+#pragma unroll 1
+    for (int c = ka.c0; c < cend; ++c) {
+      const __amdgpu_buffer_rsrc_t rnext = rec_rsrc(min(c + 1, cend - 1));
+      __syncthreads();  // A
+      Split Sf[NW];
+      read_sf(Sf);
+      // (g.Q) S0^T for this wave's token blocks
+      f32x4 Oq[TBW];
+#pragma unroll
+      for (int u = 0; u < TBW; ++u) {
+        Oq[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NW; ++ks) Oq[u] = mfma3(Qn[u][ks], Sf[ks], Oq[u]);
+      }
+      load_q(rnext);
+      __syncthreads();  // B
+      Split Db[2];
+      read_db(Db);
+
+      // O = (g.Q) S0^T + M Dl; the stores go through a buffer resource spanning this
+      // chunk's rows of the request, and a padding token's offset lies outside it,
+      // so the hardware drops that store
+      const int pbase = max(64 * c - rg.off, 0), pend = min(64 * c - rg.off + 64, rg.len);
+      const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+          a.out + (int64_t(rg.bos) + pbase) * H * D, 0, (pend - pbase) * H * D * 2, 0x00020000);
+#pragma unroll
+      for (int u = 0; u < TBW; ++u) {
+        const int tb = tw + NW * u;
+        f32x4 o = Oq[u];
+#pragma unroll
+        for (int ksp = 0; ksp < 2; ++ksp) o = mfma3(Mn[u][ksp], Db[ksp], o);  // zero above the diagonal
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int pos = 64 * c - rg.off + 16 * tb + 4 * g4 + j;
+          const int offs = (pos >= pbase && pos < pend) ? (((pos - pbase) * H + h) * D + v0 + r16) * 2 : 0x7fffffff;
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(a.scale * o[j]), orsrc, offs, 0, 0);
+        }
+      }
+      load_m(rnext);
+
+      // conv rows of a snapshot at a boundary that ends this chunk
+      if (a.snap_interval > 0 && vt == 0) {
+        const int done = min(64 * (c + 1) - rg.off, rg.len);
+        const int dst = snap_dst(done);
+        if (dst > 0 && dst < ka.slots) {
+          uint16_t *conv_dst = ka.conv + (int64_t(a.layer) * ka.slots + dst) * kConvRows * C;
+          for (int i = otid; i < 3 * 3 * D; i += 64 * NW) {
+            const int row = i / (3 * D), k = i % (3 * D);
+            const int64_t ch = int64_t(k / D) * H * D + int64_t(h) * D + k % D;
+            conv_dst[row * C + ch] = conv_row_value(done - 3 + row, ch);
           }
         }
       }
@@ -1152,7 +1193,7 @@ __global__ __launch_bounds__((64 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs 
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int cb = 2 * wave + hh;
-    if (kAllCb || cb < NCB) {
+    if (state_wave && (kAllCb || cb < NCB)) {
       const int64_t o = int64_t(v0 + r16) * D + 16 * cb + 4 * g4;
       if (done_all) store_state4(Slive + o, S[hh]);
       else st4(carry + o, S[hh]);
@@ -1197,7 +1238,7 @@ hipError_t launch_prep(const KArgs &ka, hipStream_t s) {
 
 template <int D>
 hipError_t launch_scan(const KArgs &ka, bool bf, hipStream_t s) {
-  const dim3 grid(unsigned(ka.a.batch) * ka.heads * ka.vt_count), block(64 * Rec<D>::NKS);
+  const dim3 grid(unsigned(ka.a.batch) * ka.heads * ka.vt_count), block(128 * Rec<D>::NKS);
   if (bf) hipLaunchKernelGGL((prefill_scan_kernel<D, uint16_t>), grid, block, 0, s, ka);
   else hipLaunchKernelGGL((prefill_scan_kernel<D, float>), grid, block, 0, s, ka);
   return hipGetLastError();
