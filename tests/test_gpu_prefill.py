@@ -272,6 +272,7 @@ def test_prefill_full_kda_workload():
     case = Case(seed=cfg.seed, H=cfg.heads, D=cfg.head_k, lens=[6144], bf16=True, amode=1,
                 snap=64, warm=[0], N=cfg.slots)
     pool, out = case.run_gpu()
+    assert int(pool.err_word.item()) == 0
     ref, o_ref, e = case.run_oracle()
     check(case, pool, out, ref, o_ref)
 
