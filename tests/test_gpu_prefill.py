@@ -264,6 +264,19 @@ def test_prefill_long_request_windows_match_single_pass():
     check(case, p1, o1, ref, o_ref)
 
 
+def test_prefill_very_long_request():
+    """One request of 100,000 tokens (1,563 chunks, a partial last one) beside a
+    short one, warm start, per-channel decay, bf16 pool, a snapshot every 4096
+    tokens from an unaligned-to-4096 start: the whole result against the oracle."""
+    print("prefill parity: 100k-token request", flush=True)
+    case = Case(seed=31, H=2, D=16, lens=[100_000, 37], bf16=True, amode=1, snap=4096,
+                start=[1024, 64], warm=[1, 1], path=TWO)
+    pool, out = case.run_gpu()
+    assert int(pool.err_word.item()) == 0
+    ref, o_ref, e = case.run_oracle()
+    check(case, pool, out, ref, o_ref)
+
+
 def test_prefill_full_kda_workload():
     """12 heads, K=V=128, one request of 6144 tokens, per-channel decay, bf16
     pool, snapshot at every 64-token boundary: checked in full."""
