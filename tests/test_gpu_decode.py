@@ -77,6 +77,7 @@ def _assert_parity(pool, out, ref, o_ref, layer, live, extra_written=()):
     ("D64 fp32 KDA", 3, 1, 40, 6, 64, False, 17, 1),
     ("D128 fp32 GDN", 4, 1, 64, 8, 128, False, 33, 0),
     ("D128 bf16 KDA", 5, 3, 64, 12, 128, True, 20, 1),
+    ("D128 bf16 KDA every slot live", 6, 1, 600, 3, 128, True, 599, 1),
 ])
 def test_decode_parity(name, seed, L, N, H, D, bf16, B, amode):
     print(f"decode parity: {name}", flush=True)
