@@ -20,10 +20,11 @@
 //         Every contraction runs on bf16 MFMA in a three-product hi/lo split,
 //         which carries about 16 mantissa bits and fp32 range.
 //   scan  (one workgroup per (request, head, 16 rows of V); serial over chunks):
-//         wave w keeps the state columns of channels [32w, 32w+32) in fp32
-//         registers, forms its share of W S0^T and (g.Q) S0^T, and one LDS
-//         exchange per chunk completes Dl; every wave then updates its own state
-//         columns and one 16-token block of outputs.  No operand is transposed
+//         state wave w keeps the state columns of channels [32w, 32w+32) in fp32
+//         registers and forms Dl for one 16-token block; one LDS exchange per
+//         chunk completes Dl, and every state wave updates its own columns.  As
+//         many output waves form (g.Q) S0^T + M Dl for their token blocks and
+//         store them, off the state's serial chain.  No operand is transposed
 //         on the way: the record is stored in MFMA operand order, with the
 //         32-wide k steps permuted the way two 16x16 accumulator tiles lie in a
 //         wave's registers (see pk below), so accumulators feed the next product
