@@ -400,20 +400,6 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
                                         *reinterpret_cast<const bf16x4 *>(pQl + o + 16), 0, 1, 2, 3, 4, 5, 6, 7);
         frag_store(rec + RC::QF, tb * NKS + ks, ln, sp);
       }
-      for (int it = rel; it < NCB * 2 * 64; it += 384) {  // G(63,.)K = R e^{L_63}, tokens along k
-        const int ln = it & 63, ksp = (it >> 6) & 1, cb = it >> 7;
-        const int cc = 16 * cb + (ln & 15), g = ln >> 4;
-        float tot = 0.f;
-        for (int kb = 0; kb < 4; ++kb) tot += sTot[kb * KD + cc];
-        const float g63 = fexp2(tot);
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int o = (32 * ksp + pk(g, e)) * KP + cc;
-          v[e] = (static_cast<float>(pRh[o]) + static_cast<float>(pRl[o])) * g63;
-        }
-        frag_store(rec + RC::KF, cb * 2 + ksp, ln, split8(v));
-      }
       // M fragments (tb 0 and 1, ks' 1) lie above the diagonal; the scan multiplies
       // them anyway to keep its loop free of branches, so store zeros
       for (int it = rel; it < 256; it += 384) {
@@ -426,6 +412,22 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
         for (int kb = 0; kb < 4; ++kb) tot += sTot[kb * KD + cc];
         recGC[cc] = fexp2(tot);
       }
+    }
+    // G(63,.)K = R e^{L_63}, tokens along k, on every wave (the tile products of waves
+    // 0..9 take less time than the record writes of waves 10..15)
+    for (int it = tid; it < NCB * 2 * 64; it += kPrepThreads) {
+      const int ln = it & 63, ksp = (it >> 6) & 1, cb = it >> 7;
+      const int cc = 16 * cb + (ln & 15), g = ln >> 4;
+      float tot = 0.f;
+      for (int kb = 0; kb < 4; ++kb) tot += sTot[kb * KD + cc];
+      const float g63 = fexp2(tot);
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int o = (32 * ksp + pk(g, e)) * KP + cc;
+        v[e] = (static_cast<float>(pRh[o]) + static_cast<float>(pRl[o])) * g63;
+      }
+      frag_store(rec + RC::KF, cb * 2 + ksp, ln, split8(v));
     }
     __syncthreads();  // the R and Q planes are free from here on
     if (wave < 10) {
