@@ -64,6 +64,16 @@ constexpr int kPrepThreads = 1024;
 __device__ __forceinline__ int uniform_clamp(int v, int hi) {
   return __builtin_amdgcn_readfirstlane(max(min(v, hi), 0));
 }
+// lane s of each quad's value v, in all four lanes (DPP quad_perm [s, s, s, s]; s
+// is a constant after unrolling)
+__device__ __forceinline__ float quad_bcast(float v, int s) {
+  switch (s) {
+    case 0: return dpp_mov<0x00>(v);
+    case 1: return dpp_mov<0x55>(v);
+    case 2: return dpp_mov<0xAA>(v);
+    default: return dpp_mov<0xFF>(v);
+  }
+}
 constexpr float kMidRange = 60.f;  // max |log2| of a factor on the diagonal fast path
 // A chunk takes the chunk-reference path when no 16-token block decays any channel
 // by more than 2^-kBlockSpan, so that e^{+-L} stays within 2^(+-4 kBlockSpan).
@@ -463,27 +473,40 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
     __syncthreads();
 
     // ---- F3: inverses D_m of the unit lower-triangular diagonal blocks --------
-    if (wave == 0) {
-      const int m = lane >> 4, j = lane & 15;  // lane: column j of block m
-      float x[16];
+    if (wave < 4) {
+      // Block m = wave, column j of the inverse on the four lanes 4j..4j+3: lane p
+      // owns rows 4k + p of the column's right-hand side and subtracts each x_t as
+      // soon as it is known (x_t is broadcast from its owner lane), so every row
+      // takes the same fused multiply-adds in the same order as a row-by-row
+      // substitution, and the chain per row step is one broadcast and one FMA.
+      const int m = wave, j = lane >> 2, p = lane & 3;
+      f32x4 Lr[4][4];  // rows 4k + p of block m, columns 0..15
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        float v = (t == j) ? 1.f : 0.f;
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-        for (int i = 0; i < t; ++i) v = fmaf(-fA[(16 * m + t) * TP + 16 * m + i], x[i], v);
-        x[t] = v;
-        fD[(16 * m + t) * DPT + j] = v;
+        for (int c4 = 0; c4 < 4; ++c4) Lr[k][c4] = ld4(fA + (16 * m + 4 * k + p) * TP + 16 * m + 4 * c4);
+      float bc[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bc[k] = (4 * k + p == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int t = 0; t < 15; ++t) {
+        const float xt = quad_bcast(bc[t >> 2], t & 3);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (4 * k + p > t) bc[k] = fmaf(-Lr[k][t >> 2][t & 3], xt, bc[k]);
       }
-    } else if (wave <= 6) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) fD[(16 * m + 4 * k + p) * DPT + j] = bc[k];
+    } else if (wave < 10) {
       // -N_mk for the six blocks below the diagonal, split once for every wave
-      const int q = wave - 1;
+      const int q = wave - 4;
       const int m = q < 1 ? 1 : q < 3 ? 2 : 3, k = q - m * (m - 1) / 2;
       const Split4 nf = split4s(-ld4(fA + (16 * m + r16) * TP + 16 * k + 4 * g4));
       fN[(q * 64 + lane) * 2] = nf.hi;
       fN[(q * 64 + lane) * 2 + 1] = nf.lo;
     } else {
       if constexpr (KD != D) {  // W's channel padding (the solve writes channels < D)
-        for (int i = tid - 448; i < 64 * (KD - D); i += kPrepThreads - 448) {
+        for (int i = tid - 640; i < 64 * (KD - D); i += kPrepThreads - 640) {
           const int t = i / (KD - D), cc = D + i % (KD - D);
           fW[t * DP + cc] = 0.f;
         }
