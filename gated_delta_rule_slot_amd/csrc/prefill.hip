@@ -523,16 +523,21 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
       const int tile = isw ? wave - NCB : wave;
       const int col = 16 * tile + r16;
       Split4 XS[4];
+      // every block's right-hand side first: its LDS reads are then in flight together
+      // instead of one round trip per block step of the substitution
+      f32x4 Yb[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        f32x4 acc;
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = 16 * m + 4 * g4 + j;
           const float yv = isw ? static_cast<float>(pPh[t * KP + col]) + static_cast<float>(pPl[t * KP + col])
                                : fV[t * DP + col];
-          acc[j] = sB[t] * yv;
+          Yb[m][j] = sB[t] * yv;
         }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4 acc = Yb[m];
 #pragma unroll
         for (int k = 0; k < m; ++k) {
           const int q = m * (m - 1) / 2 + k;
