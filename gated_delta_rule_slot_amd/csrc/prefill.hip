@@ -520,9 +520,6 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
     //      accumulators and enter the next k = 16 products as operands unchanged.
     if (wave < 2 * NCB) {
       const bool isw = wave >= NCB;
-      // the W tiles read two planes per value and finish last: they win issue
-      // arbitration against the V tiles on their SIMD for this phase
-      if (isw) __builtin_amdgcn_s_setprio(2);
       const int tile = isw ? wave - NCB : wave;
       const int col = 16 * tile + r16;
       Split4 XS[4];
@@ -557,7 +554,6 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
           for (int j = 0; j < 4; ++j) fW[(16 * m + 4 * g4 + j) * DP + col] = X[j];
         }
       }
-      __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
 
