@@ -492,6 +492,84 @@ def test_decode_track_points_from_the_page(golden_dir):
     assert hits == spec["checkpoints"]
 
 
+@pytest.mark.parametrize("alpha_mode", [oracle.ALPHA_PER_CHANNEL, oracle.ALPHA_PER_HEAD])
+@pytest.mark.parametrize("ssm_dtype", [oracle.SSM_F32, oracle.SSM_BF16])
+def test_batched_decode_equals_single_request_calls(alpha_mode, ssm_dtype):
+    """oracle_decode_step over B requests in one call equals B calls of one
+    request each, and a one-token oracle_prefill per request (page
+    "企业官网建设流程全解析", "--mamba-track-interval": the step folds one
+    token per request; a request whose length reaches a multiple of the interval
+    snapshots into track_slots[b][next_track_idx[b]]).  The pool has K != V, two
+    layers and three heads, so a wrong per-request stride of x, alpha, beta, out,
+    the slot table, the track pairs or the next index lands on another request's
+    data or slot.  Covered: a reserved slot (0), a slot past the pool (flagged),
+    a request that snapshots into track index 1, one into index 0, one whose
+    designated track entry is masked (0), and requests that do not snapshot.
+    fp32 build, bit-exact."""
+    L, N, H, K, V = 2, 24, 3, 8, 4
+    g = wl.generator(1212)
+    pool = oracle.Pool(L, N, H, K, V, ssm_dtype)
+    ssm, conv = wl.warm_pool(g, L, N, H, K, V, ssm_dtype == oracle.SSM_BF16)
+    pool.ssm()[:] = ssm.numpy() if ssm_dtype == oracle.SSM_F32 else wl.bf16_bits(ssm)
+    pool.conv()[:] = wl.bf16_bits(conv)
+    w = wl.bf16_bits(wl.conv_weights(g, H * (2 * K + V)))
+    slots = np.array([5, 0, 9, 2, 30, 14, 7], np.int32)
+    B = len(slots)
+    seq_after = np.array([512, 300, 257, 768, 1024, 1280, 9], np.int32)
+    track = np.array([[17, 18], [19, 20], [21, 22], [3, 4], [11, 12], [0, 23], [15, 16]], np.int32)
+    nxt = np.array([1, 0, 0, 0, 1, 0, 1], np.int32)
+    inp = wl.projected_inputs(g, B, H, K, V, alpha_mode)
+    x, a, b = wl.bf16_bits(inp["x"]), inp["alpha"].numpy(), inp["beta"].numpy()
+    kw = dict(scale=0.75, flags=oracle.L2NORM_K, track_interval=256, precision="f32")
+
+    batched = pool.copy()
+    out, err = oracle.decode_step(batched, 1, slots, x, w, a, alpha_mode, b,
+                                  seq_len_after=seq_after, track_slots=track,
+                                  next_track_idx=nxt, **kw)
+    assert err == 1                                   # slot 30 is past the pool
+    single = pool.copy()
+    for i in range(B):
+        o1, e1 = oracle.decode_step(single, 1, slots[i:i + 1], x[i:i + 1], w, a[i:i + 1],
+                                    alpha_mode, b[i:i + 1], seq_len_after=seq_after[i:i + 1],
+                                    track_slots=track[i:i + 1], next_track_idx=nxt[i:i + 1], **kw)
+        assert e1 == (1 if slots[i] >= N else 0)
+        np.testing.assert_array_equal(out[i], o1[0])
+    assert np.array_equal(batched.ssm_bytes, single.ssm_bytes)
+    assert np.array_equal(batched.conv(), single.conv())
+
+    # One-token prefill calls with the same snapshot rule give the same pool
+    # and outputs (the prefill indexing is pinned by the per-head test above).
+    pre = pool.copy()
+    for i in range(B):
+        if not 0 < slots[i] < N:
+            continue
+        o1, e1 = oracle.prefill(pre, 1, [0, 1], slots[i:i + 1], x[i:i + 1], w, a[i:i + 1],
+                                alpha_mode, b[i:i + 1], has_initial_state=[1],
+                                start_len=seq_after[i:i + 1] - 1, scale=0.75,
+                                flags=oracle.L2NORM_K, snap_interval=256,
+                                track_slots=track[i:i + 1], next_track_idx=nxt[i:i + 1],
+                                precision="f32")
+        assert e1 == 0
+        np.testing.assert_array_equal(out[i], o1[0])
+    assert np.array_equal(batched.ssm_bytes, pre.ssm_bytes)
+    assert np.array_equal(batched.conv(), pre.conv())
+
+    # What landed where: live slots changed, snapshots in the designated track
+    # slots only, the masked entry and the skipped requests wrote nothing.
+    changed = lambda p, l, s: not np.array_equal(p.ssm()[l, s], pool.ssm()[l, s])
+    for i, s in enumerate(slots):
+        if 0 < s < N:
+            assert changed(batched, 1, s) and not changed(batched, 0, s)
+    snaps = {18: 5, 3: 2}                             # track slot -> the live slot it copies
+    for t, s in snaps.items():
+        assert np.array_equal(batched.ssm()[1, t], batched.ssm()[1, s])
+        assert np.array_equal(batched.conv()[1, t], batched.conv()[1, s])
+    untouched = [n for n in range(1, N) if n not in set(slots.tolist()) | set(snaps)]
+    for n in untouched:
+        assert not changed(batched, 1, n), n
+    assert not out[1].any() and not out[4].any()
+
+
 def test_prefill_walkthrough_from_the_page(golden_dir):
     """1200 tokens in calls of 512/512/176 with snapshot interval 512: slot B
     (track[0]) holds the state at 512, slot C (track[1]) the state at 1024, and
