@@ -17,7 +17,8 @@ from ._binding import (  # noqa: F401
     ALPHA_PER_CHANNEL, ALPHA_PER_HEAD, CONV_SILU, ERRW_BAD_SEQLENS, ERRW_BAD_SLOT,
     ERRW_BAD_TRACK_SLOT, ERRW_BAD_TREE, GDN_BF16, GDN_F32, L2NORM_K, L2NORM_Q, LIB_PATH,
     CKPT_FULL, CKPT_PRESENT, CKPT_STORED, MAX_RING_POSITIONS, MAX_TREE_NODES, CheckpointIndex,
-    GdnError, PREFILL_ONE_KERNEL, PREFILL_TWO_KERNEL, ReplayRing, StatePool, ckpt_chain_hashes,
+    GdnError, PREFILL_ONE_KERNEL, PREFILL_TWO_KERNEL, SNAP_LAST_ONLY, ReplayRing, StatePool,
+    ckpt_chain_hashes,
     conv_gdn_prefill_chunked, gdn_accept_scatter, gdn_decode_step, gdn_prefill_workspace_bytes, gdn_verify_tree, last_error,
     replayssm_commit, replayssm_ring_bytes, replayssm_verify, restore_slots, state_pool_bytes,
     state_pool_create, track_snapshot,

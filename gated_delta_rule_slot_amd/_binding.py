@@ -19,6 +19,7 @@ GDN_F32, GDN_BF16 = 0, 1
 ALPHA_PER_HEAD, ALPHA_PER_CHANNEL = 0, 1
 L2NORM_K, L2NORM_Q, CONV_SILU = 1, 2, 4
 PREFILL_ONE_KERNEL, PREFILL_TWO_KERNEL = 8, 16
+SNAP_LAST_ONLY = 32
 ERRW_BAD_SLOT, ERRW_BAD_TRACK_SLOT, ERRW_BAD_SEQLENS, ERRW_BAD_TREE = 1, 2, 4, 8
 MAX_TREE_NODES = 1024
 MAX_RING_POSITIONS = 64

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <new>
 
 #include "common.hpp"
@@ -145,7 +146,7 @@ GDN_API gdn_status conv_gdn_prefill_chunked(
   if (alpha_mode != GDN_ALPHA_PER_HEAD && alpha_mode != GDN_ALPHA_PER_CHANNEL)
     return fail(GDN_ERR_ARG, "alpha_mode %d unknown", alpha_mode);
   if (flags & ~uint32_t(GDN_F_L2NORM_K | GDN_F_L2NORM_Q | GDN_F_CONV_SILU | GDN_F_PREFILL_ONE_KERNEL |
-                        GDN_F_PREFILL_TWO_KERNEL))
+                        GDN_F_PREFILL_TWO_KERNEL | GDN_F_SNAP_LAST_ONLY))
     return fail(GDN_ERR_ARG, "unknown flag bits 0x%x", flags);
   if ((flags & GDN_F_PREFILL_ONE_KERNEL) && (flags & GDN_F_PREFILL_TWO_KERNEL))
     return fail(GDN_ERR_ARG, "GDN_F_PREFILL_ONE_KERNEL and GDN_F_PREFILL_TWO_KERNEL both set");
@@ -166,12 +167,16 @@ GDN_API gdn_status conv_gdn_prefill_chunked(
   if (x && !aligned(x, 16)) return fail(GDN_ERR_UNSUPPORTED, "x must be 16-byte aligned");
   if (out && !aligned(out, 16)) return fail(GDN_ERR_UNSUPPORTED, "out must be 16-byte aligned");
   if (!aligned(alpha, 16)) return fail(GDN_ERR_UNSUPPORTED, "alpha must be 16-byte aligned");
-  const size_t need_min = size_t(batch) * pool->d.heads * gdn::prefill_record_bytes(pool) +
-                          gdn::prefill_carry_bytes(pool, batch);
-  if (!workspace || workspace_bytes < need_min)
-    return fail(GDN_ERR_ARG, "workspace of %zu bytes is below the minimum %zu", workspace_bytes,
-                need_min);
-  if (!aligned(workspace, 256)) return fail(GDN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  // the one-kernel path keeps every intermediate on chip and takes no workspace
+  if (!one_kernel) {
+    const size_t need_min = size_t(batch) * pool->d.heads * gdn::prefill_record_bytes(pool) +
+                            gdn::prefill_carry_bytes(pool, batch);
+    if (!workspace || workspace_bytes < need_min)
+      return fail(GDN_ERR_ARG, "workspace of %zu bytes is below the minimum %zu", workspace_bytes,
+                  need_min);
+    if (!aligned(workspace, 256))
+      return fail(GDN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  }
   gdn::PrefillArgs a{layer,       batch,          total_tokens,  max_seqlen, cu_seqlens,
                      slot_table,  has_initial_state, start_len, x,          conv_w,
                      alpha,       alpha_mode,     beta,          scale,      flags,
@@ -242,22 +247,50 @@ GDN_API gdn_status restore_slots(gdn_pool_t pool, int32_t n_ops, const gdn_resto
     delete[] dst;
     return fail(GDN_ERR_ARG, "out of host memory");
   }
+  // the copies of one call run in parallel, so no copy may read a slot that another
+  // copy of the call writes, and no two copies may write one slot: such a call is
+  // rejected before any outcome is set
   int n = 0;
   const int slots = pool->d.slots;
   for (int i = 0; i < n_ops; ++i) {
     const gdn_restore_op &op = ops[i];
-    if (!op.restore_requested) continue;
     const int s = op.restore_src_slot_id, d = op.linear_state_id;
-    if (s < 1 || s >= slots || d < 1 || d >= slots) {
-      has_initial_state[i] = 0;  // COLD_START
-      continue;
-    }
-    if (s != d) {
+    if (op.restore_requested && s >= 1 && s < slots && d >= 1 && d < slots && s != d) {
       src[n] = s;
       dst[n] = d;
       ++n;
     }
-    has_initial_state[i] = 1;  // RESTORED
+  }
+  if (n > 1) {
+    int32_t *sorted = new (std::nothrow) int32_t[n];
+    if (!sorted) {
+      delete[] src;
+      delete[] dst;
+      return fail(GDN_ERR_ARG, "out of host memory");
+    }
+    std::copy(dst, dst + n, sorted);
+    std::sort(sorted, sorted + n);
+    int bad = 0, what = 0;
+    for (int i = 0; i + 1 < n && !bad; ++i)
+      if (sorted[i] == sorted[i + 1]) bad = sorted[i], what = 1;
+    for (int i = 0; i < n && !bad; ++i)
+      if (std::binary_search(sorted, sorted + n, src[i])) bad = src[i], what = 2;
+    delete[] sorted;
+    if (bad) {
+      delete[] src;
+      delete[] dst;
+      return fail(GDN_ERR_ARG,
+                  what == 1 ? "restore_slots: slot %d is the destination of two copies"
+                            : "restore_slots: slot %d is both a copy source and a copy destination",
+                  bad);
+    }
+  }
+  for (int i = 0; i < n_ops; ++i) {
+    const gdn_restore_op &op = ops[i];
+    if (!op.restore_requested) continue;
+    const int s = op.restore_src_slot_id, d = op.linear_state_id;
+    has_initial_state[i] = (s < 1 || s >= slots || d < 1 || d >= slots) ? 0   // COLD_START
+                                                                          : 1;  // RESTORED
   }
   hipError_t e = n ? gdn::launch_copy_host_pairs(pool, n, src, dst,
                                                  static_cast<hipStream_t>(stream))

@@ -1003,17 +1003,20 @@ __global__ __launch_bounds__((128 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs
     }
   }
 
-  // snapshots: only the last boundary of each ping-pong parity in this call is
-  // stored (an earlier one is overwritten by a later boundary of the same call,
-  // so the pool afterwards is the same); per-request values are read once here
-  // so that no load inside the chunk loop waits behind the operand loads
+  // snapshots: every boundary of the call is stored, or with GDN_F_SNAP_LAST_ONLY
+  // only the last boundary of each ping-pong parity (an earlier one is overwritten
+  // by a later boundary of the same call, so the pool afterwards is the same);
+  // per-request values are read once here so that no load inside the chunk loop
+  // waits behind the operand loads
   int sl = 0, nxt = 0, trk0 = 0, trk1 = 0, snap_lo = 0x7fffffff;
   if (a.snap_interval > 0) {
     sl = a.start_len[b];
     nxt = a.next_track_idx[b];
     trk0 = a.track_slots[2 * b];
     trk1 = a.track_slots[2 * b + 1];
-    snap_lo = (sl + rg.len) / a.snap_interval - sl / a.snap_interval - 2;
+    snap_lo = (a.flags & GDN_F_SNAP_LAST_ONLY)
+                  ? (sl + rg.len) / a.snap_interval - sl / a.snap_interval - 2
+                  : 0;
   }
   // the track slot a chunk ending at request position `done` snapshots into, or 0
   auto snap_dst = [&](int done) {

@@ -257,15 +257,18 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
     if (warm) S[kb] = load_s4<TS>(Slive + int64_t(vcol) * D + 16 * kb + 4 * g);
   }
 
-  // snapshots: only the last boundary of each ping-pong parity in the call is
-  // stored (an earlier one is overwritten by a later one of the same parity)
+  // snapshots: every boundary of the call is stored, or with GDN_F_SNAP_LAST_ONLY
+  // only the last boundary of each ping-pong parity (an earlier one is overwritten
+  // by a later one of the same parity)
   int sl = 0, nxt = 0, trk0 = 0, trk1 = 0, snap_lo = 0x7fffffff;
   if (a.snap_interval > 0) {
     sl = a.start_len[b];
     nxt = a.next_track_idx[b];
     trk0 = a.track_slots[2 * b];
     trk1 = a.track_slots[2 * b + 1];
-    snap_lo = (sl + rg.len) / a.snap_interval - sl / a.snap_interval - 2;
+    snap_lo = (a.flags & GDN_F_SNAP_LAST_ONLY)
+                  ? (sl + rg.len) / a.snap_interval - sl / a.snap_interval - 2
+                  : 0;
   }
 
   f32x4 Y[4], OQ[4];  // per chunk: Diag(b) (V - Diag(g) K S0^T) and Diag(g) Q S0^T

@@ -84,12 +84,18 @@ enum { GDN_ALPHA_PER_HEAD = 0, GDN_ALPHA_PER_CHANNEL = 1 };
 enum { GDN_F_L2NORM_K = 1u, GDN_F_L2NORM_Q = 2u, GDN_F_CONV_SILU = 4u };
 /* prefill path (conv_gdn_prefill_chunked only; with neither bit the library
  * chooses): ONE_KERNEL runs each (request, head) start to end in one workgroup with
- * the state on chip and needs no workspace beyond the minimum; it serves a decay per
- * head (GDN_ALPHA_PER_HEAD) at head dim 128 with max_seqlen * channels * 2 < 2^31,
- * and suits batches of many requests.
+ * the state on chip and takes no workspace (NULL and 0 are accepted); it serves a
+ * decay per head (GDN_ALPHA_PER_HEAD) at head dim 128 with
+ * max_seqlen * channels * 2 < 2^31, and suits batches of many requests.
  * TWO_KERNEL prepares every chunk in parallel and then scans them; it serves every
- * shape and suits a few long requests. */
+ * shape, needs the workspace, and suits a few long requests. */
 enum { GDN_F_PREFILL_ONE_KERNEL = 8u, GDN_F_PREFILL_TWO_KERNEL = 16u };
+/* prefill snapshots (conv_gdn_prefill_chunked only): by default every boundary of
+ * the call is written to its track slot.  With SNAP_LAST_ONLY only the last
+ * boundary of each ping-pong parity is written: an earlier boundary of the same
+ * parity is overwritten within the call, so the pool after the call is the same,
+ * but another stream reading a track slot during the call sees fewer states. */
+enum { GDN_F_SNAP_LAST_ONLY = 32u };
 
 /* bits a kernel may set in the pool's error word (sticky; the caller clears it) */
 enum {
@@ -187,12 +193,15 @@ gdn_status gdn_prefill_workspace_bytes(gdn_pool_t pool, int32_t batch, int32_t m
  *             (page "SGLang Mamba Radix Cache 深度解析", configuration:
  *             mamba_cache_chunk_size defaults to 64).
  * workspace   device scratch of workspace_bytes bytes, 256-byte aligned, owned by the
- *             caller and not read across calls (see gdn_prefill_workspace_bytes)
- * flags       GDN_F_L2NORM_K | GDN_F_L2NORM_Q | GDN_F_CONV_SILU, and at most one of
- *             GDN_F_PREFILL_ONE_KERNEL / GDN_F_PREFILL_TWO_KERNEL (ONE_KERNEL on a
- *             shape it does not serve returns GDN_ERR_UNSUPPORTED).  Without either,
- *             the one-kernel path runs when it serves the shape and batch * heads >= 128.
- *             Both paths compute the same thing to the stated tolerance.
+ *             caller and not read across calls (see gdn_prefill_workspace_bytes).  The
+ *             one-kernel path does not use it (NULL and 0 are accepted there); the
+ *             two-kernel path returns GDN_ERR_ARG below the minimum.
+ * flags       GDN_F_L2NORM_K | GDN_F_L2NORM_Q | GDN_F_CONV_SILU, GDN_F_SNAP_LAST_ONLY,
+ *             and at most one of GDN_F_PREFILL_ONE_KERNEL / GDN_F_PREFILL_TWO_KERNEL
+ *             (ONE_KERNEL on a shape it does not serve returns GDN_ERR_UNSUPPORTED).
+ *             Without either, the one-kernel path runs when it serves the shape and
+ *             batch * heads >= 128.  Both paths compute the same thing to the stated
+ *             tolerance.
  * The live slot receives the state after the last token.  Requests of length 0
  * leave a warm slot unchanged and zero a cold one. */
 gdn_status conv_gdn_prefill_chunked(gdn_pool_t pool, int32_t layer, int32_t batch,
@@ -225,7 +234,10 @@ gdn_status gdn_decode_step(gdn_pool_t pool, int32_t layer, int32_t batch,
  * >= slots (or src <= 0 with dst > 0) skips it and sets GDN_ERRW_BAD_TRACK_SLOT.
  * This is the masked track copy (page "企业官网建设流程全解析", section
  * "--mamba-track-interval", the scatter into the track slot) and copy_from /
- * fork (page "SGLang之MambaRadixCache机制", section 3.2).  Byte-exact. */
+ * fork (page "SGLang之MambaRadixCache机制", section 3.2).  Byte-exact.
+ * The pairs are copied in parallel: the destinations must be distinct and no
+ * source may be the destination of another pair (a chain a->b, b->c has no
+ * defined result).  The arrays live on the device, so this is not checked. */
 gdn_status track_snapshot(gdn_pool_t pool, int32_t layer_begin, int32_t layer_end, int32_t n,
                           const int32_t *src_slots, const int32_t *dst_slots, void *stream);
 
@@ -236,8 +248,11 @@ gdn_status track_snapshot(gdn_pool_t pool, int32_t layer_begin, int32_t layer_en
  *   src < 1 or src >= slots or dst < 1 or dst >= slots -> 0 (COLD_START), no copy
  *   src == dst                                   -> 1 (RESTORED), no copy
  *   otherwise: copy conv + ssm of every layer    -> 1 (RESTORED)
- * If a launch fails, every requested op of the call is set to 0 and GDN_ERR_HIP
- * is returned.  The copies are queued on the stream (no synchronisation). */
+ * The copies run in parallel, so a call in which two copies write one slot, or
+ * a copy reads a slot that another copy of the call writes, returns GDN_ERR_ARG
+ * with has_initial_state untouched and launches nothing.  If a launch fails,
+ * every requested op of the call is set to 0 and GDN_ERR_HIP is returned.  The
+ * copies are queued on the stream (no synchronisation). */
 gdn_status restore_slots(gdn_pool_t pool, int32_t n_ops, const gdn_restore_op *ops,
                          int64_t *has_initial_state, void *stream);
 

@@ -48,6 +48,27 @@ def worst_unit_rel_l2(got: np.ndarray, want: np.ndarray, unit_axes: int) -> floa
     return worst
 
 
+def unit_rel_l2(got: np.ndarray, want: np.ndarray, unit_axes: int, chunk: int = 2048) -> np.ndarray:
+    """Relative L2 of every unit formed by the leading ``unit_axes`` axes, as an
+    array of that shape.  uint16 inputs are bf16 bits and are widened first; the
+    work goes in blocks of ``chunk`` units to bound the host memory.  A unit whose
+    reference and result are both zero scores 0."""
+    lead = got.shape[:unit_axes]
+    n = int(np.prod(lead))
+    g = got.reshape(n, -1)
+    w = want.reshape(n, -1)
+    res = np.zeros(n, dtype=np.float64)
+    for i in range(0, n, chunk):
+        gi = widen(g[i:i + chunk]) if g.dtype == np.uint16 else g[i:i + chunk].astype(np.float64)
+        wi = widen(w[i:i + chunk]) if w.dtype == np.uint16 else w[i:i + chunk].astype(np.float64)
+        num = np.linalg.norm(gi - wi, axis=1)
+        den = np.linalg.norm(wi, axis=1)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.where(num > 0, np.inf, 0.0))
+        res[i:i + chunk] = r
+    return res.reshape(lead)
+
+
 def pool_to_oracle(ssm: torch.Tensor, conv: torch.Tensor) -> oracle.Pool:
     """Copy a device (or host) pool into an oracle host pool, byte for byte."""
     L, N, H, V, K = ssm.shape

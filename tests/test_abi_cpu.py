@@ -113,8 +113,13 @@ def test_calls_reject_bad_arguments_before_launch():
             1 | B.PREFILL_ONE_KERNEL, fake, 0, None, None, fake, 1 << 30, None) == -3
         assert "one-kernel" in B.last_error()
         assert B._lib.conv_gdn_prefill_chunked(
-            h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0, 1 | 32, fake,
+            h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0, 1 | 64, fake,
             0, None, None, fake, 1 << 30, None) == -1
+        # the two-kernel path needs its workspace (tiny batch: the library's choice)
+        assert B._lib.conv_gdn_prefill_chunked(
+            h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0,
+            1 | B.SNAP_LAST_ONLY, fake, 0, None, None, None, 0, None) == -1
+        assert "workspace" in B.last_error()
         # layer range for copies
         assert B._lib.track_snapshot(h, 0, 2, 1, fake, fake, None) == -2
         # draft trees: node count range, required buffers, alignment of node buffers
@@ -169,6 +174,34 @@ def test_restore_rules_without_copies_are_host_only():
         ops = [(3, 0, 2), (3, 1, -1), (3, 1, 8), (0, 1, 2), (4, 1, 4)]
         got = B.restore_slots(pool, ops, [7, 7, 7, 7, 7], stream=type("S", (), {"cuda_stream": 0})())
         assert got == [7, 0, 0, 0, 1]
+        pool.handle = None
+    finally:
+        B._lib.state_pool_destroy(h)
+
+
+def test_restore_rejects_chained_and_duplicate_copies():
+    """The copies of one restore call run in parallel, so a call where a copy
+    reads a slot another copy writes, or two copies write one slot, is rejected
+    on the host with has_initial_state untouched (nothing is launched)."""
+    st, h = _create()
+    assert st == 0
+    try:
+        S = type("S", (), {"cuda_stream": 0})()
+        pool = B.StatePool(h, None, None, None, (1, 8, 2, 16, 16))
+        for ops in ([(3, 1, 2), (5, 1, 3)],           # 2 -> 3 and 3 -> 5: a chain
+                    [(5, 1, 3), (3, 1, 2)],           # the same, listed the other way
+                    [(3, 1, 2), (3, 1, 4)],           # two copies into slot 3
+                    [(4, 1, 6), (6, 1, 4)]):          # a swap
+            with pytest.raises(RuntimeError, match="restore_slots"):
+                B.restore_slots(pool, ops, [7] * len(ops), stream=S)
+        hi = (ct.c_int64 * 2)(7, 7)
+        arr = (B.RestoreOp * 2)(B.RestoreOp(3, 1, 2), B.RestoreOp(5, 1, 3))
+        assert B._lib.restore_slots(h, 2, arr, hi, None) == -1
+        assert list(hi) == [7, 7]
+        # no copy is involved when src == dst, a request is off or a source is
+        # missing, so these do not conflict with the copy into 3
+        got = B.restore_slots(pool, [(3, 1, 3), (2, 0, 3), (3, 1, -1)], [7, 7, 7], stream=S)
+        assert got == [1, 7, 0]
         pool.handle = None
     finally:
         B._lib.state_pool_destroy(h)

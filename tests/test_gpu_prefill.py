@@ -277,6 +277,32 @@ def test_prefill_very_long_request():
     check(case, pool, out, ref, o_ref)
 
 
+LAST_ONLY = 32  # GDN_F_SNAP_LAST_ONLY
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("D128 bf16 KDA, two kernels", dict(seed=5, H=4, D=128, lens=[300, 70, 2], bf16=True, snap=64,
+                                        start=[64, 37, 126], warm=[1, 1, 1])),
+    ("D128 bf16 GDN, two kernels", dict(seed=12, H=4, D=128, lens=[300, 70, 2, 129], bf16=True,
+                                        amode=0, snap=64, start=[64, 37, 126, 0], warm=[1, 1, 1, 0],
+                                        path=TWO)),
+    ("D128 bf16 GDN, one kernel", dict(seed=12, H=4, D=128, lens=[300, 70, 2, 129], bf16=True,
+                                       amode=0, snap=64, start=[64, 37, 126, 0], warm=[1, 1, 1, 0],
+                                       path=ONE)),
+])
+def test_prefill_snapshots_last_only(name, kw):
+    """GDN_F_SNAP_LAST_ONLY stores only the last boundary of each ping-pong parity;
+    the pool after the call is the one the oracle's every-boundary definition
+    gives (slots, states and conv rows)."""
+    print(f"prefill snapshots, last of each parity only: {name}", flush=True)
+    case = Case(**kw)
+    case.path |= LAST_ONLY
+    pool, out = case.run_gpu()
+    ref, o_ref, e = case.run_oracle()
+    check(case, pool, out, ref, o_ref)
+    assert int(pool.err_word.item()) == 0
+
+
 def test_prefill_full_kda_workload():
     """12 heads, K=V=128, one request of 6144 tokens, per-channel decay, bf16
     pool, snapshot at every 64-token boundary: checked in full."""
@@ -303,15 +329,19 @@ def test_prefill_warm_gdn_subset(path):
     check(case, pool, out, ref, o_ref)
 
 
-def test_prefill_warm_workload_launch_sampled():
+@pytest.mark.timeout(600)
+def test_prefill_warm_workload_launch():
     """The prefix-hit warm prefill in the launch configuration the benchmark times:
     64 requests whose remaining lengths follow the benchmark's seeded prefix mix
     (13600 - 6144 * min(2, P // 6144), P ~ U[0, 13600)), 32 heads, K=V=128, scalar
     decay, fp32 pool of 81 slots, restored requests warm, the library's default
-    path (64 x 32 units: one kernel).  Inputs are drawn on the device; three
-    requests (the two shortest and a middle one) are checked against the oracle."""
+    path (64 x 32 units: one kernel, called without a workspace).  Inputs are
+    drawn on the device.  Checked against the oracle, every head: the two
+    shortest requests, a middle one, the first and the last cold 13,600-token
+    request (the longest, which the kernel's longest-first order starts first and
+    last among equals) and the first warm 7,456-token one."""
     import gated_delta_rule_slot_amd as gdn
-    print("prefill parity: warm-prefill launch, sampled requests", flush=True)
+    print("prefill parity: warm-prefill launch", flush=True)
     cfg = wl.WARM_PREFILL
     H, D, N, B, T_full = cfg.heads, cfg.head_k, cfg.slots, 64, 13600
     C = 3 * H * D
@@ -341,16 +371,17 @@ def test_prefill_warm_workload_launch_sampled():
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     pool = gdn.state_pool_create(ssm, conv, err)
     out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(gdn.gdn_prefill_workspace_bytes(pool, B, max(lens)), dtype=torch.uint8, device=dev)
     gdn.conv_gdn_prefill_chunked(pool, 0, cu.to(dev), slots.to(dev),
                                  torch.tensor(warm, dtype=torch.int32, device=dev), x, w, alpha,
                                  cfg.alpha_mode, beta, out, max(lens),
-                                 start_len=torch.tensor(depth, dtype=torch.int32, device=dev),
-                                 workspace=ws)
+                                 start_len=torch.tensor(depth, dtype=torch.int32, device=dev))
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     order = sorted(range(B), key=lambda i: lens[i])
-    pick = sorted({order[0], order[1], order[B // 2]})
+    cold = [i for i in range(B) if lens[i] == T_full]
+    warm1 = [i for i in range(B) if lens[i] == T_full - 6144]
+    assert cold and warm1
+    pick = sorted({order[0], order[1], order[B // 2], cold[0], cold[-1], warm1[0]})
     sub = [(int(cu[i]), int(cu[i + 1])) for i in pick]
     sl = [lens[i] for i in pick]
     idx = torch.cat([torch.arange(a, b) for a, b in sub]).to(dev)

@@ -14,7 +14,7 @@ import torch
 import oracle
 import workloads as wl
 from tests.helpers import (REL_L2_TOL, bf16_np, device_ssm_values, pool_bytes_equal, pool_to_oracle,
-                           ssm_values, widen, worst_unit_rel_l2)
+                           ssm_values, unit_rel_l2, widen, worst_unit_rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -232,13 +232,26 @@ def test_accept_scatter_flags_bad_input():
     assert torch.equal(pool.ssm[0, s[1]], ns[1, 2])
 
 
-def test_verify_full_size_tree_sampled():
+@pytest.mark.timeout(600)
+def test_verify_full_size_tree_every_unit():
     """The benchmark's draft-tree verify launch: 32 requests, a 63-node breadth-first
-    tree of topk 4, 32 heads, K = V = 128, bf16 state, decay per head.  The GPU runs
-    the whole launch; two requests are checked against the oracle (requests are
-    independent, so the oracle takes only those)."""
+    tree of topk 4, 32 heads, K = V = 128, bf16 state, decay per head.  Every
+    (request, node, head) unit of the launch is compared with the oracle, twice:
+
+    * step by step: the oracle takes each node's token from the GPU's own stored
+      parent state and conv rows (the live slot's for a root), as one decode step.
+      This isolates the kernel's step; every unit must be within 2e-3.
+    * end to end: the oracle walks the whole tree from the live slots.  Both sides
+      round every node state to bf16 before its children read it, and where the
+      GPU's fp32 and the oracle's fp64 values fall on two sides of a bf16 rounding
+      boundary the two trees carry different parents from then on, so the
+      difference grows with depth.  The measured worst per depth is asserted
+      against the bound stated for it (2e-3 on node states at every depth and on
+      outputs at depths 1 and 2, 3e-3 on outputs at depth 3).
+
+    Conv rows of every node are bit-exact copies of inputs on both sides."""
     import gated_delta_rule_slot_amd as gdn
-    print("verify: full-size tree launch, sampled requests", flush=True)
+    print("verify: full-size tree launch, every unit", flush=True)
     B, T, H, D = 32, 63, 32, 128
     N, C = 1 + 3 * B, H * 3 * D
     g, ssm, conv, w, inp, slots = _spec_inputs(106, 1, N, H, D, True, B, T, 0)
@@ -255,21 +268,56 @@ def test_verify_full_size_tree_sampled():
                         out, ns, nc)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
-    sample = [5, 30]
+    assert torch.equal(pool.ssm.cpu(), ssm) and torch.equal(pool.conv.cpu(), conv)  # live slots only read
+    out_h, ns_h, nc_h = bf16_np(out), bf16_np(ns), bf16_np(nc)
+    par = parent[0].tolist()
+    depth = np.array([1 if p < 0 else 0 for p in par])
+    for n, p in enumerate(par):
+        if p >= 0:
+            depth[n] = depth[p] + 1
+
+    # step by step: node (b, n) from the GPU's stored parent, one oracle decode step
+    cond = oracle.Pool(1, 1 + B * T, H, D, D, oracle.SSM_BF16)
+    ssm_b, conv_b = bf16_np(ssm), bf16_np(conv)
+    pidx = np.array(par)
+    for b in range(B):
+        rows = slice(1 + b * T, 1 + (b + 1) * T)
+        live = int(slots[b])
+        cond.ssm()[0, rows] = np.where((pidx < 0)[:, None, None, None], ssm_b[0, live][None],
+                                       ns_h[b, np.maximum(pidx, 0)])
+        cond.conv()[0, rows] = np.where((pidx < 0)[:, None, None], conv_b[0, live][None],
+                                        nc_h[b, np.maximum(pidx, 0)])
+    o_c, e_c = oracle.decode_step(cond, 0, np.arange(1, 1 + B * T, dtype=np.int32),
+                                  wl.bf16_bits(x).reshape(B * T, C), wl.bf16_bits(w),
+                                  a.numpy().reshape(B * T, H), 0, bt.numpy().reshape(B * T, H))
+    assert e_c == 0
+    eo_c = unit_rel_l2(out_h.reshape(B * T, H, D), o_c, 2)
+    es_c = unit_rel_l2(ns_h.reshape(B * T, H, D, D), cond.ssm()[0, 1:], 2)
+    assert np.array_equal(nc_h.reshape(B * T, 3, C), cond.conv()[0, 1:])
+    print(f"  step by step, all {B * T * H} units: worst out {eo_c.max():.2e}  state {es_c.max():.2e}",
+          flush=True)
+    del cond
+
+    # end to end: the oracle's own tree walk from the live slots
     ref = pool_to_oracle(ssm, conv)
     o_ref, ns_ref, nc_ref, e = oracle.verify_tree(
-        ref, 0, slots.numpy()[sample], parent.numpy()[sample], wl.bf16_bits(x)[sample], wl.bf16_bits(w),
-        a.numpy()[sample], 0, bt.numpy()[sample])
+        ref, 0, slots.numpy(), parent.numpy(), wl.bf16_bits(x), wl.bf16_bits(w), a.numpy(), 0,
+        bt.numpy())
     assert e == 0
-    eo = worst_unit_rel_l2(widen(bf16_np(out[sample])), widen(o_ref), 3)
-    es = 0.0
-    for i, b in enumerate(sample):  # node by node, to keep the host copies small
-        for n in range(T):
-            got = ns[b, n].cpu().to(torch.float64).numpy()
-            es = max(es, worst_unit_rel_l2(got, widen(ns_ref[i, n]), 1))
-    print(f"  worst unit rel-L2: out {eo:.2e}  node state {es:.2e}", flush=True)
-    assert eo <= REL_L2_TOL and es <= REL_L2_TOL
-    assert np.array_equal(bf16_np(nc[sample]), nc_ref)
+    assert np.array_equal(nc_h, nc_ref)
+    eo = unit_rel_l2(out_h, o_ref, 3)            # [B, T, H]
+    es = unit_rel_l2(ns_h, ns_ref, 3)
+    del ns_ref
+    worst = {}
+    for d in sorted(set(depth.tolist())):
+        sel = depth == d
+        worst[d] = (float(eo[:, sel].max()), float(es[:, sel].max()))
+        print(f"  end to end, depth {d} ({int(sel.sum())} nodes x {B} requests x {H} heads): "
+              f"worst out {worst[d][0]:.2e}  state {worst[d][1]:.2e}", flush=True)
+    assert eo_c.max() <= REL_L2_TOL and es_c.max() <= REL_L2_TOL
+    out_bound = {1: REL_L2_TOL, 2: REL_L2_TOL, 3: 1.5 * REL_L2_TOL}
+    for d, (wo, ws) in worst.items():
+        assert wo <= out_bound[d] and ws <= REL_L2_TOL, (d, wo, ws)
 
     # the benchmark's commit of that launch (a depth-3 node per request, tracking every
     # 256; three requests cross a multiple of 256 at depths 1, 2 and 3): the pool must
@@ -284,8 +332,8 @@ def test_verify_full_size_tree_sampled():
     gdn.gdn_accept_scatter(pool, 0, slots.cuda(), parent.cuda(), accepted.cuda(), ns, nc,
                            seq_len_before=before.cuda(), track_interval=256, track_slots=track.cuda(),
                            next_track_idx=nxt.cuda())
-    e3 = oracle.accept_scatter(ref2, 0, slots.numpy(), parent.numpy(), accepted.numpy(), bf16_np(ns),
-                               bf16_np(nc), seq_len_before=before.numpy(), track_interval=256,
+    e3 = oracle.accept_scatter(ref2, 0, slots.numpy(), parent.numpy(), accepted.numpy(), ns_h,
+                               nc_h, seq_len_before=before.numpy(), track_interval=256,
                                track_slots=track.numpy(), next_track_idx=nxt.numpy())
     torch.cuda.synchronize()
     assert e3 == 0 and int(err.item()) == 0
