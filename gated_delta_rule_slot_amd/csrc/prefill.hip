@@ -1158,14 +1158,38 @@ __global__ __launch_bounds__((128 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs
       }
     }
   } else {
+    const int otid = tid - 64 * NW;  // thread index among the output waves
+    // conv rows of a boundary snapshot of head h: 3 rows x (q, k, v) x D channels,
+    // one 16-byte piece per output thread.  The piece of chunk c's boundary is
+    // loaded during chunk c - 1, right after that chunk's Q operands, so that its
+    // store in chunk c waits on no load issued later (loads and stores retire in
+    // issue order through one counter).
+    constexpr int kSegPieces = D / 8, kConvPieces = 9 * kSegPieces;
+    const bool conv_snap_thread = a.snap_interval > 0 && vt == 0 && otid < kConvPieces;
+    const int cp_row = otid / (3 * kSegPieces), cp_seg = (otid / kSegPieces) % 3;
+    const int64_t cp_ch = int64_t(cp_seg) * H * D + int64_t(h) * D + (otid % kSegPieces) * 8;
+    auto conv_fetch = [&](int cc, int &dst) -> u32x4 {
+      dst = 0;
+      if (!conv_snap_thread || cc >= cend) return u32x4{0u, 0u, 0u, 0u};
+      const int done = min(64 * (cc + 1) - rg.off, rg.len);
+      dst = snap_dst(done);
+      if (dst <= 0 || dst >= ka.slots) return u32x4{0u, 0u, 0u, 0u};
+      const int q = done - 3 + cp_row;
+      if (q >= 0) return *reinterpret_cast<const u32x4 *>(a.x + int64_t(rg.bos + q) * C + cp_ch);
+      if (warm) return *reinterpret_cast<const u32x4 *>(conv_live + int64_t(3 + q) * C + cp_ch);
+      return u32x4{0u, 0u, 0u, 0u};
+    };
+    int cdst;
+    u32x4 cpiece;
     {
       const __amdgpu_buffer_rsrc_t r0 = rec_rsrc(ka.c0);
       load_q(r0);
       __builtin_amdgcn_sched_barrier(0);
+      cpiece = conv_fetch(ka.c0, cdst);
+      __builtin_amdgcn_sched_barrier(0);
       load_m(r0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int otid = tid - 64 * NW;  // thread index among the output waves
 #pragma unroll 1
     for (int c = ka.c0; c < cend; ++c) {
       const __amdgpu_buffer_rsrc_t rnext = rec_rsrc(min(c + 1, cend - 1));
@@ -1181,6 +1205,10 @@ __global__ __launch_bounds__((128 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs
         for (int ks = 0; ks < NW; ++ks) Oq[u] = mfma3(Qn[u][ks], Sf[ks], Oq[u]);
       }
       load_q(rnext);
+      __builtin_amdgcn_sched_barrier(0);
+      int cdst_next;
+      const u32x4 cpiece_next = conv_fetch(c + 1, cdst_next);
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();  // B
       Split Db[2];
       read_db(Db);
@@ -1207,18 +1235,12 @@ __global__ __launch_bounds__((128 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs
       load_m(rnext);
 
       // conv rows of a snapshot at a boundary that ends this chunk
-      if (a.snap_interval > 0 && vt == 0) {
-        const int done = min(64 * (c + 1) - rg.off, rg.len);
-        const int dst = snap_dst(done);
-        if (dst > 0 && dst < ka.slots) {
-          uint16_t *conv_dst = ka.conv + (int64_t(a.layer) * ka.slots + dst) * kConvRows * C;
-          for (int i = otid; i < 3 * 3 * D; i += 64 * NW) {
-            const int row = i / (3 * D), k = i % (3 * D);
-            const int64_t ch = int64_t(k / D) * H * D + int64_t(h) * D + k % D;
-            conv_dst[row * C + ch] = conv_row_value(done - 3 + row, ch);
-          }
-        }
+      if (cdst > 0 && cdst < ka.slots) {
+        uint16_t *conv_dst = ka.conv + (int64_t(a.layer) * ka.slots + cdst) * kConvRows * C;
+        *reinterpret_cast<u32x4 *>(conv_dst + int64_t(cp_row) * C + cp_ch) = cpiece;
       }
+      cpiece = cpiece_next;
+      cdst = cdst_next;
     }
   }
 
