@@ -3,7 +3,8 @@
 The entry points mirror include/gdn_slot.h one to one:
 
   state_pool_bytes, state_pool_create, gdn_prefill_workspace_bytes,
-  conv_gdn_prefill_chunked, gdn_decode_step, track_snapshot, restore_slots,
+  conv_gdn_prefill_chunked, conv_gdn_prefill_chunked_noalloc, gdn_decode_step,
+  track_snapshot, restore_slots,
   gdn_verify_tree, gdn_accept_scatter, replayssm_ring_bytes, replayssm_verify,
   replayssm_commit
 
@@ -19,7 +20,8 @@ from ._binding import (  # noqa: F401
     CKPT_FULL, CKPT_PRESENT, CKPT_STORED, MAX_RING_POSITIONS, MAX_TREE_NODES, CheckpointIndex,
     GdnError, PREFILL_ONE_KERNEL, PREFILL_TWO_KERNEL, SNAP_LAST_ONLY, ReplayRing, StatePool,
     ckpt_chain_hashes,
-    conv_gdn_prefill_chunked, gdn_accept_scatter, gdn_decode_step, gdn_prefill_workspace_bytes, gdn_verify_tree, last_error,
+    NOALLOC_SCRATCH_BYTES, conv_gdn_prefill_chunked, conv_gdn_prefill_chunked_noalloc,
+    gdn_accept_scatter, gdn_decode_step, gdn_prefill_workspace_bytes, gdn_verify_tree, last_error,
     replayssm_commit, replayssm_ring_bytes, replayssm_verify, restore_slots, state_pool_bytes,
     state_pool_create, track_snapshot,
 )

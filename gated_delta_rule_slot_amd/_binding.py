@@ -20,6 +20,7 @@ ALPHA_PER_HEAD, ALPHA_PER_CHANNEL = 0, 1
 L2NORM_K, L2NORM_Q, CONV_SILU = 1, 2, 4
 PREFILL_ONE_KERNEL, PREFILL_TWO_KERNEL = 8, 16
 SNAP_LAST_ONLY = 32
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDN_NOALLOC_SCRATCH_BYTES
 ERRW_BAD_SLOT, ERRW_BAD_TRACK_SLOT, ERRW_BAD_SEQLENS, ERRW_BAD_TREE = 1, 2, 4, 8
 MAX_TREE_NODES = 1024
 MAX_RING_POSITIONS = 64
@@ -64,6 +65,9 @@ _lib.gdn_last_error.restype = ct.c_char_p
 _lib.conv_gdn_prefill_chunked.argtypes = [
     _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _u32,
     _vp, _i32, _vp, _vp, _vp, _sz, _vp]
+_lib.conv_gdn_prefill_chunked_noalloc.argtypes = [
+    _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _u32,
+    _vp, _i32, _vp, _vp, _vp]
 _lib.gdn_prefill_workspace_bytes.argtypes = [_vp, _i32, _i32, ct.POINTER(_sz)]
 _lib.gdn_decode_step.argtypes = [
     _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _u32, _vp, _vp, _i32, _vp, _vp, _vp]
@@ -95,6 +99,7 @@ _lib.replayssm_verify.argtypes = [
 _lib.replayssm_commit.argtypes = [
     _vp, ct.POINTER(RingDesc), _i32, _i32, _vp, _vp, _u32, _vp, _i32, _vp, _vp, _vp]
 for _f in ("state_pool_bytes", "state_pool_create", "conv_gdn_prefill_chunked",
+           "conv_gdn_prefill_chunked_noalloc",
            "gdn_prefill_workspace_bytes", "gdn_decode_step", "track_snapshot", "restore_slots",
            "gdn_verify_tree", "gdn_accept_scatter", "replayssm_ring_bytes", "replayssm_verify",
            "replayssm_commit", "ckpt_chain_hashes", "ckpt_index_create", "ckpt_index_match",
@@ -223,6 +228,34 @@ def conv_gdn_prefill_chunked(pool: StatePool, layer, cu_seqlens, slot_table, has
         _ptr(has_initial_state), _ptr(start_len), _ptr(x), _ptr(conv_w), _ptr(alpha), alpha_mode,
         _ptr(beta), float(scale), flags, _ptr(out), snap_interval, _ptr(track_slots),
         _ptr(next_track_idx), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def conv_gdn_prefill_chunked_noalloc(pool: StatePool, layer, cu_seqlens, slot_table,
+                                     has_initial_state, x, conv_w, alpha, alpha_mode, beta, out,
+                                     max_seqlen, start_len=None, scale=1.0, flags=L2NORM_K,
+                                     snap_interval=0, track_slots=None, next_track_idx=None,
+                                     stream=None):
+    """conv_gdn_prefill_chunked without a workspace: the library's fixed per-device
+    scratch serves the two-kernel path and nothing is allocated."""
+    B = slot_table.numel()
+    T = x.shape[0] if x is not None else 0
+    H, V, K = pool.heads, pool.head_v, pool.head_k
+    _need(cu_seqlens, torch.int32, B + 1, "cu_seqlens")
+    _need(slot_table, torch.int32, B, "slot_table")
+    _need(has_initial_state, torch.int32, B, "has_initial_state")
+    _need(start_len, torch.int32, B, "start_len")
+    _need(x, torch.bfloat16, T * pool.channels, "x")
+    _need(conv_w, torch.bfloat16, pool.channels * 4, "conv_w")
+    _need(alpha, torch.float32, T * H * (K if alpha_mode == ALPHA_PER_CHANNEL else 1), "alpha")
+    _need(beta, torch.float32, T * H, "beta")
+    _need(out, torch.bfloat16, T * H * V, "out")
+    _need(track_slots, torch.int32, 2 * B, "track_slots")
+    _need(next_track_idx, torch.int32, B, "next_track_idx")
+    _check(_lib.conv_gdn_prefill_chunked_noalloc(
+        pool.handle, layer, B, T, int(max_seqlen), _ptr(cu_seqlens), _ptr(slot_table),
+        _ptr(has_initial_state), _ptr(start_len), _ptr(x), _ptr(conv_w), _ptr(alpha), alpha_mode,
+        _ptr(beta), float(scale), flags, _ptr(out), snap_interval, _ptr(track_slots),
+        _ptr(next_track_idx), _stream(stream)))
 
 
 def gdn_decode_step(pool: StatePool, layer, slot_table, x, conv_w, alpha, alpha_mode, beta, out,

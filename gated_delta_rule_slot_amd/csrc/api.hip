@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "common.hpp"
@@ -79,6 +80,43 @@ gdn_status launched(hipError_t e, const char *what) {
 
 }  // namespace
 
+// ---- fixed scratch of the allocation-free prefill entry point ----------------
+// The two-kernel prefill's records and state carry, for callers that cannot
+// allocate.  Each GPU the library runs on holds one copy of this array until the
+// process ends.  Its host-side name is only a stand-in for the symbol: host code
+// uses the device address that hipGetSymbolAddress returns for the current
+// device, kept per device after the first call on it.  Every call on one GPU
+// shares that GPU's copy: calls that overlap on one GPU race.  Nothing needs
+// clearing between calls, since every byte the kernels read is written earlier
+// in the same call.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];  // device address of `scratch`, per device
+
+gdn_status scratch_for_current_device(void **addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GDN_ERR_UNSUPPORTED, "device %d is beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return GDN_OK;
+}
+}  // namespace
+
 GDN_API gdn_status state_pool_bytes(const gdn_pool_desc *desc, size_t *ssm_bytes,
                                     size_t *conv_bytes) {
   gdn_status s = check_shape(desc);
@@ -128,13 +166,16 @@ GDN_API gdn_status gdn_prefill_workspace_bytes(gdn_pool_t pool, int32_t batch,
   return ok();
 }
 
-GDN_API gdn_status conv_gdn_prefill_chunked(
+namespace {
+// The prefill entry points share this body.  With use_scratch the two-kernel
+// path takes the fixed per-device scratch instead of a caller workspace.
+gdn_status prefill_entry(
     gdn_pool_t pool, int32_t layer, int32_t batch, int32_t total_tokens, int32_t max_seqlen,
     const int32_t *cu_seqlens, const int32_t *slot_table, const int32_t *has_initial_state,
     const int32_t *start_len, const uint16_t *x, const uint16_t *conv_w, const float *alpha,
     int32_t alpha_mode, const float *beta, float scale, uint32_t flags, uint16_t *out,
     int32_t snap_interval, const int32_t *track_slots, const int32_t *next_track_idx,
-    void *workspace, size_t workspace_bytes, void *stream) {
+    void *workspace, size_t workspace_bytes, bool use_scratch, void *stream) {
   gdn_status s = check_pool(pool, layer);
   if (s != GDN_OK) return s;
   if (batch < 0 || batch > 65535) return fail(GDN_ERR_RANGE, "batch %d outside [0, 65535]", batch);
@@ -171,6 +212,16 @@ GDN_API gdn_status conv_gdn_prefill_chunked(
   if (!one_kernel) {
     const size_t need_min = size_t(batch) * pool->d.heads * gdn::prefill_record_bytes(pool) +
                             gdn::prefill_carry_bytes(pool, batch);
+    if (use_scratch) {
+      if (need_min > size_t(GDN_NOALLOC_SCRATCH_BYTES))
+        return fail(GDN_ERR_RANGE,
+                    "the two-kernel prefill of %d requests x %d heads needs %zu bytes of scratch "
+                    "at least; the fixed scratch holds %zu (split the batch)",
+                    batch, pool->d.heads, need_min, size_t(GDN_NOALLOC_SCRATCH_BYTES));
+      gdn_status ss = scratch_for_current_device(&workspace);
+      if (ss != GDN_OK) return ss;
+      workspace_bytes = size_t(GDN_NOALLOC_SCRATCH_BYTES);
+    }
     if (!workspace || workspace_bytes < need_min)
       return fail(GDN_ERR_ARG, "workspace of %zu bytes is below the minimum %zu", workspace_bytes,
                   need_min);
@@ -187,6 +238,33 @@ GDN_API gdn_status conv_gdn_prefill_chunked(
                     "conv_gdn_prefill_chunked launch (one kernel)");
   return launched(gdn::launch_prefill(pool, a, static_cast<hipStream_t>(stream)),
                   "conv_gdn_prefill_chunked launch");
+}
+}  // namespace
+
+GDN_API gdn_status conv_gdn_prefill_chunked(
+    gdn_pool_t pool, int32_t layer, int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    const int32_t *cu_seqlens, const int32_t *slot_table, const int32_t *has_initial_state,
+    const int32_t *start_len, const uint16_t *x, const uint16_t *conv_w, const float *alpha,
+    int32_t alpha_mode, const float *beta, float scale, uint32_t flags, uint16_t *out,
+    int32_t snap_interval, const int32_t *track_slots, const int32_t *next_track_idx,
+    void *workspace, size_t workspace_bytes, void *stream) {
+  return prefill_entry(pool, layer, batch, total_tokens, max_seqlen, cu_seqlens, slot_table,
+                       has_initial_state, start_len, x, conv_w, alpha, alpha_mode, beta, scale,
+                       flags, out, snap_interval, track_slots, next_track_idx, workspace,
+                       workspace_bytes, false, stream);
+}
+
+GDN_API gdn_status conv_gdn_prefill_chunked_noalloc(
+    gdn_pool_t pool, int32_t layer, int32_t batch, int32_t total_tokens, int32_t max_seqlen,
+    const int32_t *cu_seqlens, const int32_t *slot_table, const int32_t *has_initial_state,
+    const int32_t *start_len, const uint16_t *x, const uint16_t *conv_w, const float *alpha,
+    int32_t alpha_mode, const float *beta, float scale, uint32_t flags, uint16_t *out,
+    int32_t snap_interval, const int32_t *track_slots, const int32_t *next_track_idx,
+    void *stream) {
+  return prefill_entry(pool, layer, batch, total_tokens, max_seqlen, cu_seqlens, slot_table,
+                       has_initial_state, start_len, x, conv_w, alpha, alpha_mode, beta, scale,
+                       flags, out, snap_interval, track_slots, next_track_idx, nullptr, 0, true,
+                       stream);
 }
 
 GDN_API gdn_status gdn_decode_step(gdn_pool_t pool, int32_t layer, int32_t batch,

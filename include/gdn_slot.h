@@ -214,6 +214,34 @@ gdn_status conv_gdn_prefill_chunked(gdn_pool_t pool, int32_t layer, int32_t batc
                                     const int32_t *track_slots, const int32_t *next_track_idx,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of the fixed device scratch behind conv_gdn_prefill_chunked_noalloc: one
+ * copy per GPU the library runs on, held until the process ends. */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* conv_gdn_prefill_chunked for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, meaning and results, without the workspace: the two-kernel
+ * path works in the library's fixed per-device scratch of
+ * GDN_NOALLOC_SCRATCH_BYTES bytes (in windows of as many chunks as it holds), and
+ * the one-kernel path needs none.  The call allocates nothing and frees nothing.
+ * A two-kernel batch whose minimum workspace (gdn_prefill_workspace_bytes with
+ * max_seqlen = 64) exceeds the scratch returns GDN_ERR_RANGE and launches
+ * nothing; split the batch.  The first call on a device looks up the scratch's
+ * address there (GDN_ERR_HIP if that fails).  All calls on one GPU share its
+ * scratch, and the scratch keeps the last call's contents: calls that overlap on
+ * one GPU (different streams, or different host threads without ordering) race
+ * and must not be issued. */
+gdn_status conv_gdn_prefill_chunked_noalloc(gdn_pool_t pool, int32_t layer, int32_t batch,
+                                            int32_t total_tokens, int32_t max_seqlen,
+                                            const int32_t *cu_seqlens, const int32_t *slot_table,
+                                            const int32_t *has_initial_state,
+                                            const int32_t *start_len, const uint16_t *x,
+                                            const uint16_t *conv_w, const float *alpha,
+                                            int32_t alpha_mode, const float *beta, float scale,
+                                            uint32_t flags, uint16_t *out, int32_t snap_interval,
+                                            const int32_t *track_slots,
+                                            const int32_t *next_track_idx, void *stream);
+
 /* One decode token per request for one layer (x [batch][C], alpha [batch][heads]
  * or [batch][heads][head_k], beta [batch][heads], out [batch][heads][head_v]).
  * The state is always read from the slot.  If track_interval > 0 and

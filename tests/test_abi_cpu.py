@@ -120,6 +120,15 @@ def test_calls_reject_bad_arguments_before_launch():
             h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0,
             1 | B.SNAP_LAST_ONLY, fake, 0, None, None, None, 0, None) == -1
         assert "workspace" in B.last_error()
+        # the allocation-free prefill refuses a two-kernel batch beyond its fixed scratch
+        # (before touching the device)
+        assert B._lib.conv_gdn_prefill_chunked_noalloc(
+            h, 0, 65535, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0, 1, fake,
+            0, None, None, None) == -2
+        assert "scratch" in B.last_error()
+        assert B._lib.conv_gdn_prefill_chunked_noalloc(
+            h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0, 1, fake,
+            32, fake, fake, None) == -1
         # layer range for copies
         assert B._lib.track_snapshot(h, 0, 2, 1, fake, fake, None) == -2
         # draft trees: node count range, required buffers, alignment of node buffers
