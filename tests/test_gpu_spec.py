@@ -245,9 +245,8 @@ def test_verify_full_size_tree_every_unit():
       round every node state to bf16 before its children read it, and where the
       GPU's fp32 and the oracle's fp64 values fall on two sides of a bf16 rounding
       boundary the two trees carry different parents from then on, so the
-      difference grows with depth.  The measured worst per depth is asserted
-      against the bound stated for it (2e-3 on node states at every depth and on
-      outputs at depths 1 and 2, 3e-3 on outputs at depth 3).
+      difference grows with depth (worst output unit 4.1e-4, 1.2e-3 and 1.8e-3 at
+      depths 1, 2 and 3).  Every unit must be within 2e-3.
 
     Conv rows of every node are bit-exact copies of inputs on both sides."""
     import gated_delta_rule_slot_amd as gdn
@@ -315,9 +314,8 @@ def test_verify_full_size_tree_every_unit():
         print(f"  end to end, depth {d} ({int(sel.sum())} nodes x {B} requests x {H} heads): "
               f"worst out {worst[d][0]:.2e}  state {worst[d][1]:.2e}", flush=True)
     assert eo_c.max() <= REL_L2_TOL and es_c.max() <= REL_L2_TOL
-    out_bound = {1: REL_L2_TOL, 2: REL_L2_TOL, 3: 1.5 * REL_L2_TOL}
     for d, (wo, ws) in worst.items():
-        assert wo <= out_bound[d] and ws <= REL_L2_TOL, (d, wo, ws)
+        assert wo <= REL_L2_TOL and ws <= REL_L2_TOL, (d, wo, ws)
 
     # the benchmark's commit of that launch (a depth-3 node per request, tracking every
     # 256; three requests cross a multiple of 256 at depths 1, 2 and 3): the pool must
