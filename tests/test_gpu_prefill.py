@@ -316,6 +316,33 @@ def test_prefill_full_kda_workload():
     check(case, pool, out, ref, o_ref)
 
 
+def test_prefill_single_pass_matches_scratch_windows():
+    """The full KDA workload shape (12 heads, one request, snapshots every 64) in one
+    pass over a full workspace equals, bit for bit, the no-alloc entry point, whose
+    64 MiB scratch holds 37 chunks per window (three windows with the fp32 carry
+    between them), and the oracle; a second call on a warm, unaligned request
+    follows on the same scratch."""
+    import gated_delta_rule_slot_amd as gdn
+    print("prefill: single pass against scratch windows", flush=True)
+    for seed, lens, start, warm in ((31, [6144], [0], [0]), (32, [2500], [192], [1])):
+        case = Case(seed=seed, H=12, D=128, lens=lens, bf16=True, amode=1, snap=64, start=start,
+                    warm=warm, N=8)
+        p1, o1 = case.run_gpu()
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        p2 = gdn.state_pool_create(case.ssm.cuda(), case.conv.cuda(), err)
+        o2 = torch.full_like(o1, -7.0)
+        gdn.conv_gdn_prefill_chunked_noalloc(
+            p2, case.layer, case.cu.cuda(), case.slots.cuda(), case.warm.cuda(), case.inp["x"].cuda(),
+            case.w.cuda(), case.inp["alpha"].cuda(), case.amode, case.inp["beta"].cuda(), o2,
+            max(lens), start_len=case.start.cuda(), snap_interval=case.snap,
+            track_slots=case.track.cuda(), next_track_idx=case.nxt.cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+        assert torch.equal(p1.ssm, p2.ssm) and torch.equal(p1.conv, p2.conv)
+        ref, o_ref, e = case.run_oracle()
+        check(case, p1, o1, ref, o_ref)
+
+
 @pytest.mark.parametrize("path", [ONE, TWO], ids=["one-kernel", "two-kernel"])
 def test_prefill_warm_gdn_subset(path):
     """32 heads, K=V=128, scalar decay, fp32 pool, warm starts at a 6144
