@@ -15,16 +15,17 @@
 //             out[b][n]
 //
 // Layout and work split.  A workgroup owns a block of state rows of one
-// (request, head).  It visits the nodes grouped by parent (a stable sort by
-// parent index, which still puts every parent before its children because a
-// parent's index is smaller than its children's): a parent's state is loaded
-// once into registers and every child of it is computed from that copy, so the
-// state stream reads each parent once instead of once per child.  When a group's
-// parent is the node computed just before (a chain), its state is carried over
-// in registers and not read at all.  Every lane owns the same 16-byte row pieces
-// for every node, so a node's state is re-read only by the lane that stored it:
-// in-order memory access within a lane makes that read see the store, and no
-// barrier is needed for the state.  The conv windows are built from x and the
+// (request, head).  It visits the nodes depth first (preorder, children in index
+// order), so every node's parent is either the node visited just before or one
+// of its ancestors on the current path.  The parent state a node starts from
+// comes from registers: the node just computed (carried over), or the kept state
+// of the live slot or of the current depth-1 or depth-2 ancestor (a node of
+// depth 1 or 2 that has children is kept when it is computed).  The only parents
+// read from memory, besides the live state once, are ancestors deeper than 2
+// that are not the node just computed.  Every lane owns the same 16-byte
+// row pieces for every node, so a node's state is re-read only by the lane that
+// stored it: in-order memory access within a lane makes that read see the
+// store, and no barrier is needed for the state.  The conv windows are built from x and the
 // live rows alone, never from another workgroup's node buffers, so the row
 // blocks of one head are independent; the block with the first rows writes the
 // node conv rows.
@@ -52,7 +53,7 @@ struct VerifyShape {
 
 template <int D, typename TS, int kAlphaMode>
 __global__ __launch_bounds__((VerifyShape<D, TS>::THREADS))
-__attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 1))) void gdn_verify_kernel(
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1))) void gdn_verify_kernel(
     const TS *__restrict__ ssm, const uint16_t *__restrict__ conv, int32_t *err, int slots,
     int heads, VerifyArgs a) {
   using SV = StateVec<TS>;
@@ -80,7 +81,8 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 1))) void gdn_verify_kernel(
   const int64_t tok0 = int64_t(b) * T;  // node 0's row in x, alpha, beta and out
 
   __shared__ int spar[kMaxTreeNodes];  // parent of each node
-  __shared__ int sord[kMaxTreeNodes];  // nodes in visiting order: by parent, then index
+  __shared__ int sord[kMaxTreeNodes];  // nodes in visiting order: depth-first preorder
+  __shared__ short sfirst[kMaxTreeNodes + 1], snext[kMaxTreeNodes], sdepth[kMaxTreeNodes];
   // per visiting position: {node, successor, successor's parent, flags}, see below
   __shared__ int4 splan[kMaxTreeNodes];
   __shared__ __attribute__((aligned(16))) float sy[2][3 * D];  // q | k | v, double buffered
@@ -94,36 +96,57 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 1))) void gdn_verify_kernel(
   }
   bad = __syncthreads_or(bad);
   if (!bad) {
-    // rank of node c = nodes with a smaller parent + earlier nodes with the same parent
-    for (int c = threadIdx.x; c < T; c += SH::THREADS) {
-      const int p = spar[c];
-      int pos = 0;
-      for (int i = 0; i < T; ++i) {
-        const int q = spar[i];
-        pos += (q < p) | ((q == p) & (i < c));
+    // children lists in index order (entry T stands for the live state), then the
+    // depth-first preorder by one thread (the tree has at most 1024 nodes)
+    if (threadIdx.x == 0) {
+      for (int n = 0; n <= T; ++n) sfirst[n] = -1;
+      for (int n = T - 1; n >= 0; --n) {
+        const int p = spar[n] < 0 ? T : spar[n];
+        snext[n] = sfirst[p];
+        sfirst[p] = short(n);
       }
-      sord[pos] = c;
+      int n = sfirst[T], k = 0;
+      while (n >= 0) {
+        sord[k++] = n;
+        sdepth[n] = short(spar[n] < 0 ? 1 : sdepth[spar[n]] + 1);
+        if (sfirst[n] >= 0) {
+          n = sfirst[n];
+        } else {
+          while (n >= 0 && snext[n] < 0) n = spar[n];
+          if (n >= 0) n = snext[n];
+        }
+      }
     }
     __syncthreads();
     // The walk's plan, one entry per position i, so that a step reads its tree
     // facts with one shared-memory load instead of chasing parents:
     //   x: node n,  y: successor nn (n itself after the last node),
-    //   z: nn's parent np (the group's parent state),
+    //   z: nn's parent np (the state nn starts from),
     //   w: bits 0-1 used = x rows in nn's window (its nearest ancestors, up to 3),
     //      bits 2-11 np's parent, 12-21 np's grandparent (window rows 1 and 0),
-    //      bit 22 carry (np is n: keep n's state), bit 23 regroup (load np's state).
+    //      bit 22 carry (np is n), bit 23 load (np's state from np's node buffer),
+    //      bits 24/25 take the kept depth-1 / depth-2 state, bits 26/27 keep n's
+    //      state as the depth-1 / depth-2 one (n has children), bit 28 take the
+    //      kept live state.
     for (int i = threadIdx.x; i < T; i += SH::THREADS) {
-      const int n = sord[i], p = spar[n];
+      const int n = sord[i];
       const bool last = i + 1 == T;
       const int nn = last ? n : sord[i + 1];
-      const int np = last ? p : spar[nn];
-      const bool carry = !last && np == n;
-      const bool regroup = !last && !carry && np != p;
+      const int np = last ? spar[n] : spar[nn];
+      const int dn = sdepth[n], dp = np >= 0 ? sdepth[np] : 0;
+      // a sibling successor starts from the parent state already in place
+      const bool carry = !last && np == n, keep = !last && np == spar[n];
+      const bool take0 = !last && !carry && !keep && dp == 0;
+      const bool take1 = !last && !carry && !keep && dp == 1, take2 = !last && !carry && !keep && dp == 2;
+      const bool load = !last && !carry && !keep && dp >= 3;
+      const bool kids = sfirst[n] >= 0;
       const int a1 = np >= 0 ? spar[np] : -1;
       const int a2 = a1 >= 0 ? spar[a1] : -1;
       const int used = np < 0 ? 0 : a1 < 0 ? 1 : a2 < 0 ? 2 : 3;
       splan[i] = make_int4(n, nn, np, used | (max(a1, 0) << 2) | (max(a2, 0) << 12) |
-                                          (int(carry) << 22) | (int(regroup) << 23));
+                                          (int(carry) << 22) | (int(load) << 23) | (int(take1) << 24) |
+                                          (int(take2) << 25) | (int(kids && dn == 1) << 26) |
+                                          (int(kids && dn == 2) << 27) | (int(take0) << 28));
     }
     __syncthreads();
   }
@@ -153,13 +176,17 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 1))) void gdn_verify_kernel(
   auto block = [&](const TS *base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<TS *>(base), 0, kBlockBytes, 0x00020000);
   };
-  SR cur[ITERS];  // the current group's parent state, in the pool dtype
+  SR cur[ITERS];  // the parent state of the node being computed, in the pool dtype
+  // the kept states of the live slot and of the current depth-1 and depth-2 ancestors
+  SR keep0[ITERS], keep1[ITERS], keep2[ITERS];
   {
     const __amdgpu_buffer_rsrc_t lr = block(live);
 #pragma unroll
     for (int it = 0; it < ITERS; ++it)
       if (ROWS % RPI == 0 || it * RPI + row_in_group < ROWS)
         cur[it] = __builtin_bit_cast(SR, __builtin_amdgcn_raw_buffer_load_b128(lr, loff, it * kPieceStep, 0));
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) keep0[it] = cur[it];
   }
 
   // ---- conv items: CW channels of the head's q | k | v per thread ------------
@@ -234,7 +261,9 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 1))) void gdn_verify_kernel(
     // the next node: a sibling (same parent state), the child of this node
     // (carry this node's state), or the first child of an earlier node (load)
     const bool carry = (fl >> 22) & 1;
-    const bool regroup = (fl >> 23) & 1;  // then np >= 0: only the first group has -1
+    const bool regroup = (fl >> 23) & 1;  // np's state from its node buffer
+    const bool take0 = (fl >> 28) & 1, take1 = (fl >> 24) & 1, take2 = (fl >> 25) & 1;
+    const bool keepn1 = (fl >> 26) & 1, keepn2 = (fl >> 27) & 1;
     if (conv_lane) {
 #pragma unroll
       for (int e = 0; e < CW; ++e) {
@@ -321,7 +350,12 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 1))) void gdn_verify_kernel(
 #pragma unroll
         for (int e = 0; e < VEC; ++e) s[e] = fmaf(d, kk[e], s[e]);
         const SR w = SV::from_f32(s);  // what the pool dtype holds: a child starts from this
+        if (keepn1) keep1[it] = w;
+        if (keepn2) keep2[it] = w;
         if (carry) cur[it] = w;
+        else if (take0) cur[it] = keep0[it];
+        else if (take1) cur[it] = keep1[it];
+        else if (take2) cur[it] = keep2[it];
         else if (regroup)
           cur[it] = __builtin_bit_cast(SR, __builtin_amdgcn_raw_buffer_load_b128(nsrc, loff, it * kPieceStep, 0));
         // The piece offset goes into the lane offset, not the scalar offset: a
