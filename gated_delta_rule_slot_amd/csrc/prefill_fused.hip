@@ -51,8 +51,7 @@ constexpr int kOrderedBatch = 1024;  // batches up to this size are taken longes
 // values, 1 KiB, lane-major.
 constexpr int kKN = 0;                    // K  [tb 4][ks 4][plane 2]
 constexpr int kQN = kKN + 32 * 1024;      // Q  [tb 4][ks 4][plane 2]
-constexpr int kKT = kQN + 32 * 1024;      // K^T [cb 8][ks 2][plane 2]
-constexpr int kMF = kKT + 32 * 1024;      // M  [pair 6][plane 2], pairs (tb, ks), ks <= tb/2
+constexpr int kMF = kQN + 32 * 1024;      // M  [pair 6][plane 2], pairs (tb, ks), ks <= tb/2
 // k = 16 A-operand fragments, split once where they are made: lane l holds row
 // l % 16, columns 4(l/16)..+3 of a 16x16 block as hi[4] | lo[4] bf16 (16 bytes)
 constexpr int kNF = kMF + 12 * 1024;      // -N_mk, blocks below the diagonal, [6][64][16 B]
@@ -80,12 +79,10 @@ __device__ __forceinline__ int xv_off(int row, int byte) {
 __device__ __forceinline__ int pair_idx(int tb, int ks) { return tb < 2 ? tb : 2 * tb - 2 + ks; }
 
 // Operand lane l of a K or Q fragment idx (= tb * 4 + ks) is stored in slot
-// l ^ (idx & 3), and of a K^T fragment idx (= cb * 2 + ks) in slot l ^ (cb & 7).
-// The writers fill several fragments at once with lanes that would otherwise
-// share banks; the XOR spreads them, and a reader's 8-lane groups still cover
-// 8 distinct 16-byte slots.
+// l ^ (idx & 3).  The writers fill several fragments at once with lanes that
+// would otherwise share banks; the XOR spreads them, and a reader's 8-lane groups
+// still cover 8 distinct 16-byte slots.
 __device__ __forceinline__ int kn_slot(int idx, int l) { return l ^ (idx & 3); }
-__device__ __forceinline__ int kt_slot(int idx, int l) { return l ^ ((idx >> 1) & 7); }
 __device__ __forceinline__ int nf_idx(int m, int k) { return m * (m - 1) / 2 + k; }  // m > k
 
 __device__ __forceinline__ void split4_put(char *lds, int off, int lane, const f32x4 &v) {
@@ -102,6 +99,36 @@ __device__ __forceinline__ Split frag_lds(const char *lds, int off, int idx, int
   Split s;
   s.hi = *reinterpret_cast<const bf16x8 *>(lds + off + (2 * idx) * 1024 + lane * 16);
   s.lo = *reinterpret_cast<const bf16x8 *>(lds + off + (2 * idx + 1) * 1024 + lane * 16);
+  return s;
+}
+
+// A K^T operand fragment (rows = channels 16cb..16cb+15, k = tokens 32ks + pk)
+// read from the K fragments with the gfx950 transposing LDS read: within each
+// 16-lane group, ds_read_b64_tr_b16 hands lane 4a + b element b of the 4 x 16-bit
+// chunk addressed by lane 4k + a, as its element k.  So lane 4k + a of group g
+// addresses channels 16cb + 4a..+3 of token 32ks + 4g + k (first read) or
+// 32ks + 16 + 4g + k (second read); in a K fragment those four channels are one
+// 8-byte half of a lane's slot.
+typedef short s16x4t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4t lds_read_tr16(const char *lds, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4t *)(const_cast<char *>(lds) + off));
+}
+__device__ __forceinline__ Split kt_frag(const char *lds, int cb, int ks, int lane) {
+  const int g = lane >> 4, a = lane & 3, k = (lane >> 2) & 3;
+  const int kc = cb >> 1, e0 = 4 * (cb & 1);  // channel group of K, first slot of the half
+  s16x4t h[2], l[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int t = 32 * ks + 16 * half + 4 * g + k;
+    const int idx = (t >> 4) * 4 + kc;
+    const int off = kKN + 2 * idx * 1024 + kn_slot(idx, (t & 15) + 16 * a) * 16 + 2 * e0;
+    h[half] = lds_read_tr16(lds, off);
+    l[half] = lds_read_tr16(lds, off + 1024);
+  }
+  Split s;
+  s.hi = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  s.lo = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l[0], l[1], 0, 1, 2, 3, 4, 5, 6, 7));
   return s;
 }
 
@@ -438,8 +465,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
       }
       // rows = tokens: element (t, 32ks + p) of fragment (t>>4, ks) sits in lane
       // (t&15) + 16((p&15)>>2), slot (p&3) + 4(p>>4)
-      // each value is split once (pairs of adjacent channels); K^T takes the same
-      // bf16 halves regrouped into pairs of adjacent tokens
+      // each value is split once (pairs of adjacent channels)
       const int fo = w < 4 ? kQN : kKN;
       Split2 sp[4][4];
 #pragma unroll
@@ -451,16 +477,6 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
         for (int hf = 0; hf < 2; ++hf)
           frag_put4w(lds, fo, (t >> 4) * 4 + (co >> 2), kn_slot(co >> 2, (t & 15) + 16 * (2 * (co & 1) + hf)),
                      4 * ((co >> 1) & 1), sp[rr][2 * hf], sp[rr][2 * hf + 1]);
-      }
-      if (w >= 4) {  // K^T: rows = channels, tokens along k in the same order
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = 8 * co + e, p = e >> 1, hh = e & 1;
-          const Split2 t01{halves(sp[0][p].hi, sp[1][p].hi, hh), halves(sp[0][p].lo, sp[1][p].lo, hh)};
-          const Split2 t23{halves(sp[2][p].hi, sp[3][p].hi, hh), halves(sp[2][p].lo, sp[3][p].lo, hh)};
-          frag_put4w(lds, kKT, (ch >> 4) * 2 + (tq >> 3), kt_slot((ch >> 4) * 2, (ch & 15) + 16 * (tq & 3)),
-                     4 * ((tq >> 2) & 1), t01, t23);
-        }
       }
     }
     lds_barrier();
@@ -616,7 +632,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
       S[kb] *= g63;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        S[kb] = mfma3(frag_lds(lds, kKT, kb * 2 + ks, kt_slot(kb * 2 + ks, lane)), dgop[ks], S[kb]);
+        S[kb] = mfma3(kt_frag(lds, kb, ks, lane), dgop[ks], S[kb]);
     }
 
     // snapshot at a boundary that ends this chunk
