@@ -327,12 +327,18 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
   auto load_chunk = [&](int t, int p0) {
     const int co = t & 15, tq = (t & 255) >> 4;
     const int ch0 = (w >> 2) * H * D + h * D + 8 * co;
+    // byte offsets: one multiply per thread, then a uniform step per row
+    const int rs = int(C) * 2;
+    const int xo = ((p0 + 4 * tq - 3) * int(C) + ch0) * 2;
 #pragma unroll
-    for (int i = 0; i < 7; ++i) xr[i] = row_x(p0 + 4 * tq - 3 + i, ch0);
+    for (int i = 0; i < 7; ++i)
+      xr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, xo + i * rs, 0, 0));
+    const int it0 = t, vo = ((p0 - 3 + (it0 >> 4)) * int(C) + 2 * H * D + h * D + 8 * (it0 & 15)) * 2;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {  // 67 staged rows x 16 chunks of 16 bytes
-      const int it = min(t + u * kFThreads, 67 * 16 - 1);
-      sv[u] = row_x(p0 - 3 + (it >> 4), 2 * H * D + h * D + 8 * (it & 15));
+      const int it = t + u * kFThreads;  // row (it >> 4) = (t >> 4) + 32u
+      const int off = it < 67 * 16 ? vo + 32 * u * rs : ((p0 - 3 + 66) * int(C) + 2 * H * D + h * D + 8 * 15) * 2;
+      sv[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
     }
     const int toff = (p0 + (t & 63)) * H * 4;  // outside [0, len) reads zero
     av = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ares, toff, 0, 0));
@@ -381,13 +387,18 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
         X1[tb] = mfma3(kf[i & 1], sop, X1[tb]);
         XQ[tb] = mfma3(qf[i & 1], sop, XQ[tb]);
       }
+      // staged row 16tb + 4g + q of this lane's V column: the row swizzle takes one
+      // value for q < 4 and another for q >= 4, the same in every tb
+      const int xb0 = kXV + 4 * g * 256 + (((vcol >> 3) ^ (2 * (g & 3))) << 4) + 2 * (vcol & 7);
+      const int xb1 = kXV + 4 * g * 256 + (((vcol >> 3) ^ (2 * ((g + 1) & 3))) << 4) + 2 * (vcol & 7);
   #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         // staged rows t0 .. t0 + 6 of this lane's V column, as pairs of adjacent rows
         const int t0 = 16 * tb + 4 * g;
         uint32_t xc[7], xp[6];
   #pragma unroll
-        for (int q = 0; q < 7; ++q) xc[q] = *reinterpret_cast<const uint16_t *>(lds + xv_off(t0 + q, 2 * vcol));
+        for (int q = 0; q < 7; ++q)
+          xc[q] = *reinterpret_cast<const uint16_t *>(lds + (q < 4 ? xb0 : xb1) + tb * 4096 + q * 256);
   #pragma unroll
         for (int q = 0; q < 6; ++q) xp[q] = halves(xc[q], xc[q + 1], 0);
   #pragma unroll
@@ -396,10 +407,10 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
           float acc = dot2_bf16(vw[0], xp[j], 0.f);
           acc = dot2_bf16(vw[1], xp[j + 2], acc);
           if (silu) acc = acc / (1.f + __expf(-acc));
-          const int pos = p0 + t;
-          const float v = (pos >= 0 && pos < rg.len) ? acc : 0.f;
+          // a token outside the request has b = 0, so its row of Y is zero whatever
+          // its conv value
           const float gt = LB[128 + t];
-          Y[tb][j] = LB[64 + t] * (v - gt * X1[tb][j]);
+          Y[tb][j] = LB[64 + t] * (acc - gt * X1[tb][j]);
           OQ[tb][j] = gt * XQ[tb][j];
         }
       }
@@ -440,16 +451,18 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
     {
       float y[4][8];
 #pragma unroll
+      // Tokens outside the request (padding before a warm start's first position,
+      // or past its end) keep their conv values: their b is zero, so their rows of
+      // Y, of N = Diag(b) A and of Dl are zero, and every product that reads their
+      // k or q multiplies it by a zero of Dl (their outputs are not stored).
       for (int rr = 0; rr < 4; ++rr) {
-        const int pos = p0 + 4 * tq + rr;
-        const bool valid = pos >= 0 && pos < rg.len;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           // taps (0, 1) and (2, 3) multiply positions (pos - 3, pos - 2) and (pos - 1, pos)
           float acc = dot2_bf16(iw[e >> 1][2 * (e & 1)], tok_pair(xr[rr], xr[rr + 1], e), 0.f);
           acc = dot2_bf16(iw[e >> 1][2 * (e & 1) + 1], tok_pair(xr[rr + 2], xr[rr + 3], e), acc);
           if (silu) acc = acc / (1.f + __expf(-acc));
-          y[rr][e] = valid ? acc : 0.f;
+          y[rr][e] = acc;
         }
         if (inorm) {  // wave-uniform; the 16 lanes of a token quad share the sum
           float ss = 0.f;
