@@ -334,15 +334,24 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
     for (int i = 0; i < 7; ++i)
       xr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, xo + i * rs, 0, 0));
     const int it0 = t, vo = ((p0 - 3 + (it0 >> 4)) * int(C) + 2 * H * D + h * D + 8 * (it0 & 15)) * 2;
+    // Every load instruction issued here costs the CU's vector-memory path, which
+    // bounds this phase: the third group of staged pieces (pieces 1024..1071) is
+    // loaded by wave 0 alone, and the decays and b (one token per lane) only by
+    // wave 0, which uses them.
 #pragma unroll
     for (int u = 0; u < 3; ++u) {  // 67 staged rows x 16 chunks of 16 bytes
-      const int it = t + u * kFThreads;  // row (it >> 4) = (t >> 4) + 32u
-      const int off = it < 67 * 16 ? vo + 32 * u * rs : ((p0 - 3 + 66) * int(C) + 2 * H * D + h * D + 8 * 15) * 2;
-      sv[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
+      if (u < 2 || w == 0) {
+        const int it = t + u * kFThreads;  // row (it >> 4) = (t >> 4) + 32u
+        const int off =
+            it < 67 * 16 ? vo + 32 * u * rs : ((p0 - 3 + 66) * int(C) + 2 * H * D + h * D + 8 * 15) * 2;
+        sv[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
+      }
     }
-    const int toff = (p0 + (t & 63)) * H * 4;  // outside [0, len) reads zero
-    av = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ares, toff, 0, 0));
-    bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bres, toff, 0, 0));
+    if (w == 0) {
+      const int toff = (p0 + (t & 63)) * H * 4;  // outside [0, len) reads zero
+      av = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ares, toff, 0, 0));
+      bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bres, toff, 0, 0));
+    }
   };
   load_chunk(tid, -rg.off);
   u32x4 iw[4];  // taps of the conv item's 8 channels
