@@ -504,6 +504,10 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
     lds_barrier();
 
     // ================= P2 =======================================================
+    // The next chunk's inputs are issued in two halves, so that the CU's vector-
+    // memory path is shared out: waves 0-3 (their P2 work is the latency-bound
+    // diagonal inverse) here, waves 4-7 at the start of P3.
+    if (w < 4) load_chunk(tid_c, p0 + 64);
     // a transposed M tile (lane holds M[16m+r][16k+4g+j]): decay mask, then this
     // lane's own slot run of the M fragment
     auto put_m = [&](int m, int k, const f32x4 &cc) {
@@ -613,7 +617,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
     lds_barrier();
 
     // ================= P3: Dl, O, state update ==================================
-    load_chunk(tid_c, p0 + 64);  // the next chunk's inputs (clamped on the last)
+    if (w >= 4) load_chunk(tid_c, p0 + 64);  // the next chunk's inputs (clamped on the last)
     // (I + N) Dl = Y by blocks: Dl_m = D_m (Y_m - sum_{k<m} N_mk Dl_k); each block of
     // Dl enters the next products as a k = 16 B operand straight from its accumulator
     f32x4 Dl[4];
