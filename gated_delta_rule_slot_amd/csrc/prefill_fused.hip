@@ -21,8 +21,8 @@
 // [16w, 16w + 16), held transposed (tiles of S^T, 16 channels x 16 rows) in fp32
 // accumulators.  Per chunk:
 //   P1  conv + norms of q and k (an item is 8 channels x 4 tokens) written as
-//       bf16 hi/lo MFMA fragments: K and Q (rows = tokens) and K^T (rows =
-//       channels); raw v rows staged; log2 decays (cumulated) and b (wave 0).
+//       bf16 hi/lo MFMA fragments K and Q (rows = tokens); raw v rows staged;
+//       log2 decays (cumulated) and b (wave 0).
 //   P2  waves 0-3: the diagonal 16x16 block m = w of N = Diag(b) A and the
 //       inverse D_m of I + N_mm by forward substitution; waves 4-7: the M
 //       fragments and the blocks of N below the diagonal blocks.  Then every
@@ -30,11 +30,14 @@
 //       and Y = Diag(b) (V - Diag(g) K S0^T).
 //   P3  every wave: Dl for its rows by block forward substitution,
 //       Dl_m = D_m (Y_m - sum_{k<m} N_mk Dl_k), then O (staged in LDS and
-//       written out as whole rows during the next chunk) and the state update;
+//       written out as whole rows during the next chunk) and the state update,
+//       whose K^T operand is read from the K fragments by transposing LDS reads;
 //       a snapshot when the chunk ends on a boundary.
 // Every contraction runs on bf16 MFMA in the three-product hi/lo split of
 // mfma.hpp.  Accumulators enter the next product without a transpose (the k order
 // pk), and fragments in LDS are stored in operand order.
+#include <type_traits>
+
 #include "common.hpp"
 #include "lanes.hpp"
 #include "mfma.hpp"
@@ -301,13 +304,15 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
   f32x4 Y[4], OQ[4];  // per chunk: Diag(b) (V - Diag(g) K S0^T) and Diag(g) Q S0^T
 
   // The staged outputs of the chunk at position p0 go out as 16-byte rows pieces
-  // (rows outside the request fall outside the resource and are dropped).
+  // (rows outside the request fall outside the resource and are dropped), NT
+  // threads writing 1024 / NT pieces each.
   const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
       a.out + (int64_t(rg.bos) * H + h) * D, 0, rg.len * H * D * 2, 0x00020000);
-  auto flush_out = [&](int t, int p0) {
+  auto flush_out = [&](int t, int p0, auto nt) {
+    constexpr int NT = decltype(nt)::value;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int it = t + u * kFThreads, row = it >> 4, pc = it & 15;
+    for (int u = 0; u < 1024 / NT; ++u) {
+      const int it = t + u * NT, row = it >> 4, pc = it & 15;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + kOS + row * kOP + 16 * pc);
       __builtin_amdgcn_raw_buffer_store_b128(v, ores, ((p0 + row) * H * D + 8 * pc) * 2, 0, 0);
     }
@@ -427,7 +432,6 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
 
 
     // ================= P1: conv, norms, fragments; staged v rows; decays =========
-    if (c > 0) flush_out(tid_c, p0 - 64);  // the previous chunk's outputs
     if (p0 < 3 && warm) {  // rows at positions -3..-1 come from the slot's conv rows
 #pragma unroll
       for (int i = 0; i < 7; ++i) xr[i] = row_vec(p0 + 4 * tq - 3 + i, (w >> 2) * H * D + h * D + 8 * co);
@@ -613,6 +617,9 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
       }
       }
     }
+    // the previous chunk's outputs (the staged rows are rewritten only in phase 3):
+    // here the stores meet no load issue on the vector-memory path
+    if (c > 0) flush_out(tid_c, p0 - 64, std::integral_constant<int, kFThreads>());
     ks0_products(p0);  // every wave, two per SIMD
     lds_barrier();
 
@@ -687,7 +694,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
   }
 
   // ---- end of the request: live slot -------------------------------------------
-  flush_out(tid, 64 * (rg.nch - 1) - rg.off);
+  flush_out(tid, 64 * (rg.nch - 1) - rg.off, std::integral_constant<int, kFThreads>());
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) store_s4(Slive + int64_t(vcol) * D + 16 * kb + 4 * g, S[kb]);
   // read every new conv row before writing any: the old rows may be inputs
