@@ -169,7 +169,14 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
 
   const PrefillArgs &a = ka.a;
   const int H = ka.heads;
-  const int b = blockIdx.x / ka.w, cl = blockIdx.x % ka.w, c = ka.c0 + cl, h = blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs in turn; each XCD is given a contiguous
+  // range of (chunk, head) items with the head fastest, so the heads of one chunk,
+  // which read adjacent pieces of the same input and decay rows, run together on
+  // one XCD and share its L2.
+  const int nblk = gridDim.x * gridDim.y, lin = blockIdx.y * gridDim.x + blockIdx.x;
+  const int qn = nblk / 8, rn = nblk % 8, xcd = lin % 8;
+  const int id = xcd * qn + min(xcd, rn) + lin / 8;
+  const int h = id % H, bc = id / H, b = bc / ka.w, cl = bc % ka.w, c = ka.c0 + cl;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
