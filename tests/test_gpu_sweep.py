@@ -62,6 +62,35 @@ def test_prefill_random_cases(i):
         check(case, pool, out, ref, o_ref, o_exact=o_exact)
 
 
+ONE_KERNEL_LENGTHS = [1, 5, 63, 64, 65, 130, 257, 400, 700]
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_prefill_one_kernel_random_cases(i):
+    """The one-kernel path (decay per head, head dim 128) on random batches of
+    longer requests: warm and cold starts at arbitrary positions, fp32 or bf16
+    pool, norm and SiLU flags, snapshots every boundary or the last of each parity."""
+    r = np.random.default_rng(90000 + i)
+    H = int(r.integers(1, 5))
+    B = int(r.integers(1, 7))
+    lens = [int(v) for v in r.choice(ONE_KERNEL_LENGTHS, size=B)]
+    bf16 = bool(r.integers(0, 2))
+    flags = int(r.choice([1, 3, 5, 7]))
+    snap = int(r.choice([0, 64, 128]))
+    warm = [int(v) for v in r.integers(0, 2, size=B)]
+    start = [int(v) for v in r.integers(0, 400, size=B)]
+    path = ONE | (32 if r.integers(0, 3) == 0 else 0)  # GDN_F_SNAP_LAST_ONLY
+    print(f"one-kernel sweep {i}: H={H} lens={lens} bf16={bf16} flags={flags} snap={snap} "
+          f"warm={warm} start={start} path={path}", flush=True)
+    case = Case(seed=91000 + i, H=H, D=128, lens=lens, bf16=bf16, amode=0, warm=warm, start=start,
+                flags=flags, scale=0.75, snap=snap, path=path)
+    pool, out = case.run_gpu()
+    assert int(pool.err_word.item()) == 0
+    ref, o_ref, e, o_exact = case.run_oracle(exact=True)
+    assert e == 0
+    check(case, pool, out, ref, o_ref, o_exact=o_exact)
+
+
 @pytest.mark.parametrize("i", range(12))
 def test_decode_random_cases(i):
     r = np.random.default_rng(7000 + i)
