@@ -169,13 +169,13 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
 
   const PrefillArgs &a = ka.a;
   const int H = ka.heads;
-  // Workgroups are dealt to the 8 XCDs in turn; each XCD is given a contiguous
-  // range of (chunk, head) items with the head fastest, so the heads of one chunk,
-  // which read adjacent pieces of the same input and decay rows, run together on
-  // one XCD and share its L2.
-  const int nblk = gridDim.x * gridDim.y, lin = blockIdx.y * gridDim.x + blockIdx.x;
-  const int qn = nblk / 8, rn = nblk % 8, xcd = lin % 8;
-  const int id = xcd * qn + min(xcd, rn) + lin / 8;
+  // (chunk, head) items in dispatch order with the head fastest: the heads of one
+  // chunk, which read adjacent pieces of the same input and decay rows and write
+  // adjacent records, run at the same time.  (Measured on MI355X against the chunk
+  // fastest: 4% faster for a 64-request window, 3% for one long request.  Keeping
+  // each XCD on one contiguous range of items as well was 9% slower for the
+  // 64-request window.)
+  const int id = blockIdx.y * gridDim.x + blockIdx.x;
   const int h = id % H, bc = id / H, b = bc / ka.w, cl = bc % ka.w, c = ka.c0 + cl;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
