@@ -247,7 +247,17 @@ __global__ __launch_bounds__((ReplayShape<D, TS>::THREADS)) void replay_commit_k
   typedef typename CV::raw CR;
   constexpr bool PERCH = kAlphaMode == GDN_ALPHA_PER_CHANNEL;
 
-  const int h = blockIdx.x, b = blockIdx.y;
+  // (request, head) from the launch index with each XCD given a contiguous run of
+  // pairs, heads fastest, whose state blocks are adjacent in the pool (as in the
+  // decode kernel; measured 2% faster here, and 2% slower for the verify kernels)
+  int h, b;
+  {
+    const int n = int(gridDim.x) * int(gridDim.y), w = int(blockIdx.y * gridDim.x + blockIdx.x);
+    const int q = n >> 3, rm = n & 7, x = w & 7, i = w >> 3;
+    const int id = (x < rm ? x * (q + 1) : rm * (q + 1) + (x - rm) * q) + i;
+    h = id % int(gridDim.x);
+    b = id / int(gridDim.x);
+  }
   const int H = heads, P = a.ring.positions;
   const int lane = threadIdx.x & 63, part = threadIdx.x >> 6;
   const int64_t C = int64_t(H) * 3 * D;
