@@ -71,7 +71,18 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1))) void gdn_verify_kernel(
   typedef typename CV::raw CR;
   typedef typename SV::raw SR;
 
-  const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  // (request, head) from the launch index with each XCD given a contiguous run of
+  // pairs, heads fastest: the node buffers of a request's heads are adjacent
+  // (measured 1.5-2.5% faster on the 32-request, 63-node launch)
+  int h, b;
+  {
+    const int n = int(gridDim.x) * int(gridDim.y), w = int(blockIdx.y * gridDim.x + blockIdx.x);
+    const int q = n >> 3, rm = n & 7, x = w & 7, i = w >> 3;
+    const int id = (x < rm ? x * (q + 1) : rm * (q + 1) + (x - rm) * q) + i;
+    h = id % int(gridDim.x);
+    b = id / int(gridDim.x);
+  }
+  const int split = blockIdx.z;
   const int T = a.nodes;
   const int H = heads;
   const int64_t C = int64_t(H) * 3 * D;
