@@ -211,6 +211,71 @@ def run_kda_prefill(torch, gdn, wl, dev, reps=5):
             "cu_parallelism_ceiling": "serial scan over 96 chunks on 12 heads x 8 value tiles = 96 of 256 CUs"}
 
 
+def run_kda_batch_prefill(torch, gdn, wl, dev, reps=3, B=64, ws_cap=8 << 30):
+    """The KDA prefill shape (12 heads, K=V=128, per-channel decay, bf16 pool) for a
+    batch of 64 requests x 6144 tokens, cold, every 64-token boundary stored to the
+    request's ping-pong track slots.  The library's default path (768 (request, head)
+    units: the one-kernel prefill) and the two-kernel path are timed on the same call."""
+    cfg = wl.KDA_PREFILL
+    H, D, Tr = cfg.heads, cfg.head_k, 6144
+    C = H * 3 * D
+    T = B * Tr
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 1)
+    x = torch.randn(T, C, generator=g, device=dev, dtype=torch.bfloat16)
+    alpha = torch.sigmoid(torch.randn(T, H, D, generator=g, device=dev) + 3.0)
+    beta = torch.sigmoid(torch.randn(T, H, generator=g, device=dev))
+    w = wl.conv_weights(wl.generator(cfg.seed + 1), C).to(dev)
+    N = 3 * B + 1
+    ssm = torch.zeros(1, N, H, D, D, dtype=torch.bfloat16, device=dev)
+    conv = torch.zeros(1, N, 3, C, dtype=torch.bfloat16, device=dev)
+    pool = gdn.state_pool_create(ssm, conv, torch.zeros(1, dtype=torch.int32, device=dev))
+    cu = wl.cu_seqlens([Tr] * B).to(dev)
+    slots = torch.arange(1, B + 1, dtype=torch.int32, device=dev)
+    track = torch.arange(B + 1, 3 * B + 1, dtype=torch.int32, device=dev).reshape(B, 2).contiguous()
+    cold = torch.zeros(B, dtype=torch.int32, device=dev)
+    start = torch.zeros(B, dtype=torch.int32, device=dev)
+    nxt = torch.zeros(B, dtype=torch.int32, device=dev)
+    out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(min(gdn.gdn_prefill_workspace_bytes(pool, B, Tr), ws_cap), dtype=torch.uint8, device=dev)
+
+    def call(flags, workspace):
+        gdn.conv_gdn_prefill_chunked(pool, 0, cu, slots, cold, x, w, alpha, cfg.alpha_mode, beta, out, Tr,
+                                     start_len=start, flags=flags, snap_interval=64, track_slots=track,
+                                     next_track_idx=nxt, workspace=workspace)
+
+    def timed(flags, workspace):
+        call(flags, workspace)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a, b = event_pair()
+            a.record()
+            call(flags, workspace)
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return sorted(ms)[len(ms) // 2] / 1e3
+
+    t_one = timed(gdn.L2NORM_K, None)
+    t_two = timed(gdn.L2NORM_K | gdn.PREFILL_TWO_KERNEL, ws)
+    assert int(pool.err_word.item()) == 0
+    flops = T * H * 140.6e3
+    io = T * (C * 2 + H * D * 4 + H * 4 + H * D * 2) + C * 8
+    byts = io + B * ((Tr // 64) * (H * D * D * 2 + 3 * C * 2) + H * D * D * 2 + 3 * C * 2)
+    del pool, ssm, conv, x, alpha, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": "KDA chunked prefill, batch: 12 heads, K=V=128, 64 x 6144 tokens, cold, "
+                        "snapshot every 64, bf16 pool",
+            "prefill_path": "one kernel (library default for 768 (request, head) units)",
+            "tokens": T, "ms": t_one * 1e3, "tokens_per_s": T / t_one,
+            "hbm_frac": byts / t_one / 1e9 / HBM_PEAK_GBS,
+            "mfma_util_vs_bf16_peak": flops / t_one / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "algorithmic_bytes": byts, "algorithmic_flops": flops,
+            "two_kernel_ms": t_two * 1e3, "two_kernel_tokens_per_s": T / t_two,
+            "workspace_bytes_two_kernel": int(ws_cap)}
+
+
 # ------------------------------------------------- KDA decode with tracking --
 def run_kda_decode_tracking(torch, gdn, wl, dev, steps=16, warmup=2):
     """69 KDA layers per step, batch 256, bf16 pool of 1024 slots, per-channel decay,
@@ -632,8 +697,8 @@ def main():
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
-    ap.add_argument("--extra", default="kda_prefill,restore,kda_decode_tracking,warm_prefill,"
-                    "spec_verify,replayssm", help="comma-separated secondary workloads to run")
+    ap.add_argument("--extra", default="kda_prefill,kda_batch_prefill,restore,kda_decode_tracking,"
+                    "warm_prefill,spec_verify,replayssm", help="comma-separated secondary workloads to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -652,6 +717,7 @@ def main():
     value = r["tokens"] / r["elapsed"]
     extra = {"hbm_copy_calibration_GBps": copy_calibration(torch, dev)}
     runs = {"kda_prefill": ("KDA prefill", run_kda_prefill),
+            "kda_batch_prefill": ("KDA prefill, batch of 64 requests", run_kda_batch_prefill),
             "restore": ("restore", run_restore),
             "kda_decode_tracking": ("KDA decode with tracking (69 layers)", run_kda_decode_tracking),
             "warm_prefill": ("prefix-hit restore + warm prefill (24 layers)", run_warm_prefill),

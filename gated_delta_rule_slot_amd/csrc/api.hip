@@ -192,10 +192,9 @@ gdn_status prefill_entry(
   if ((flags & GDN_F_PREFILL_ONE_KERNEL) && (flags & GDN_F_PREFILL_TWO_KERNEL))
     return fail(GDN_ERR_ARG, "GDN_F_PREFILL_ONE_KERNEL and GDN_F_PREFILL_TWO_KERNEL both set");
   // (the one-kernel path addresses a request's rows with 32-bit byte offsets)
-  const bool one_ok = alpha_mode == GDN_ALPHA_PER_HEAD && pool->d.head_k == 128 &&
-                      int64_t(max_seqlen) * pool->C * 2 < (int64_t(1) << 31);
+  const bool one_ok = pool->d.head_k == 128 && int64_t(max_seqlen) * pool->C * 2 < (int64_t(1) << 31);
   if ((flags & GDN_F_PREFILL_ONE_KERNEL) && !one_ok)
-    return fail(GDN_ERR_UNSUPPORTED, "the one-kernel prefill serves a decay per head at head dim 128 (and max_seqlen * channels * 2 < 2^31)");
+    return fail(GDN_ERR_UNSUPPORTED, "the one-kernel prefill serves head dim 128 (and max_seqlen * channels * 2 < 2^31)");
   const bool one_kernel = (flags & GDN_F_PREFILL_ONE_KERNEL) ||
                           (one_ok && !(flags & GDN_F_PREFILL_TWO_KERNEL) &&
                            int64_t(batch) * pool->d.heads >= kOneKernelMinUnits);

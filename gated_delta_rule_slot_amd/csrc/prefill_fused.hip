@@ -117,7 +117,9 @@ __device__ __forceinline__ s16x4t lds_read_tr16(const char *lds, int off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4t *)(const_cast<char *>(lds) + off));
 }
-__device__ __forceinline__ Split kt_frag(const char *lds, int cb, int ks, int lane) {
+// (base: the fragment region; SLOT: its lane-slot permutation)
+template <typename SLOT>
+__device__ __forceinline__ Split kt_frag_at(const char *lds, int base, SLOT slot, int cb, int ks, int lane) {
   const int g = lane >> 4, a = lane & 3, k = (lane >> 2) & 3;
   const int kc = cb >> 1, e0 = 4 * (cb & 1);  // channel group of K, first slot of the half
   s16x4t h[2], l[2];
@@ -125,7 +127,7 @@ __device__ __forceinline__ Split kt_frag(const char *lds, int cb, int ks, int la
   for (int half = 0; half < 2; ++half) {
     const int t = 32 * ks + 16 * half + 4 * g + k;
     const int idx = (t >> 4) * 4 + kc;
-    const int off = kKN + 2 * idx * 1024 + kn_slot(idx, (t & 15) + 16 * a) * 16 + 2 * e0;
+    const int off = base + 2 * idx * 1024 + slot(idx, (t & 15) + 16 * a) * 16 + 2 * e0;
     h[half] = lds_read_tr16(lds, off);
     l[half] = lds_read_tr16(lds, off + 1024);
   }
@@ -133,6 +135,9 @@ __device__ __forceinline__ Split kt_frag(const char *lds, int cb, int ks, int la
   s.hi = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
   s.lo = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l[0], l[1], 0, 1, 2, 3, 4, 5, 6, 7));
   return s;
+}
+__device__ __forceinline__ Split kt_frag(const char *lds, int cb, int ks, int lane) {
+  return kt_frag_at(lds, kKN, [](int idx, int l) { return kn_slot(idx, l); }, cb, ks, lane);
 }
 
 // 4 consecutive values of one fragment lane, both planes, already split
@@ -705,14 +710,711 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
   if (tid < 144) *reinterpret_cast<u32x4 *>(conv_live + row * C + ch) = nv;
 }
 
+// =========================================================== decay per channel ==
+// The same walk for a decay per channel (the KDA form).  With L_t the log2 decay
+// of each channel cumulated from the chunk start, g_t = 2^L_t is a vector, and the
+// decay factor of a pair (t, i) splits as 2^L_t 2^-L_i.  In a chunk where every
+// channel keeps g_63 >= 2^-96, these factors lie within 2^+-96 and are folded into
+// three operand planes built once per chunk (rows = tokens):
+//     P = k . g,   R = k . g^-1,   Q' = q . g
+//     A = P R^T (i < t),   M = Q' R^T (i <= t)
+//     (I + Diag(b) A) Dl = Diag(b) (V - P S0^T)
+//     O = Q' S0^T + M Dl,   S_end = (S0 + Dl^T R) Diag(g_63)
+// (the derivation: unroll S_t = S_{t-1} Diag(a_t) + d_t k_t^T from the chunk start;
+// S_{t-1} Diag(a_t) = S0 Diag(g_t) + sum_{i<t} d_i (k_i . 2^(L_t - L_i))^T).  The
+// planes hold the conv outputs before the key and query norms, which are scalars
+// per token and are applied outside the products.  A conv item here is 4 channels x
+// 4 tokens of both q and k, laid out so that the 16 token groups of a channel are
+// the 16 lanes of a row: the decay products are scanned across the row with DPP.
+// A chunk in which some channel decays below 2^-96 is run token by token instead,
+// which is exact for any decay down to a = 0.
+constexpr int kAP = 0;                         // P  [tb 4][ks 4][plane 2]
+constexpr int kAQ = kAP + 32 * 1024;           // Q'
+constexpr int kAR = kAQ + 32 * 1024;           // R (a chunk run token by token: a, fp32 [64][128])
+constexpr int kAM = kAR + 32 * 1024;           // M  [pair 6][plane 2]
+constexpr int kANF = kAM + 12 * 1024;          // -N_mk
+constexpr int kADF = kANF + 6 * 1024;          // D_m
+constexpr int kALD = kADF + 4 * 1024;          // diagonal blocks; in phase 1 the norm partial sums [8][64][2]
+constexpr int kALB = kALD + 4 * 16 * kBP * 4;  // b, 1/|q|, 1/|k| per token; g_63 per channel; flags
+constexpr int kAXV = kALB + 336 * 4;           // raw v rows, as kXV
+constexpr int kAOS = kAXV + 67 * 256;          // outputs, as kOS
+constexpr int kAW = kAOS + 64 * kOP;           // conv taps of q and k, bf16 [2][128][4]
+constexpr int kALdsBytes = kAW + 2 * 128 * 8;
+static_assert(kALdsBytes <= 160 * 1024, "LDS budget");
+static_assert(8 * 64 * 2 * 4 <= 4 * 16 * kBP * 4, "norm partial sums fit the diagonal-block region");
+constexpr int kLbIq = 64, kLbIk = 128, kLbG = 192, kLbFlag = 320;  // float offsets in the kALB block
+constexpr float kPlaneFloor = 0x1p-96f;  // smallest g_63 the planes take
+
+// Lane-slot permutation of the fragments here: the writers of phase 1 fill four
+// fragments at once with lanes 16 apart; the XOR gives every lane of a fragment
+// its own bank group.
+__device__ __forceinline__ int ka_slot(int, int l) { return l ^ ((l >> 4) & 3); }
+
+__device__ __forceinline__ int xv_off_at(int base, int row, int byte) {
+  return base + row * 256 + ((((byte >> 4) ^ (2 * ((row >> 2) & 3))) << 4) | (byte & 15));
+}
+
+// product of v over the lanes at or below this one in its row of 16 (DPP row shifts;
+// a lane with no source multiplies by the 1.0 kept as the old value)
+template <int N>
+__device__ __forceinline__ float row_shr_or_one(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(v), 0x110 + N, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_prefix_prod(float v) {
+  v *= row_shr_or_one<1>(v);
+  v *= row_shr_or_one<2>(v);
+  v *= row_shr_or_one<4>(v);
+  v *= row_shr_or_one<8>(v);
+  return v;
+}
+// sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the gfx950 row swaps)
+__device__ __forceinline__ float cross_row_sum(float v) {
+  const int lane = threadIdx.x & 63;
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v += __uint_as_float((lane & 16) ? r[0] : r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v += __uint_as_float((lane & 32) ? r[0] : r[1]);
+  return v;
+}
+
+template <typename TS>
+__global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) {
+  constexpr int D = kFD;
+  __shared__ __attribute__((aligned(16))) char lds[kALdsBytes];
+  float *LB = reinterpret_cast<float *>(lds + kALB);  // b, 1/|q|, 1/|k| (64 each), g_63 (128), flags
+  int *LF = reinterpret_cast<int *>(lds + kALB) + kLbFlag;
+  const auto slot_fn = [](int idx, int l) { return ka_slot(idx, l); };
+
+  const PrefillArgs &a = fa.a;
+  const int H = fa.heads;
+  const int h = blockIdx.x % H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // requests longest first, as in the kernel above
+  int b = blockIdx.x / H;
+  if (a.batch <= kOrderedBatch) {
+    __shared__ int s_req;
+    for (int i = tid; i < a.batch; i += kFThreads) {
+      const int ni = req_geom(a, i).nch;
+      int rank = 0;
+      for (int j = 0; j < a.batch; ++j) {
+        const int nj = req_geom(a, j).nch;
+        rank += (nj > ni) | ((nj == ni) & (j < i));
+      }
+      if (rank == b) s_req = i;
+    }
+    __syncthreads();
+    b = s_req;
+  }
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+
+  const ReqGeom rg = req_geom(a, b);
+  if (!rg.ok) {
+    if (fa.err && h == 0 && tid == 0) atomicOr(fa.err, GDN_ERRW_BAD_SEQLENS);
+    return;
+  }
+  const int64_t C = int64_t(H) * 3 * D;
+  const int slot = a.slot_table[b];
+  if (slot <= 0 || slot >= fa.slots) {
+    if (slot >= fa.slots && fa.err && h == 0 && tid == 0) atomicOr(fa.err, GDN_ERRW_BAD_SLOT);
+    for (int i = tid; i < rg.len * (D / 8); i += kFThreads) {
+      const int pos = i / (D / 8), o = i % (D / 8);
+      *reinterpret_cast<u32x4 *>(a.out + (int64_t(rg.bos + pos) * H + h) * D + 8 * o) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
+  const bool warm = a.has_initial_state[b] != 0;
+  TS *ssm = static_cast<TS *>(fa.ssm);
+  TS *Slive = ssm + ((int64_t(a.layer) * fa.slots + slot) * H + h) * int64_t(D) * D;
+  uint16_t *conv_live = fa.conv + (int64_t(a.layer) * fa.slots + slot) * kConvRows * C;
+
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.x) + int64_t(rg.bos) * C, 0, rg.len * int(C) * 2, 0x00020000);
+  // 4 channels (from ch) of the input row at request position q; positions -3..-1
+  // from the slot's conv rows on a warm start
+  auto row_vec8 = [&](int q, int ch) -> u32x2 {
+    if (q < 0 && q >= -3 && warm) return *reinterpret_cast<const u32x2 *>(conv_live + (3 + q) * C + ch);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xres, (q * int(C) + ch) * 2, 0, 0));
+  };
+  auto row_vec = [&](int q, int ch) -> u32x4 {
+    if (q < 0 && q >= -3 && warm) return *reinterpret_cast<const u32x4 *>(conv_live + (3 + q) * C + ch);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, (q * int(C) + ch) * 2, 0, 0));
+  };
+  auto conv_item = [&](int i, int done, int &ch, int &row) -> u32x4 {
+    row = i / 48;
+    const int oc = i % 48;
+    ch = (oc >> 4) * H * D + h * D + 8 * (oc & 15);
+    return row_vec(done - 3 + row, ch);
+  };
+
+  if (rg.nch == 0) {  // empty request: a cold start still zeroes the slot
+    if (!warm) {
+      for (int i = tid; i < D * D / 4; i += kFThreads) store_s4(Slive + 4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int i = tid; i < 144; i += kFThreads) {
+        const int row = i / 48, oc = i % 48;
+        const int64_t ch = int64_t(oc >> 4) * H * D + int64_t(h) * D + 8 * (oc & 15);
+        *reinterpret_cast<u32x4 *>(conv_live + row * C + ch) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    return;
+  }
+
+  const bool silu = (a.flags & GDN_F_CONV_SILU) != 0;
+  const bool nq = (a.flags & GDN_F_L2NORM_Q) != 0, nk = (a.flags & GDN_F_L2NORM_K) != 0;
+  const int vcol = 16 * w + r;
+  const u32x2 vw = *reinterpret_cast<const u32x2 *>(a.conv_w + (2 * int64_t(H) * D + int64_t(h) * D + vcol) * 4);
+
+  // state: lane (r, g) of wave w holds S[16w + r][16kb + 4g + j] in S[kb][j]
+  f32x4 S[8];
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (warm) S[kb] = load_s4<TS>(Slive + int64_t(vcol) * D + 16 * kb + 4 * g);
+  }
+
+  int sl = 0, nxt = 0, trk0 = 0, trk1 = 0, snap_lo = 0x7fffffff;
+  if (a.snap_interval > 0) {
+    sl = a.start_len[b];
+    nxt = a.next_track_idx[b];
+    trk0 = a.track_slots[2 * b];
+    trk1 = a.track_slots[2 * b + 1];
+    snap_lo = (a.flags & GDN_F_SNAP_LAST_ONLY)
+                  ? (sl + rg.len) / a.snap_interval - sl / a.snap_interval - 2
+                  : 0;
+  }
+
+  f32x4 Y[4], OQ[4];
+
+  const __amdgpu_buffer_rsrc_t ores = __builtin_amdgcn_make_buffer_rsrc(
+      a.out + (int64_t(rg.bos) * H + h) * D, 0, rg.len * H * D * 2, 0x00020000);
+  auto flush_out = [&](int t, int p0) {
+#pragma unroll
+    for (int u = 0; u < 1024 / kFThreads; ++u) {
+      const int it = t + u * kFThreads, row = it >> 4, pc = it & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + kAOS + row * kOP + 16 * pc);
+      __builtin_amdgcn_raw_buffer_store_b128(v, ores, ((p0 + row) * H * D + 8 * pc) * 2, 0, 0);
+    }
+  };
+
+  // Global inputs of a chunk, loaded one chunk ahead: 7 rows of q and of k for the
+  // thread's conv item (4 channels each), the item's decays (4 tokens x 4 channels),
+  // 3 staged v pieces, and b (wave 0, one token per lane).  Positions outside the
+  // request read zero through the resources' ranges.
+  u32x2 xq[7], xk[7];
+  f32x4 al[4];
+  u32x4 sv[3];
+  float bv;
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(a.alpha) + int64_t(rg.bos) * H * D, 0, rg.len * H * D * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(a.beta) + int64_t(rg.bos) * H + h, 0, rg.len * H * 4, 0x00020000);
+  auto load_chunk = [&](int t, int p0) {
+    const int tq = t & 15, c0 = 16 * w + 4 * ((t & 63) >> 4);
+    const int rs = int(C) * 2;
+    const int xo = ((p0 + 4 * tq - 3) * int(C) + h * D + c0) * 2, ko = xo + H * D * 2;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      xq[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xres, xo + i * rs, 0, 0));
+      xk[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xres, ko + i * rs, 0, 0));
+    }
+    const int ao = ((p0 + 4 * tq) * H + h) * D * 4 + c0 * 4;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      al[rr] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ares, ao + rr * H * D * 4, 0, 0));
+    const int vo = ((p0 - 3 + (t >> 4)) * int(C) + 2 * H * D + h * D + 8 * (t & 15)) * 2;
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      if (u < 2 || w == 0) {
+        const int it = t + u * kFThreads;
+        const int off =
+            it < 67 * 16 ? vo + 32 * u * rs : ((p0 - 3 + 66) * int(C) + 2 * H * D + h * D + 8 * 15) * 2;
+        sv[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
+      }
+    }
+    if (w == 0)
+      bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bres, (p0 + (t & 63)) * H * 4, 0, 0));
+  };
+  load_chunk(tid, -rg.off);
+  // conv taps of the head's q and k channels, kept in LDS (registers are short here)
+  if (tid < 128) {
+    const int part = tid >> 6, ch = tid & 63;  // 2 channels per thread
+    *reinterpret_cast<u32x4 *>(lds + kAW + (part * 128 + 2 * ch) * 8) =
+        *reinterpret_cast<const u32x4 *>(a.conv_w + (int64_t(part) * H * D + int64_t(h) * D + 2 * ch) * 4);
+  }
+  __syncthreads();
+
+#pragma unroll 1
+  for (int c = 0; c < rg.nch; ++c) {
+    const int p0 = 64 * c - rg.off;
+    int tid_c = tid;
+    asm volatile("" : "+v"(tid_c));
+    const int lane = tid_c & 63, r = lane & 15, g = lane >> 4, vcol = 16 * w + r;
+    // conv item: tokens 4tq..4tq+3, channels c0..c0+3 of q and of k
+    const int tq = lane & 15, cg = lane >> 4, c0 = 16 * w + 4 * cg;
+
+    // the item's conv outputs (after SiLU, before the norms)
+    auto conv_items = [&](float (&yq)[4][4], float (&yk)[4][4]) {
+      u32x4 wq[2], wk[2];  // taps of the item's channels, two channels per vector
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        wq[i] = *reinterpret_cast<const u32x4 *>(lds + kAW + (c0 + 2 * i) * 8);
+        wk[i] = *reinterpret_cast<const u32x4 *>(lds + kAW + (128 + c0 + 2 * i) * 8);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float accq = dot2_bf16(wq[e >> 1][2 * (e & 1)], halves(xq[rr][e >> 1], xq[rr + 1][e >> 1], e & 1), 0.f);
+          accq = dot2_bf16(wq[e >> 1][2 * (e & 1) + 1], halves(xq[rr + 2][e >> 1], xq[rr + 3][e >> 1], e & 1), accq);
+          float acck = dot2_bf16(wk[e >> 1][2 * (e & 1)], halves(xk[rr][e >> 1], xk[rr + 1][e >> 1], e & 1), 0.f);
+          acck = dot2_bf16(wk[e >> 1][2 * (e & 1) + 1], halves(xk[rr + 2][e >> 1], xk[rr + 3][e >> 1], e & 1), acck);
+          if (silu) {
+            accq = accq / (1.f + __expf(-accq));
+            acck = acck / (1.f + __expf(-acck));
+          }
+          yq[rr][e] = accq;
+          yk[rr][e] = acck;
+        }
+      }
+    };
+    // fragment of token t for this item: rows = tokens, channel c0 + e in lane
+    // (t & 15) + 16 cg, slot e + 4 (w & 1) of fragment (t >> 4, w >> 1)
+    auto put_item = [&](int off, int rr, const float *v) {
+      const int t = 4 * tq + rr, idx = (t >> 4) * 4 + (w >> 1);
+      frag_put4(lds, off, idx, ka_slot(idx, (t & 15) + 16 * cg), 4 * (w & 1), v);
+    };
+
+    // ================= P1: conv, planes, staged v rows, decays, norm sums =======
+    if (p0 < 3 && warm) {
+#pragma unroll
+      for (int i = 0; i < 7; ++i) {
+        xq[i] = row_vec8(p0 + 4 * tq - 3 + i, h * D + c0);
+        xk[i] = row_vec8(p0 + 4 * tq - 3 + i, H * D + h * D + c0);
+      }
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int it = min(tid_c + u * kFThreads, 67 * 16 - 1);
+        sv[u] = row_vec(p0 - 3 + (it >> 4), 2 * H * D + h * D + 8 * (it & 15));
+      }
+    }
+    if (w == 0) {
+      const int dpos = p0 + lane;
+      LB[lane] = (dpos >= 0 && dpos < rg.len) ? bv : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int it = tid_c + u * kFThreads;
+      if (it < 67 * 16) *reinterpret_cast<u32x4 *>(lds + xv_off_at(kAXV, it >> 4, 16 * (it & 15))) = sv[u];
+    }
+    {
+      float yq[4][4], yk[4][4];
+      conv_items(yq, yk);
+      // squared norms over this wave's 16 channels, per token, to the partial sums
+      {
+        float s[8];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          float a2 = 0.f, b2 = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a2 = fmaf(yq[rr][e], yq[rr][e], a2);
+            b2 = fmaf(yk[rr][e], yk[rr][e], b2);
+          }
+          s[2 * rr] = cross_row_sum(a2);
+          s[2 * rr + 1] = cross_row_sum(b2);
+        }
+        if (cg == 0) {
+          float *pt = reinterpret_cast<float *>(lds + kALD) + (w * 64 + 4 * tq) * 2;
+          *reinterpret_cast<f32x4 *>(pt) = f32x4{s[0], s[1], s[2], s[3]};
+          *reinterpret_cast<f32x4 *>(pt + 4) = f32x4{s[4], s[5], s[6], s[7]};
+        }
+      }
+      // decays: g_t per channel as a product (a token outside the request has a = 1)
+      f32x4 gf[4];
+      {
+        f32x4 run = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int pos = p0 + 4 * tq + rr;
+          const bool valid = pos >= 0 && pos < rg.len;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) run[e] *= valid ? al[rr][e] : 1.f;
+          gf[rr] = run;
+        }
+        f32x4 ex;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ex[e] = row_shr_or_one<1>(row_prefix_prod(run[e]));  // tokens < 4tq
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) gf[rr] *= ex;
+        bool bad = false;
+        if (tq == 15) {  // g_63 of the item's channels
+          *reinterpret_cast<f32x4 *>(LB + kLbG + c0) = gf[3];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bad |= !(gf[3][e] >= kPlaneFloor);
+        }
+        const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+        if (lane == 0) LF[w] = any_bad ? 1 : 0;
+      }
+      // the planes P = k g, R = k / g, Q' = q g
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float pv[4], rv[4], qv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = yk[rr][e] * gf[rr][e];
+          rv[e] = yk[rr][e] * __builtin_amdgcn_rcpf(gf[rr][e]);
+          qv[e] = yq[rr][e] * gf[rr][e];
+        }
+        put_item(kAP, rr, pv);
+        put_item(kAR, rr, rv);
+        put_item(kAQ, rr, qv);
+      }
+    }
+    lds_barrier();
+    // the norms (wave 0, one token per lane) and the chunk's path
+    if (w == 0) {
+      const float *pt = reinterpret_cast<const float *>(lds + kALD) + lane * 2;
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 8; ++ww) {
+        sq += pt[ww * 128];
+        sk += pt[ww * 128 + 1];
+      }
+      LB[kLbIq + lane] = nq ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 1.f;
+      LB[kLbIk + lane] = nk ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 1.f;
+      if (lane == 0) {
+        int f = 0;
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) f |= LF[ww];
+        LF[8] = f;
+      }
+    }
+    lds_barrier();
+    const int by_token = __builtin_amdgcn_readfirstlane(LF[8]);
+
+    if (!by_token) {
+      // ================= P2 =====================================================
+      if (w < 4) load_chunk(tid_c, p0 + 64);
+      // a transposed M tile (lane holds M[16m+r][16k+4g+j]): causal mask and norms
+      auto put_m = [&](int m, int k, const f32x4 &cc) {
+        const int t = 16 * m + r;
+        const float qt = LB[kLbIq + t];
+        float mv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 16 * k + 4 * g + j;
+          mv[j] = i <= t ? qt * LB[kLbIk + i] * cc[j] : 0.f;
+        }
+        frag_put4(lds, kAM, pair_idx(m, k >> 1), lane, 4 * (k & 1), mv);
+        if (m == k && !(m & 1)) {
+          const float z[4] = {0.f, 0.f, 0.f, 0.f};
+          frag_put4(lds, kAM, pair_idx(m, m >> 1), lane, 4, z);
+        }
+      };
+      if (w < 4) {
+        // diagonal block m of N = Diag(b) A: lane holds P_{16m+4g+j} . R_{16m+r}
+        const int m = w;
+        f32x4 c2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int idx = m * 4 + ks;
+          c2[ks & 1] = mfma3(frag_lds(lds, kAP, idx, ka_slot(idx, lane)), frag_lds(lds, kAR, idx, ka_slot(idx, lane)),
+                             c2[ks & 1]);
+        }
+        const f32x4 cc = c2[0] + c2[1];
+        float *blk = reinterpret_cast<float *>(lds + kALD) + m * 16 * kBP;
+        const float ki = LB[kLbIk + 16 * m + r];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 4 * g + j;
+          blk[t * kBP + r] = t > r ? LB[16 * m + t] * LB[kLbIk + 16 * m + t] * ki * cc[j] : 0.f;
+        }
+        wave_lds_sync();
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          float v = (t == r) ? 1.f : 0.f;
+#pragma unroll
+          for (int i = 0; i < t; ++i) v = fmaf(-blk[t * kBP + i], x[i], v);
+          x[t] = v;
+        }
+        wave_lds_sync();
+        if (g == 0) {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) blk[t * kBP + r] = x[t];
+        }
+        wave_lds_sync();
+        split4_put(lds, kADF + m * 1024, lane, ld4(blk + r * kBP + 4 * g));
+        // the diagonal M tile (m, m): lane holds R_{16m+4g+j} . Q'_{16m+r}
+        f32x4 cm[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int idx = m * 4 + ks;
+          cm[ks & 1] = mfma3(frag_lds(lds, kAR, idx, ka_slot(idx, lane)), frag_lds(lds, kAQ, idx, ka_slot(idx, lane)),
+                             cm[ks & 1]);
+        }
+        put_m(m, m, cm[0] + cm[1]);
+      } else {
+        // the M blocks below the diagonal and the N blocks, three tiles per wave,
+        // in the order of the kernel above; lane holds R_{16k+4g+j} . (Q' or P)_{16m+r}
+        constexpr uint64_t kTilesLo = 0x190d180c09140804ull, kTilesHi = 0x1e1d0e1cull;
+        auto tile_entry = [&](int q) {
+          const int i = (w - 4) * 3 + q;
+          return int(((i < 8 ? kTilesLo >> (8 * i) : kTilesHi >> (8 * (i - 8)))) & 0xff);
+        };
+#pragma unroll
+        for (int q0 = 0; q0 < 3; q0 += 2) {
+          f32x4 cc[3];
+#pragma unroll
+          for (int q = q0; q < min(q0 + 2, 3); ++q) cc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int q = q0; q < min(q0 + 2, 3); ++q) {
+              const int e = tile_entry(q);
+              const int m = (e >> 2) & 3, k = e & 3;
+              const int ia = k * 4 + ks, ib = m * 4 + ks;
+              cc[q] = mfma3(frag_lds(lds, kAR, ia, ka_slot(ia, lane)),
+                            frag_lds(lds, (e >> 4) ? kAP : kAQ, ib, ka_slot(ib, lane)), cc[q]);
+            }
+          }
+#pragma unroll
+          for (int q = q0; q < min(q0 + 2, 3); ++q) {
+            const int e = tile_entry(q);
+            const int m = (e >> 2) & 3, k = e & 3;
+            if ((e >> 4) == 0) {
+              put_m(m, k, cc[q]);
+            } else {  // -N_mk = -b_t A[t][i] / (|k_t| |k_i|)
+              const int t = 16 * m + r;
+              const float f = -LB[t] * LB[kLbIk + t];
+              f32x4 nv;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) nv[j] = f * LB[kLbIk + 16 * k + 4 * g + j] * cc[q][j];
+              split4_put(lds, kANF + nf_idx(m, k) * 1024, lane, nv);
+            }
+          }
+        }
+      }
+      if (c > 0) flush_out(tid_c, p0 - 64);
+      // Y = Diag(b) (V - P S0^T / |k|) and Q' S0^T / |q| for this wave's rows
+      {
+        f32x4 X1[4], XQ[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          X1[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          XQ[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        Split kf[2], qf[2], sop;
+        kf[0] = frag_lds(lds, kAP, 0, ka_slot(0, lane));
+        qf[0] = frag_lds(lds, kAQ, 0, ka_slot(0, lane));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ks = i >> 2, tb = i & 3;
+          if (i + 1 < 16) {
+            const int n = ((i + 1) & 3) * 4 + ((i + 1) >> 2);
+            kf[(i + 1) & 1] = frag_lds(lds, kAP, n, ka_slot(n, lane));
+            qf[(i + 1) & 1] = frag_lds(lds, kAQ, n, ka_slot(n, lane));
+          }
+          if (tb == 0) sop = split44(S[2 * ks], S[2 * ks + 1]);
+          X1[tb] = mfma3(kf[i & 1], sop, X1[tb]);
+          XQ[tb] = mfma3(qf[i & 1], sop, XQ[tb]);
+        }
+        const int xb0 = kAXV + 4 * g * 256 + (((vcol >> 3) ^ (2 * (g & 3))) << 4) + 2 * (vcol & 7);
+        const int xb1 = kAXV + 4 * g * 256 + (((vcol >> 3) ^ (2 * ((g + 1) & 3))) << 4) + 2 * (vcol & 7);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const int t0 = 16 * tb + 4 * g;
+          uint32_t xc[7], xp[6];
+#pragma unroll
+          for (int q = 0; q < 7; ++q)
+            xc[q] = *reinterpret_cast<const uint16_t *>(lds + (q < 4 ? xb0 : xb1) + tb * 4096 + q * 256);
+#pragma unroll
+          for (int q = 0; q < 6; ++q) xp[q] = halves(xc[q], xc[q + 1], 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = t0 + j;
+            float acc = dot2_bf16(vw[0], xp[j], 0.f);
+            acc = dot2_bf16(vw[1], xp[j + 2], acc);
+            if (silu) acc = acc / (1.f + __expf(-acc));
+            Y[tb][j] = LB[t] * (acc - LB[kLbIk + t] * X1[tb][j]);
+            OQ[tb][j] = LB[kLbIq + t] * XQ[tb][j];
+          }
+        }
+      }
+      lds_barrier();
+
+      // ================= P3: Dl, O, state update ================================
+      if (w >= 4) load_chunk(tid_c, p0 + 64);
+      f32x4 Dl[4];
+      {
+        Split4 db[3];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f32x4 acc = Y[m];
+#pragma unroll
+          for (int k = 0; k < m; ++k) acc = mfma3k16(split4_get(lds, kANF + nf_idx(m, k) * 1024, lane), db[k], acc);
+          Dl[m] = mfma3k16(split4_get(lds, kADF + m * 1024, lane), split4s(acc), f32x4{0.f, 0.f, 0.f, 0.f});
+          if (m < 3) db[m] = split4s(Dl[m]);
+        }
+      }
+      Split dop[2], dgop[2];
+      dop[0] = split44(Dl[0], Dl[1]);
+      dop[1] = split44(Dl[2], Dl[3]);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Dl[tb][j] *= LB[kLbIk + 16 * tb + 4 * g + j];  // Dl / |k|
+      dgop[0] = split44(Dl[0], Dl[1]);
+      dgop[1] = split44(Dl[2], Dl[3]);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f32x4 o = OQ[tb];
+#pragma unroll
+        for (int ks = 0; ks <= (tb >> 1); ++ks) o = mfma3(frag_lds(lds, kAM, pair_idx(tb, ks), lane), dop[ks], o);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint16_t *>(lds + kAOS + (16 * tb + 4 * g + j) * kOP + 2 * vcol) = f32_to_bf16(a.scale * o[j]);
+      }
+      // S^T = Diag(g_63) (S0^T + R^T Diag(1/|k|) Dl)
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) S[kb] = mfma3(kt_frag_at(lds, kAR, slot_fn, kb, ks, lane), dgop[ks], S[kb]);
+        S[kb] *= *reinterpret_cast<const f32x4 *>(LB + kLbG + 16 * kb + 4 * g);
+      }
+    } else {
+      // ================= the chunk token by token ===============================
+      // The planes again without the decay factors (k into P, q into Q'), and the
+      // decays themselves, fp32 [t][c], in R's place.
+      {
+        float yq[4][4], yk[4][4];
+        conv_items(yq, yk);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          put_item(kAP, rr, yk[rr]);
+          put_item(kAQ, rr, yq[rr]);
+          const int pos = p0 + 4 * tq + rr;
+          const bool valid = pos >= 0 && pos < rg.len;
+          f32x4 av = al[rr];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[e] = valid ? av[e] : 1.f;
+          *reinterpret_cast<f32x4 *>(lds + kAR + ((4 * tq + rr) * D + c0) * 4) = av;
+        }
+      }
+      if (c > 0) flush_out(tid_c, p0 - 64);
+      lds_barrier();
+      load_chunk(tid_c, p0 + 64);
+      const int xv0 = 2 * vcol;
+#pragma unroll 1
+      for (int t = 0; t < 64; ++t) {
+        const float bt = LB[t], qi = LB[kLbIq + t], ki = LB[kLbIk + t];
+        const float *arow = reinterpret_cast<const float *>(lds + kAR) + t * D + 4 * g;
+        // this lane's 32 channels of k and q: slots 0-3 are channels 32ks + 4g + j,
+        // slots 4-7 channels 32ks + 16 + 4g + j, of fragment (t >> 4, ks)
+        const int fl = ka_slot(0, (t & 15) + 16 * g) * 16;
+        float u = 0.f, sq = 0.f, kq = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int fo = 2 * ((t >> 4) * 4 + ks) * 1024 + fl;
+          const u32x4 kh = *reinterpret_cast<const u32x4 *>(lds + kAP + fo);
+          const u32x4 kl = *reinterpret_cast<const u32x4 *>(lds + kAP + fo + 1024);
+          const u32x4 qh = *reinterpret_cast<const u32x4 *>(lds + kAQ + fo);
+          const u32x4 ql = *reinterpret_cast<const u32x4 *>(lds + kAQ + fo + 1024);
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int kb = 2 * ks + hf;
+            const f32x4 a4 = *reinterpret_cast<const f32x4 *>(arow + 16 * kb);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float kv = bf16_elem(kh, 4 * hf + j) + bf16_elem(kl, 4 * hf + j);
+              const float qv = bf16_elem(qh, 4 * hf + j) + bf16_elem(ql, 4 * hf + j);
+              S[kb][j] *= a4[j];
+              u = fmaf(S[kb][j], kv, u);
+              sq = fmaf(S[kb][j], qv, sq);
+              kq = fmaf(kv, qv, kq);
+            }
+          }
+        }
+        u = cross_row_sum(u);
+        sq = cross_row_sum(sq);
+        kq = cross_row_sum(kq);
+        // v of row vcol at token t: conv of staged rows t..t+3
+        uint32_t xc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xc[q] = *reinterpret_cast<const uint16_t *>(lds + xv_off_at(kAXV, t + q, xv0));
+        float vt = dot2_bf16(vw[0], halves(xc[0], xc[1], 0), 0.f);
+        vt = dot2_bf16(vw[1], halves(xc[2], xc[3], 0), vt);
+        if (silu) vt = vt / (1.f + __expf(-vt));
+        const float dk = bt * (vt - ki * u) * ki;  // d_t / |k_t|
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int fo = 2 * ((t >> 4) * 4 + ks) * 1024 + fl;
+          const u32x4 kh = *reinterpret_cast<const u32x4 *>(lds + kAP + fo);
+          const u32x4 kl = *reinterpret_cast<const u32x4 *>(lds + kAP + fo + 1024);
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              S[2 * ks + hf][j] = fmaf(dk, bf16_elem(kh, 4 * hf + j) + bf16_elem(kl, 4 * hf + j), S[2 * ks + hf][j]);
+        }
+        // o_t = scale S_t q_t = scale (S' q + d (k . q))
+        if (g == 0)
+          *reinterpret_cast<uint16_t *>(lds + kAOS + t * kOP + 2 * vcol) =
+              f32_to_bf16(a.scale * qi * (sq + dk * kq));
+      }
+    }
+
+    // snapshot at a boundary that ends this chunk
+    if (a.snap_interval > 0) {
+      const int done = min(64 * (c + 1) - rg.off, rg.len);
+      const int n_end = sl + done;
+      const int j = n_end / a.snap_interval - sl / a.snap_interval - 1;
+      if (n_end % a.snap_interval == 0 && j >= snap_lo) {
+        const int dst = ((nxt + j) & 1) ? trk1 : trk0;
+        if (dst >= fa.slots) {
+          if (fa.err && tid == 0) atomicOr(fa.err, GDN_ERRW_BAD_TRACK_SLOT);
+        } else if (dst > 0) {
+          TS *Sd = ssm + ((int64_t(a.layer) * fa.slots + dst) * H + h) * int64_t(D) * D;
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) store_s4(Sd + int64_t(vcol) * D + 16 * kb + 4 * g, S[kb]);
+          uint16_t *cd = fa.conv + (int64_t(a.layer) * fa.slots + dst) * kConvRows * C;
+          if (tid < 144) {
+            int ch, row;
+            const u32x4 v = conv_item(tid, done, ch, row);
+            *reinterpret_cast<u32x4 *>(cd + row * C + ch) = v;
+          }
+        }
+      }
+    }
+    lds_barrier();
+  }
+
+  // ---- end of the request: live slot -------------------------------------------
+  flush_out(tid, 64 * (rg.nch - 1) - rg.off);
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) store_s4(Slive + int64_t(vcol) * D + 16 * kb + 4 * g, S[kb]);
+  int ch = 0, row = 0;
+  u32x4 nv = {0u, 0u, 0u, 0u};
+  if (tid < 144) nv = conv_item(tid, rg.len, ch, row);
+  __syncthreads();
+  if (tid < 144) *reinterpret_cast<u32x4 *>(conv_live + row * C + ch) = nv;
+}
+
 }  // namespace
 
 hipError_t launch_prefill_fused(const gdn_pool *p, const PrefillArgs &a, hipStream_t s) {
-  if (p->d.head_k != kFD || p->d.head_v != kFD || a.alpha_mode != GDN_ALPHA_PER_HEAD) return hipErrorInvalidValue;
+  if (p->d.head_k != kFD || p->d.head_v != kFD) return hipErrorInvalidValue;
   FArgs fa{a, p->d.ssm_base, static_cast<uint16_t *>(p->d.conv_base), p->d.err_word, p->d.slots, p->d.heads};
   const dim3 grid(unsigned(a.batch) * p->d.heads), block(kFThreads);
-  if (p->d.ssm_dtype == GDN_BF16) hipLaunchKernelGGL(prefill_fused_kernel<uint16_t>, grid, block, 0, s, fa);
-  else hipLaunchKernelGGL(prefill_fused_kernel<float>, grid, block, 0, s, fa);
+  const bool bf16 = p->d.ssm_dtype == GDN_BF16;
+  if (a.alpha_mode == GDN_ALPHA_PER_CHANNEL) {
+    if (bf16) hipLaunchKernelGGL(prefill_fused_kda_kernel<uint16_t>, grid, block, 0, s, fa);
+    else hipLaunchKernelGGL(prefill_fused_kda_kernel<float>, grid, block, 0, s, fa);
+  } else if (bf16) {
+    hipLaunchKernelGGL(prefill_fused_kernel<uint16_t>, grid, block, 0, s, fa);
+  } else {
+    hipLaunchKernelGGL(prefill_fused_kernel<float>, grid, block, 0, s, fa);
+  }
   return hipGetLastError();
 }
 

@@ -84,9 +84,11 @@ enum { GDN_ALPHA_PER_HEAD = 0, GDN_ALPHA_PER_CHANNEL = 1 };
 enum { GDN_F_L2NORM_K = 1u, GDN_F_L2NORM_Q = 2u, GDN_F_CONV_SILU = 4u };
 /* prefill path (conv_gdn_prefill_chunked only; with neither bit the library
  * chooses): ONE_KERNEL runs each (request, head) start to end in one workgroup with
- * the state on chip and takes no workspace (NULL and 0 are accepted); it serves a
- * decay per head (GDN_ALPHA_PER_HEAD) at head dim 128 with
- * max_seqlen * channels * 2 < 2^31, and suits batches of many requests.
+ * the state on chip and takes no workspace (NULL and 0 are accepted); it serves
+ * head dim 128 with max_seqlen * channels * 2 < 2^31, for a decay per head or per
+ * channel, and suits batches of many requests.  (With a decay per channel, a chunk
+ * of 64 tokens in which some channel decays below 2^-96 in all is run token by
+ * token, which is exact but several times slower.)
  * TWO_KERNEL prepares every chunk in parallel and then scans them; it serves every
  * shape, needs the workspace, and suits a few long requests. */
 enum { GDN_F_PREFILL_ONE_KERNEL = 8u, GDN_F_PREFILL_TWO_KERNEL = 16u };

@@ -102,8 +102,8 @@ def test_calls_reject_bad_arguments_before_launch():
             h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0, 1, fake,
             0, None, None, fake, 16, None) == -1
         assert "workspace" in B.last_error()
-        # prefill path bits: both at once, and the one-kernel path on a decay per
-        # channel (it serves a decay per head only)
+        # prefill path bits: both at once, and the one-kernel path at head dim 16
+        # (it serves head dim 128 only)
         assert B._lib.conv_gdn_prefill_chunked(
             h, 0, 1, 64, 64, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1.0,
             1 | B.PREFILL_ONE_KERNEL | B.PREFILL_TWO_KERNEL, fake, 0, None, None, fake, 1 << 30,

@@ -190,6 +190,69 @@ def test_prefill_one_kernel_extreme_decay():
     check(case, pool, out, ref, o_ref)
 
 
+KDA_ONE_CASES = [
+    ("fp32 ragged warm/cold, scale", dict(seed=31, H=3, D=128, lens=[1, 63, 64, 65, 130, 200],
+                                          warm=[1, 0, 1, 1, 0, 1], scale=0.5)),
+    ("bf16 snapshots, unaligned start", dict(seed=32, H=4, D=128, lens=[300, 70, 2, 129],
+                                             bf16=True, snap=64, start=[64, 37, 126, 0],
+                                             warm=[1, 1, 1, 0])),
+    ("fp32 silu + q and k norms", dict(seed=33, H=5, D=128, lens=[190, 64, 17], flags=7)),
+    ("bf16 no norms", dict(seed=34, H=2, D=128, lens=[150, 90], bf16=True, flags=0)),
+    ("empty and bad slots", dict(seed=35, H=2, D=128, lens=[0, 40, 0, 33, 5],
+                                 slots=[3, 0, 4, 5, 20], warm=[1, 1, 0, 1, 1], N=20)),
+    ("snapshots every 128 across several chunks", dict(seed=36, H=2, D=128, lens=[640, 333],
+                                                       snap=128, start=[0, 192], warm=[0, 1])),
+]
+
+
+@pytest.mark.parametrize("name,kw", KDA_ONE_CASES, ids=[c[0] for c in KDA_ONE_CASES])
+def test_prefill_kda_one_kernel_parity(name, kw):
+    """Decay per channel at head dim 128 on the one-kernel path against the oracle."""
+    print(f"prefill KDA parity (one-kernel): {name}", flush=True)
+    case = Case(path=ONE, amode=1, **kw)
+    pool, out = case.run_gpu()
+    ref, o_ref, e = case.run_oracle()
+    check(case, pool, out, ref, o_ref)
+    assert int(pool.err_word.item()) == e
+
+
+def test_prefill_kda_one_kernel_extreme_decay():
+    """Decays per channel that leave the range of the decay-factor planes: chunks in
+    which a channel decays below 2^-96 are run token by token.  Channels at 1e-3
+    everywhere in the first request (every chunk token by token), a head at 1e-20
+    and exact zeros in the second, and one channel at 0.3 over tokens 64..127 of the
+    third (2^-111 in its second chunk only, the other chunks on the planes)."""
+    print("prefill KDA one-kernel extreme decay", flush=True)
+    case = Case(seed=37, H=3, D=128, lens=[150, 64, 260], amode=1, path=ONE, warm=[1, 0, 1])
+    a = case.inp["alpha"]
+    a[:150, :, :16] = 1e-3
+    a[150 + 20:150 + 50, 1, :] = 1e-20
+    a[150 + 5:150 + 9, 2, 7] = 0.0
+    a[214 + 64:214 + 128, 0, 100] = 0.3
+    pool, out = case.run_gpu()
+    ref, o_ref, e = case.run_oracle()
+    check(case, pool, out, ref, o_ref)
+
+
+def test_prefill_kda_one_kernel_choice_and_agreement():
+    """A batch of many KDA requests (8 x 16 = 128 units) takes the one-kernel path by
+    default: bit for bit the forced one-kernel run, and within the tolerance of the
+    two-kernel path."""
+    print("prefill KDA path choice", flush=True)
+    kw = dict(seed=38, H=16, D=128, lens=[64, 100, 37, 200, 1, 64, 129, 90], amode=1,
+              snap=64, warm=[1, 0, 1, 1, 0, 1, 1, 1])
+    d_pool, d_out = Case(**kw).run_gpu()
+    o_pool, o_out = Case(path=ONE, **kw).run_gpu()
+    t_pool, t_out = Case(path=TWO, **kw).run_gpu()
+    assert torch.equal(d_out, o_out) and torch.equal(d_pool.ssm, o_pool.ssm)
+    assert torch.equal(d_pool.conv, t_pool.conv)
+    T, H, D = d_out.shape
+    a = widen(bf16_np(o_out)).reshape(T, H, D).transpose(1, 0, 2)
+    b = widen(bf16_np(t_out)).reshape(T, H, D).transpose(1, 0, 2)
+    assert worst_unit_rel_l2(a, b, 1) <= REL_L2_TOL
+    assert worst_unit_rel_l2(device_ssm_values(o_pool.ssm)[0], device_ssm_values(t_pool.ssm)[0], 2) <= REL_L2_TOL
+
+
 def test_prefill_one_kernel_default_choice_and_agreement():
     """A batch of many GDN requests takes the one-kernel path by default; its
     result equals the forced one-kernel run bit for bit and agrees with the

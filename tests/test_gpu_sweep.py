@@ -91,6 +91,43 @@ def test_prefill_one_kernel_random_cases(i):
     check(case, pool, out, ref, o_ref, o_exact=o_exact)
 
 
+@pytest.mark.parametrize("i", range(24))
+def test_prefill_kda_one_kernel_random_cases(i):
+    """The one-kernel path with a decay per channel on random batches: warm and cold
+    starts at arbitrary positions, fp32 or bf16 pool, norm and SiLU flags, snapshot
+    modes; in a third of the cases some channels of one request decay hard enough
+    (a = 0.2 .. 0.35 over a stretch) that chunks run token by token."""
+    r = np.random.default_rng(92000 + i)
+    H = int(r.integers(1, 5))
+    B = int(r.integers(1, 7))
+    lens = [int(v) for v in r.choice(ONE_KERNEL_LENGTHS, size=B)]
+    bf16 = bool(r.integers(0, 2))
+    flags = int(r.choice([0, 1, 3, 5, 7]))
+    snap = int(r.choice([0, 64, 128]))
+    warm = [int(v) for v in r.integers(0, 2, size=B)]
+    start = [int(v) for v in r.integers(0, 400, size=B)]
+    path = ONE | (32 if r.integers(0, 3) == 0 else 0)  # GDN_F_SNAP_LAST_ONLY
+    hard = r.integers(0, 3) == 0
+    print(f"KDA one-kernel sweep {i}: H={H} lens={lens} bf16={bf16} flags={flags} snap={snap} "
+          f"warm={warm} start={start} path={path} hard={hard}", flush=True)
+    case = Case(seed=93000 + i, H=H, D=128, lens=lens, bf16=bf16, amode=1, warm=warm, start=start,
+                flags=flags, scale=0.75, snap=snap, path=path)
+    if hard:
+        b = int(r.integers(0, B))
+        s0 = int(case.cu[b])
+        n = lens[b]
+        t0 = int(r.integers(0, n))
+        t1 = min(n, t0 + int(r.integers(1, 160)))
+        chans = r.choice(128, size=int(r.integers(1, 9)), replace=False)
+        hh = int(r.integers(0, H))
+        case.inp["alpha"][s0 + t0:s0 + t1, hh, chans] = float(r.uniform(0.2, 0.35))
+    pool, out = case.run_gpu()
+    assert int(pool.err_word.item()) == 0
+    ref, o_ref, e, o_exact = case.run_oracle(exact=True)
+    assert e == 0
+    check(case, pool, out, ref, o_ref, o_exact=o_exact)
+
+
 @pytest.mark.parametrize("i", range(12))
 def test_decode_random_cases(i):
     r = np.random.default_rng(7000 + i)
