@@ -767,6 +767,10 @@ __device__ __forceinline__ float row_prefix_prod(float v) {
   v *= row_shr_or_one<8>(v);
   return v;
 }
+// the value of the lane one down in its row of 16 (lane 0 takes lane 15's): DPP row_ror:1
+__device__ __forceinline__ uint32_t row_ror1(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x121, 0xF, 0xF, false));
+}
 // sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the gfx950 row swaps)
 __device__ __forceinline__ float cross_row_sum(float v) {
   const int lane = threadIdx.x & 63;
@@ -830,12 +834,6 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
 
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(a.x) + int64_t(rg.bos) * C, 0, rg.len * int(C) * 2, 0x00020000);
-  // 4 channels (from ch) of the input row at request position q; positions -3..-1
-  // from the slot's conv rows on a warm start
-  auto row_vec8 = [&](int q, int ch) -> u32x2 {
-    if (q < 0 && q >= -3 && warm) return *reinterpret_cast<const u32x2 *>(conv_live + (3 + q) * C + ch);
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xres, (q * int(C) + ch) * 2, 0, 0));
-  };
   auto row_vec = [&](int q, int ch) -> u32x4 {
     if (q < 0 && q >= -3 && warm) return *reinterpret_cast<const u32x4 *>(conv_live + (3 + q) * C + ch);
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, (q * int(C) + ch) * 2, 0, 0));
@@ -896,11 +894,14 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
     }
   };
 
-  // Global inputs of a chunk, loaded one chunk ahead: 7 rows of q and of k for the
-  // thread's conv item (4 channels each), the item's decays (4 tokens x 4 channels),
-  // 3 staged v pieces, and b (wave 0, one token per lane).  Positions outside the
-  // request read zero through the resources' ranges.
-  u32x2 xq[7], xk[7];
+  // Global inputs of a chunk, loaded one chunk ahead: 3 staged v pieces, the rows of
+  // the item's 4 tokens (4 channels of q and of k), the item's decays (4 tokens x 4
+  // channels) and b (wave 0, one token per lane), in the order phase 1 uses them.
+  // The conv's 3 earlier rows are the rows of the lane one token group down (a DPP
+  // row rotate); the first group's lanes load theirs into hq / hk (the other lanes
+  // address past the range, which reads zero and moves no data).  Positions
+  // outside the request read zero through the resources' ranges.
+  u32x2 xq[4], xk[4], hq[3], hk[3];
   f32x4 al[4];
   u32x4 sv[3];
   float bv;
@@ -911,16 +912,6 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
   auto load_chunk = [&](int t, int p0) {
     const int tq = t & 15, c0 = 16 * w + 4 * ((t & 63) >> 4);
     const int rs = int(C) * 2;
-    const int xo = ((p0 + 4 * tq - 3) * int(C) + h * D + c0) * 2, ko = xo + H * D * 2;
-#pragma unroll
-    for (int i = 0; i < 7; ++i) {
-      xq[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xres, xo + i * rs, 0, 0));
-      xk[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xres, ko + i * rs, 0, 0));
-    }
-    const int ao = ((p0 + 4 * tq) * H + h) * D * 4 + c0 * 4;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      al[rr] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ares, ao + rr * H * D * 4, 0, 0));
     const int vo = ((p0 - 3 + (t >> 4)) * int(C) + 2 * H * D + h * D + 8 * (t & 15)) * 2;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
@@ -931,6 +922,22 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
         sv[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
       }
     }
+    const int xo = ((p0 + 4 * tq) * int(C) + h * D + c0) * 2, ko = xo + H * D * 2;
+    const int ho = tq == 0 ? xo - 3 * rs : 0x7ffffff0, hko = tq == 0 ? ko - 3 * rs : 0x7ffffff0;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      hq[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xres, ho + i * rs, 0, 0));
+      hk[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xres, hko + i * rs, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xq[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xres, xo + i * rs, 0, 0));
+      xk[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xres, ko + i * rs, 0, 0));
+    }
+    const int ao = ((p0 + 4 * tq) * H + h) * D * 4 + c0 * 4;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      al[rr] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ares, ao + rr * H * D * 4, 0, 0));
     if (w == 0)
       bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bres, (p0 + (t & 63)) * H * 4, 0, 0));
   };
@@ -953,7 +960,48 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
     const int tq = lane & 15, cg = lane >> 4, c0 = 16 * w + 4 * cg;
 
     // the item's conv outputs (after SiLU, before the norms)
-    auto conv_items = [&](float (&yq)[4][4], float (&yk)[4][4]) {
+    // (PATCH: the first chunks of a warm start, whose rows at positions -3..-1 are the
+    // slot's conv rows: loaded into fresh registers and selected, since reloading the
+    // prefetched ones under a branch makes the compiler wait for every load in flight;
+    // the other chunks take a copy of this code without the selects)
+    auto conv_items = [&](float (&yq)[4][4], float (&yk)[4][4], auto patch_c) {
+      constexpr bool PATCH = decltype(patch_c)::value;
+      u32x2 pq[7], pkk[7];
+      if constexpr (PATCH) {
+#pragma unroll
+        for (int i = 0; i < 7; ++i) {  // rows 4tq - 3 + i
+          const int pos = i < 3 ? p0 - 3 + i : p0 + 4 * tq + i - 3;
+          pq[i] = pkk[i] = u32x2{0u, 0u};
+          if (pos >= -3 && pos < 0) {
+            pq[i] = *reinterpret_cast<const u32x2 *>(conv_live + (3 + pos) * C + h * D + c0);
+            pkk[i] = *reinterpret_cast<const u32x2 *>(conv_live + (3 + pos) * C + H * D + h * D + c0);
+          }
+        }
+        // (vmcnt 0 here, where only the first chunks pass: left pending, these loads
+        // would make the compiler wait for every load in flight on the common path)
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+      }
+      auto use = [&](int i, int pos, const u32x2 &v, const u32x2 *pv) {
+        return (PATCH && pos >= -3 && pos < 0) ? pv[i] : v;
+      };
+      // rows 4tq-3 .. 4tq+3: three from the lane one token group down (or loaded, in
+      // the first group), then its own
+      u32x2 rq[7], rk[7];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rq[3 + i] = use(3 + i, p0 + 4 * tq + i, xq[i], pq);
+        rk[3 + i] = use(3 + i, p0 + 4 * tq + i, xk[i], pkk);
+      }
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const u32x2 fq = use(i, p0 - 3 + i, hq[i], pq), fk = use(i, p0 - 3 + i, hk[i], pkk);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t nq = row_ror1(rq[4 + i][e]), nk = row_ror1(rk[4 + i][e]);
+          rq[i][e] = tq == 0 ? fq[e] : nq;
+          rk[i][e] = tq == 0 ? fk[e] : nk;
+        }
+      }
       u32x4 wq[2], wk[2];  // taps of the item's channels, two channels per vector
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -964,10 +1012,10 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
       for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float accq = dot2_bf16(wq[e >> 1][2 * (e & 1)], halves(xq[rr][e >> 1], xq[rr + 1][e >> 1], e & 1), 0.f);
-          accq = dot2_bf16(wq[e >> 1][2 * (e & 1) + 1], halves(xq[rr + 2][e >> 1], xq[rr + 3][e >> 1], e & 1), accq);
-          float acck = dot2_bf16(wk[e >> 1][2 * (e & 1)], halves(xk[rr][e >> 1], xk[rr + 1][e >> 1], e & 1), 0.f);
-          acck = dot2_bf16(wk[e >> 1][2 * (e & 1) + 1], halves(xk[rr + 2][e >> 1], xk[rr + 3][e >> 1], e & 1), acck);
+          float accq = dot2_bf16(wq[e >> 1][2 * (e & 1)], halves(rq[rr][e >> 1], rq[rr + 1][e >> 1], e & 1), 0.f);
+          accq = dot2_bf16(wq[e >> 1][2 * (e & 1) + 1], halves(rq[rr + 2][e >> 1], rq[rr + 3][e >> 1], e & 1), accq);
+          float acck = dot2_bf16(wk[e >> 1][2 * (e & 1)], halves(rk[rr][e >> 1], rk[rr + 1][e >> 1], e & 1), 0.f);
+          acck = dot2_bf16(wk[e >> 1][2 * (e & 1) + 1], halves(rk[rr + 2][e >> 1], rk[rr + 3][e >> 1], e & 1), acck);
           if (silu) {
             accq = accq / (1.f + __expf(-accq));
             acck = acck / (1.f + __expf(-acck));
@@ -985,30 +1033,28 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
     };
 
     // ================= P1: conv, planes, staged v rows, decays, norm sums =======
-    if (p0 < 3 && warm) {
-#pragma unroll
-      for (int i = 0; i < 7; ++i) {
-        xq[i] = row_vec8(p0 + 4 * tq - 3 + i, h * D + c0);
-        xk[i] = row_vec8(p0 + 4 * tq - 3 + i, H * D + h * D + c0);
-      }
-#pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        const int it = min(tid_c + u * kFThreads, 67 * 16 - 1);
-        sv[u] = row_vec(p0 - 3 + (it >> 4), 2 * H * D + h * D + 8 * (it & 15));
-      }
-    }
-    if (w == 0) {
-      const int dpos = p0 + lane;
-      LB[lane] = (dpos >= 0 && dpos < rg.len) ? bv : 0.f;
-    }
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const int it = tid_c + u * kFThreads;
       if (it < 67 * 16) *reinterpret_cast<u32x4 *>(lds + xv_off_at(kAXV, it >> 4, 16 * (it & 15))) = sv[u];
     }
+    // On a warm start, the staged pieces at positions -3..-1 are the slot's conv rows:
+    // each thread overwrites the pieces it has just written (LDS writes of one thread
+    // land in order).  Fresh registers, consumed here: reloading the prefetched ones
+    // under a branch would make the compiler wait for every load in flight.
+    if (p0 < 3 && warm) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int it = tid_c + u * kFThreads, pos = p0 - 3 + (it >> 4);
+        if (it < 67 * 16 && pos >= -3 && pos < 0)
+          *reinterpret_cast<u32x4 *>(lds + xv_off_at(kAXV, it >> 4, 16 * (it & 15))) =
+              *reinterpret_cast<const u32x4 *>(conv_live + (3 + pos) * C + 2 * H * D + h * D + 8 * (it & 15));
+      }
+    }
     {
       float yq[4][4], yk[4][4];
-      conv_items(yq, yk);
+      if (p0 < 3 && warm) conv_items(yq, yk, std::true_type());
+        else conv_items(yq, yk, std::false_type());
       // squared norms over this wave's 16 channels, per token, to the partial sums
       {
         float s[8];
@@ -1070,6 +1116,10 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
         put_item(kAQ, rr, qv);
       }
     }
+    if (w == 0) {  // b, the last load of the chunk
+      const int dpos = p0 + lane;
+      LB[lane] = (dpos >= 0 && dpos < rg.len) ? bv : 0.f;
+    }
     lds_barrier();
     // the norms (wave 0, one token per lane) and the chunk's path
     if (w == 0) {
@@ -1091,10 +1141,34 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
     }
     lds_barrier();
     const int by_token = __builtin_amdgcn_readfirstlane(LF[8]);
+    if (by_token) {
+      // A chunk run token by token: the planes again without the decay factors (k
+      // into P, q into Q'), and the decays themselves, fp32 [t][c], in R's place.
+      {
+        float yq[4][4], yk[4][4];
+        if (p0 < 3 && warm) conv_items(yq, yk, std::true_type());
+        else conv_items(yq, yk, std::false_type());
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          put_item(kAP, rr, yk[rr]);
+          put_item(kAQ, rr, yq[rr]);
+          const int pos = p0 + 4 * tq + rr;
+          const bool valid = pos >= 0 && pos < rg.len;
+          f32x4 av = al[rr];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[e] = valid ? av[e] : 1.f;
+          *reinterpret_cast<f32x4 *>(lds + kAR + ((4 * tq + rr) * D + c0) * 4) = av;
+        }
+      }
+    }
 
+    // ================= P2 =======================================================
+    // The next chunk's inputs are issued in two halves (waves 0-3 here, 4-7 at the
+    // start of P3), at the same two points on both paths: a third call site would
+    // keep the loop's registers from coalescing and cost a wait for every load in
+    // flight at the end of each chunk.
+    if (w < 4) load_chunk(tid_c, p0 + 64);
     if (!by_token) {
-      // ================= P2 =====================================================
-      if (w < 4) load_chunk(tid_c, p0 + 64);
       // a transposed M tile (lane holds M[16m+r][16k+4g+j]): causal mask and norms
       auto put_m = [&](int m, int k, const f32x4 &cc) {
         const int t = 16 * m + r;
@@ -1243,67 +1317,9 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
       }
       lds_barrier();
 
-      // ================= P3: Dl, O, state update ================================
-      if (w >= 4) load_chunk(tid_c, p0 + 64);
-      f32x4 Dl[4];
-      {
-        Split4 db[3];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          f32x4 acc = Y[m];
-#pragma unroll
-          for (int k = 0; k < m; ++k) acc = mfma3k16(split4_get(lds, kANF + nf_idx(m, k) * 1024, lane), db[k], acc);
-          Dl[m] = mfma3k16(split4_get(lds, kADF + m * 1024, lane), split4s(acc), f32x4{0.f, 0.f, 0.f, 0.f});
-          if (m < 3) db[m] = split4s(Dl[m]);
-        }
-      }
-      Split dop[2], dgop[2];
-      dop[0] = split44(Dl[0], Dl[1]);
-      dop[1] = split44(Dl[2], Dl[3]);
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Dl[tb][j] *= LB[kLbIk + 16 * tb + 4 * g + j];  // Dl / |k|
-      dgop[0] = split44(Dl[0], Dl[1]);
-      dgop[1] = split44(Dl[2], Dl[3]);
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        f32x4 o = OQ[tb];
-#pragma unroll
-        for (int ks = 0; ks <= (tb >> 1); ++ks) o = mfma3(frag_lds(lds, kAM, pair_idx(tb, ks), lane), dop[ks], o);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<uint16_t *>(lds + kAOS + (16 * tb + 4 * g + j) * kOP + 2 * vcol) = f32_to_bf16(a.scale * o[j]);
-      }
-      // S^T = Diag(g_63) (S0^T + R^T Diag(1/|k|) Dl)
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) S[kb] = mfma3(kt_frag_at(lds, kAR, slot_fn, kb, ks, lane), dgop[ks], S[kb]);
-        S[kb] *= *reinterpret_cast<const f32x4 *>(LB + kLbG + 16 * kb + 4 * g);
-      }
     } else {
-      // ================= the chunk token by token ===============================
-      // The planes again without the decay factors (k into P, q into Q'), and the
-      // decays themselves, fp32 [t][c], in R's place.
-      {
-        float yq[4][4], yk[4][4];
-        conv_items(yq, yk);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          put_item(kAP, rr, yk[rr]);
-          put_item(kAQ, rr, yq[rr]);
-          const int pos = p0 + 4 * tq + rr;
-          const bool valid = pos >= 0 && pos < rg.len;
-          f32x4 av = al[rr];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) av[e] = valid ? av[e] : 1.f;
-          *reinterpret_cast<f32x4 *>(lds + kAR + ((4 * tq + rr) * D + c0) * 4) = av;
-        }
-      }
       if (c > 0) flush_out(tid_c, p0 - 64);
       lds_barrier();
-      load_chunk(tid_c, p0 + 64);
       const int xv0 = 2 * vcol;
 #pragma unroll 1
       for (int t = 0; t < 64; ++t) {
@@ -1361,6 +1377,48 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
         if (g == 0)
           *reinterpret_cast<uint16_t *>(lds + kAOS + t * kOP + 2 * vcol) =
               f32_to_bf16(a.scale * qi * (sq + dk * kq));
+      }
+    }
+
+    // ================= P3: Dl, O, state update ==================================
+    if (w >= 4) load_chunk(tid_c, p0 + 64);
+    if (!by_token) {
+      f32x4 Dl[4];
+      {
+        Split4 db[3];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f32x4 acc = Y[m];
+#pragma unroll
+          for (int k = 0; k < m; ++k) acc = mfma3k16(split4_get(lds, kANF + nf_idx(m, k) * 1024, lane), db[k], acc);
+          Dl[m] = mfma3k16(split4_get(lds, kADF + m * 1024, lane), split4s(acc), f32x4{0.f, 0.f, 0.f, 0.f});
+          if (m < 3) db[m] = split4s(Dl[m]);
+        }
+      }
+      Split dop[2], dgop[2];
+      dop[0] = split44(Dl[0], Dl[1]);
+      dop[1] = split44(Dl[2], Dl[3]);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Dl[tb][j] *= LB[kLbIk + 16 * tb + 4 * g + j];  // Dl / |k|
+      dgop[0] = split44(Dl[0], Dl[1]);
+      dgop[1] = split44(Dl[2], Dl[3]);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f32x4 o = OQ[tb];
+#pragma unroll
+        for (int ks = 0; ks <= (tb >> 1); ++ks) o = mfma3(frag_lds(lds, kAM, pair_idx(tb, ks), lane), dop[ks], o);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint16_t *>(lds + kAOS + (16 * tb + 4 * g + j) * kOP + 2 * vcol) = f32_to_bf16(a.scale * o[j]);
+      }
+      // S^T = Diag(g_63) (S0^T + R^T Diag(1/|k|) Dl)
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) S[kb] = mfma3(kt_frag_at(lds, kAR, slot_fn, kb, ks, lane), dgop[ks], S[kb]);
+        S[kb] *= *reinterpret_cast<const f32x4 *>(LB + kLbG + 16 * kb + 4 * g);
       }
     }
 
