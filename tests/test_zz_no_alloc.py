@@ -35,7 +35,7 @@ def _inputs(seed, H, D, lens, amode, bf16, N):
                 warm=warm, start=start, nxt=nxt, lens=lens, H=H, D=D, amode=amode)
 
 
-def _run(c, noalloc, snap):
+def _run(c, noalloc, snap, flags=1):
     import gated_delta_rule_slot_amd as gdn
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     pool = gdn.state_pool_create(c["ssm"].cuda(), c["conv"].cuda(), err)
@@ -45,7 +45,7 @@ def _run(c, noalloc, snap):
             c["w"].cuda(), c["inp"]["alpha"].cuda(), c["amode"], c["inp"]["beta"].cuda(), out,
             max(c["lens"]))
     kw = dict(start_len=c["start"].cuda(), snap_interval=snap, track_slots=c["track"].cuda(),
-              next_track_idx=c["nxt"].cuda())
+              next_track_idx=c["nxt"].cuda(), flags=flags)
     if noalloc:
         gdn.conv_gdn_prefill_chunked_noalloc(*args, **kw)
     else:
@@ -102,7 +102,9 @@ def test_noalloc_prefill_matches_workspace_entry_on_two_calls():
         print(f"  bit-identical to the workspace entry; oracle worst unit rel-L2 out {eo:.2e} "
               f"state {es:.2e}", flush=True)
         assert eo <= REL_L2_TOL and es <= REL_L2_TOL
-    # a two-kernel batch beyond the scratch is refused before any launch
+    # a two-kernel batch beyond the scratch is refused before any launch (the batch
+    # would take the one-kernel path by default, which needs no scratch; the path is
+    # forced)
     c = _inputs(74, 12, 128, [64] * 400, 1, True, 1300)
     with pytest.raises(gdn.GdnError, match="scratch"):
-        _run(c, True, 0)
+        _run(c, True, 0, flags=1 | gdn.PREFILL_TWO_KERNEL)
