@@ -399,6 +399,87 @@ def test_prefill_full_kda_workload():
     check(case, pool, out, ref, o_ref)
 
 
+def test_prefill_kda_batch_launch():
+    """The KDA prefill shape for a batch, in the launch configuration the benchmark
+    times: 64 cold requests x 6144 tokens, 12 heads, K=V=128, per-channel decay, bf16
+    pool, every 64-token boundary stored to the requests' track slots, the library's
+    default path (768 units: one kernel).  Inputs are drawn on the device.  Three
+    requests (first, middle, last) against the oracle: outputs, live states, both
+    track slots and conv rows.  Every (request, head) unit against the two-kernel
+    path on the same inputs: outputs and live states within the tolerance."""
+    import gated_delta_rule_slot_amd as gdn
+    print("prefill parity: KDA batch launch", flush=True)
+    cfg = wl.KDA_PREFILL
+    H, D, B, Tr = cfg.heads, cfg.head_k, 64, 6144
+    C, T, N = 3 * H * D, B * Tr, 3 * B + 1
+    dev = torch.device("cuda")
+    gd = torch.Generator(device=dev)
+    gd.manual_seed(cfg.seed + 7)
+    x = torch.randn(T, C, generator=gd, device=dev).to(torch.bfloat16)
+    k = x[:, H * D:2 * H * D].view(T, H, D).float()         # keys L2-normalised per head
+    x[:, H * D:2 * H * D] = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16).view(T, H * D)
+    del k
+    alpha = torch.sigmoid(torch.randn(T, H, D, generator=gd, device=dev) + 3.0)
+    beta = torch.sigmoid(torch.randn(T, H, generator=gd, device=dev))
+    w = wl.conv_weights(wl.generator(cfg.seed + 7), C).to(dev)
+    g = wl.generator(cfg.seed + 8)
+    ssm0 = (0.25 * torch.randn(1, N, H, D, D, generator=g)).to(torch.bfloat16)
+    conv0 = torch.randn(1, N, 3, C, generator=g).to(torch.bfloat16)
+    cu = wl.cu_seqlens([Tr] * B)
+    slots = torch.arange(1, B + 1, dtype=torch.int32)
+    track = torch.arange(B + 1, 3 * B + 1, dtype=torch.int32).reshape(B, 2).contiguous()
+    nxt = torch.randint(0, 2, (B,), generator=g, dtype=torch.int32)
+    zeros = torch.zeros(B, dtype=torch.int32)
+
+    def run(flags, workspace=None):
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        pool = gdn.state_pool_create(ssm0.to(dev), conv0.to(dev), err)
+        out = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+        gdn.conv_gdn_prefill_chunked(pool, 0, cu.to(dev), slots.to(dev), zeros.to(dev), x, w, alpha,
+                                     cfg.alpha_mode, beta, out, Tr, start_len=zeros.to(dev),
+                                     flags=flags, snap_interval=64, track_slots=track.to(dev),
+                                     next_track_idx=nxt.to(dev), workspace=workspace)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        return pool, out
+
+    pool, out = run(gdn.L2NORM_K)
+    ws = torch.empty(min(gdn.gdn_prefill_workspace_bytes(pool, B, Tr), 8 << 30), dtype=torch.uint8,
+                     device=dev)
+    pool2, out2 = run(gdn.L2NORM_K | gdn.PREFILL_TWO_KERNEL, ws)
+    del ws
+    # every unit against the two-kernel path (on the device, in fp32)
+    a, b = out.float().view(B, Tr, H, D), out2.float().view(B, Tr, H, D)
+    rel = ((a - b).square().sum(dim=(1, 3)) / b.square().sum(dim=(1, 3))).sqrt()
+    sa = pool.ssm[0, 1:B + 1].float()
+    sb = pool2.ssm[0, 1:B + 1].float()
+    rels = ((sa - sb).square().sum(dim=(2, 3)) / sb.square().sum(dim=(2, 3))).sqrt()
+    print(f"  one kernel against two kernels, all {B * H} units: out {rel.max().item():.2e}  "
+          f"state {rels.max().item():.2e}", flush=True)
+    assert rel.max().item() <= REL_L2_TOL and rels.max().item() <= REL_L2_TOL
+    del a, b, out2, pool2
+    # three requests against the oracle
+    pick = [0, B // 2, B - 1]
+    idx = torch.cat([torch.arange(int(cu[i]), int(cu[i + 1])) for i in pick]).to(dev)
+    ref = pool_to_oracle(ssm0, conv0)
+    o_ref, e = oracle.prefill(
+        ref, 0, wl.cu_seqlens([Tr] * 3).numpy(), slots[pick].numpy(), wl.bf16_bits(x[idx].cpu()),
+        wl.bf16_bits(w.cpu()), alpha[idx].cpu().numpy(), cfg.alpha_mode, beta[idx].cpu().numpy(),
+        has_initial_state=np.zeros(3, np.int32), start_len=np.zeros(3, np.int32), snap_interval=64,
+        track_slots=track[pick].numpy(), next_track_idx=nxt[pick].numpy())
+    assert e == 0
+    got = widen(bf16_np(out[idx])).reshape(-1, H, D)
+    want = widen(o_ref).reshape(-1, H, D)
+    eo = max(worst_unit_rel_l2(got[i * Tr:(i + 1) * Tr].transpose(1, 0, 2),
+                               want[i * Tr:(i + 1) * Tr].transpose(1, 0, 2), 1) for i in range(3))
+    sp = [int(slots[i]) for i in pick] + [int(t) for i in pick for t in track[i]]
+    es = worst_unit_rel_l2(device_ssm_values(pool.ssm)[0, sp], ssm_values(ref)[0, sp], 2)
+    print(f"  requests {pick} against the oracle: worst unit rel-L2 out {eo:.2e}  state {es:.2e} "
+          f"(live and track slots)", flush=True)
+    assert eo <= REL_L2_TOL and es <= REL_L2_TOL
+    assert np.array_equal(bf16_np(pool.conv[0, sp]), ref.conv()[0, sp])
+
+
 def test_prefill_single_pass_matches_scratch_windows():
     """The full KDA workload shape (12 heads, one request, snapshots every 64) in one
     pass over a full workspace equals, bit for bit, the no-alloc entry point, whose
