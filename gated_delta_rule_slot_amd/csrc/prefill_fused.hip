@@ -1,5 +1,7 @@
-// prefill_fused.hip -- chunked prefill in one kernel, for a decay shared by all
-// channels of a head (the GDN form), head dim 128.
+// prefill_fused.hip -- chunked prefill in one kernel per (request, head), head dim
+// 128: prefill_fused_kernel for a decay shared by all channels of a head (the GDN
+// form, described here), prefill_fused_kda_kernel for a decay per channel (the KDA
+// form, described where it starts below).
 //
 // The recurrence (page "企业官网建设流程全解析", Kimi K3 notes, section
 // "Speculative decoding")
