@@ -238,10 +238,20 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
         // taps (0, 1) and (2, 3) multiply positions (pos - 3, pos - 2) and (pos - 1, pos)
         float acc = dot2_bf16(wr[e >> 1][2 * (e & 1)], tok_pair(xr[r], xr[r + 1], e), 0.f);
         acc = dot2_bf16(wr[e >> 1][2 * (e & 1) + 1], tok_pair(xr[r + 2], xr[r + 3], e), acc);
-        if (silu) acc = acc / (1.f + __expf(-acc));
         y[r][e] = valid ? acc : 0.f;
       }
-      if (norm) {  // wave-uniform: the G lanes of a token set share the sum
+    }
+    // SiLU in one branch after the loops (silu(0) = 0 keeps the masked values): a
+    // flag tested inside the unrolled loops costs a branch per conv output
+    if (silu) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[r][e] = y[r][e] / (1.f + __expf(-y[r][e]));
+    }
+    if (norm) {  // wave-uniform: the G lanes of a token set share the sum
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = fmaf(y[r][e], y[r][e], ss);

@@ -191,7 +191,9 @@ struct FArgs {
   int slots, heads;
 };
 
-template <typename TS>
+// SILU is a template parameter: a flag tested inside the unrolled conv loops costs a
+// branch (and register copies at its merge) per conv output.
+template <typename TS, bool SILU>
 __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
   constexpr int D = kFD;
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
     return;
   }
 
-  const bool silu = (a.flags & GDN_F_CONV_SILU) != 0;
+  constexpr bool silu = SILU;
 
   // ---- constants of the call --------------------------------------------------
   // conv item (P1) of waves 0-3: q, of waves 4-7: k
@@ -484,7 +486,12 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
           if (silu) acc = acc / (1.f + __expf(-acc));
           y[rr][e] = acc;
         }
-        if (inorm) {  // wave-uniform; the 16 lanes of a token quad share the sum
+      }
+      // (the norm's flag in one branch: tested inside the unrolled loop it costs a
+      // branch per token)
+      if (inorm) {  // wave-uniform; the 16 lanes of a token quad share the sum
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
           float ss = 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) ss = fmaf(y[rr][e], y[rr][e], ss);
@@ -783,7 +790,7 @@ __device__ __forceinline__ float cross_row_sum(float v) {
   return v;
 }
 
-template <typename TS>
+template <typename TS, bool SILU>
 __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) {
   constexpr int D = kFD;
   __shared__ __attribute__((aligned(16))) char lds[kALdsBytes];
@@ -859,7 +866,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
     return;
   }
 
-  const bool silu = (a.flags & GDN_F_CONV_SILU) != 0;
+  constexpr bool silu = SILU;
   const bool nq = (a.flags & GDN_F_L2NORM_Q) != 0, nk = (a.flags & GDN_F_L2NORM_K) != 0;
   const int vcol = 16 * w + r;
   const u32x2 vw = *reinterpret_cast<const u32x2 *>(a.conv_w + (2 * int64_t(H) * D + int64_t(h) * D + vcol) * 4);
@@ -1466,14 +1473,17 @@ hipError_t launch_prefill_fused(const gdn_pool *p, const PrefillArgs &a, hipStre
   if (p->d.head_k != kFD || p->d.head_v != kFD) return hipErrorInvalidValue;
   FArgs fa{a, p->d.ssm_base, static_cast<uint16_t *>(p->d.conv_base), p->d.err_word, p->d.slots, p->d.heads};
   const dim3 grid(unsigned(a.batch) * p->d.heads), block(kFThreads);
-  const bool bf16 = p->d.ssm_dtype == GDN_BF16;
+  const bool bf16 = p->d.ssm_dtype == GDN_BF16, silu = (a.flags & GDN_F_CONV_SILU) != 0;
   if (a.alpha_mode == GDN_ALPHA_PER_CHANNEL) {
-    if (bf16) hipLaunchKernelGGL(prefill_fused_kda_kernel<uint16_t>, grid, block, 0, s, fa);
-    else hipLaunchKernelGGL(prefill_fused_kda_kernel<float>, grid, block, 0, s, fa);
-  } else if (bf16) {
-    hipLaunchKernelGGL(prefill_fused_kernel<uint16_t>, grid, block, 0, s, fa);
+    if (bf16 && silu) hipLaunchKernelGGL((prefill_fused_kda_kernel<uint16_t, true>), grid, block, 0, s, fa);
+    else if (bf16) hipLaunchKernelGGL((prefill_fused_kda_kernel<uint16_t, false>), grid, block, 0, s, fa);
+    else if (silu) hipLaunchKernelGGL((prefill_fused_kda_kernel<float, true>), grid, block, 0, s, fa);
+    else hipLaunchKernelGGL((prefill_fused_kda_kernel<float, false>), grid, block, 0, s, fa);
   } else {
-    hipLaunchKernelGGL(prefill_fused_kernel<float>, grid, block, 0, s, fa);
+    if (bf16 && silu) hipLaunchKernelGGL((prefill_fused_kernel<uint16_t, true>), grid, block, 0, s, fa);
+    else if (bf16) hipLaunchKernelGGL((prefill_fused_kernel<uint16_t, false>), grid, block, 0, s, fa);
+    else if (silu) hipLaunchKernelGGL((prefill_fused_kernel<float, true>), grid, block, 0, s, fa);
+    else hipLaunchKernelGGL((prefill_fused_kernel<float, false>), grid, block, 0, s, fa);
   }
   return hipGetLastError();
 }
