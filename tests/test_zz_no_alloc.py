@@ -2,7 +2,8 @@
 
 conv_gdn_prefill_chunked_noalloc runs the same kernels as conv_gdn_prefill_chunked
 in the library's fixed per-device scratch (the two-kernel path in windows of as
-many chunks as the scratch holds; the one-kernel path needs no scratch).  Windows
+many chunks as the scratch holds; the one-kernel paths, for a decay per head and per
+channel, need no scratch).  Windows
 leave the result bit-identical, so each call is compared bit for bit with the
 workspace entry point on an identical pool (outputs, every slot's state and conv
 rows), and with the oracle to the stated tolerance.  Two calls run in a row, the
@@ -87,10 +88,12 @@ def test_noalloc_prefill_matches_workspace_entry_on_two_calls():
     # scratch holds 12 chunks of records per window, so the call runs in 4 windows
     # call 2: a smaller input on the same scratch, 1 request of 300 tokens
     # call 3: a GDN batch of 128 units on the one-kernel path (no scratch)
+    # call 4: a KDA batch of 132 units on the one-kernel path (no scratch)
     calls = [
         ("two-kernel, windows", _inputs(71, 12, 128, [3000, 1700, 64], 1, True, 16), 64),
         ("two-kernel, smaller", _inputs(72, 12, 128, [300], 1, True, 8), 64),
         ("one-kernel", _inputs(73, 4, 128, [200] * 32, 0, False, 100), 128),
+        ("one-kernel, KDA", _inputs(75, 12, 128, [150, 64, 1, 200, 90, 65, 130, 7, 64, 300, 40], 1, True, 40), 64),
     ]
     for name, c, snap in calls:
         print(f"no-alloc prefill: {name}", flush=True)
