@@ -84,10 +84,14 @@ __device__ __forceinline__ int xv_off(int row, int byte) {
 __device__ __forceinline__ int pair_idx(int tb, int ks) { return tb < 2 ? tb : 2 * tb - 2 + ks; }
 
 // Operand lane l of a K or Q fragment idx (= tb * 4 + ks) is stored in slot
-// l ^ (idx & 3).  The writers fill several fragments at once with lanes that
-// would otherwise share banks; the XOR spreads them, and a reader's 8-lane groups
-// still cover 8 distinct 16-byte slots.
-__device__ __forceinline__ int kn_slot(int idx, int l) { return l ^ (idx & 3); }
+// l ^ (idx & 3) ^ 8((l >> 5) & 1).  The writers fill several fragments at once with
+// lanes that would otherwise share banks, and the XOR by idx spreads them.  The
+// XOR of bit 3 by bit 5 serves the transposing reads of the state update: a
+// 16-lane group of such a read addresses 4 tokens in each of 4 channel octets,
+// slots 16 apart, which without it fall on the same banks (measured on gfx950
+// with in-bounds probes: 64 -> 45 cycles per read instruction and wave with 8
+// waves reading; the 16-byte operand reads and the writers are no slower).
+__device__ __forceinline__ int kn_slot(int idx, int l) { return l ^ (idx & 3) ^ (8 * ((l >> 5) & 1)); }
 __device__ __forceinline__ int nf_idx(int m, int k) { return m * (m - 1) / 2 + k; }  // m > k
 
 __device__ __forceinline__ void split4_put(char *lds, int off, int lane, const f32x4 &v) {
@@ -754,10 +758,16 @@ static_assert(8 * 64 * 2 * 4 <= 4 * 16 * kBP * 4, "norm partial sums fit the dia
 constexpr int kLbIq = 64, kLbIk = 128, kLbG = 192, kLbFlag = 320;  // float offsets in the kALB block
 constexpr float kPlaneFloor = 0x1p-96f;  // smallest g_63 the planes take
 
-// Lane-slot permutation of the fragments here: the writers of phase 1 fill four
-// fragments at once with lanes 16 apart; the XOR gives every lane of a fragment
-// its own bank group.
-__device__ __forceinline__ int ka_slot(int, int l) { return l ^ ((l >> 4) & 3); }
+// Lane-slot permutation of the fragments here.  The 16 lanes of a channel group
+// write 4 tokens into each of the 4 token-block fragments (tb = idx >> 2) at once,
+// and those fragments lie a multiple of the bank span apart: the XOR by tb gives
+// each of them its own bank positions (measured on gfx950 with in-bounds probes:
+// 512 -> 128 cycles per 8-byte write pair and wave with 8 waves writing).  The XOR
+// of bit 3 by bit 5 serves the transposing reads of the state update, as in the
+// kernel for a decay per head.
+__device__ __forceinline__ int ka_slot(int idx, int l) {
+  return l ^ (idx & 3) ^ (idx >> 2) ^ (8 * ((l >> 5) & 1));
+}
 
 __device__ __forceinline__ int xv_off_at(int base, int row, int byte) {
   return base + row * 256 + ((((byte >> 4) ^ (2 * ((row >> 2) & 3))) << 4) | (byte & 15));
@@ -1336,11 +1346,11 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
         const float *arow = reinterpret_cast<const float *>(lds + kAR) + t * D + 4 * g;
         // this lane's 32 channels of k and q: slots 0-3 are channels 32ks + 4g + j,
         // slots 4-7 channels 32ks + 16 + 4g + j, of fragment (t >> 4, ks)
-        const int fl = ka_slot(0, (t & 15) + 16 * g) * 16;
+        const int fl = (t & 15) + 16 * g;  // this lane's fragment lane
         float u = 0.f, sq = 0.f, kq = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int fo = 2 * ((t >> 4) * 4 + ks) * 1024 + fl;
+          const int fi = (t >> 4) * 4 + ks, fo = 2 * fi * 1024 + ka_slot(fi, fl) * 16;
           const u32x4 kh = *reinterpret_cast<const u32x4 *>(lds + kAP + fo);
           const u32x4 kl = *reinterpret_cast<const u32x4 *>(lds + kAP + fo + 1024);
           const u32x4 qh = *reinterpret_cast<const u32x4 *>(lds + kAQ + fo);
@@ -1373,7 +1383,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
         const float dk = bt * (vt - ki * u) * ki;  // d_t / |k_t|
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int fo = 2 * ((t >> 4) * 4 + ks) * 1024 + fl;
+          const int fi = (t >> 4) * 4 + ks, fo = 2 * fi * 1024 + ka_slot(fi, fl) * 16;
           const u32x4 kh = *reinterpret_cast<const u32x4 *>(lds + kAP + fo);
           const u32x4 kl = *reinterpret_cast<const u32x4 *>(lds + kAP + fo + 1024);
 #pragma unroll
