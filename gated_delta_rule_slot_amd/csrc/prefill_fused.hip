@@ -123,9 +123,11 @@ __device__ __forceinline__ s16x4t lds_read_tr16(const char *lds, int off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4t *)(const_cast<char *>(lds) + off));
 }
-// (base: the fragment region; SLOT: its lane-slot permutation)
+// (base: the fragment region; SLOT: its lane-slot permutation; tb_pad: bytes added to
+// the fragments of each later token block)
 template <typename SLOT>
-__device__ __forceinline__ Split kt_frag_at(const char *lds, int base, SLOT slot, int cb, int ks, int lane) {
+__device__ __forceinline__ Split kt_frag_at(const char *lds, int base, SLOT slot, int cb, int ks, int lane,
+                                            int tb_pad = 0) {
   const int g = lane >> 4, a = lane & 3, k = (lane >> 2) & 3;
   const int kc = cb >> 1, e0 = 4 * (cb & 1);  // channel group of K, first slot of the half
   s16x4t h[2], l[2];
@@ -133,7 +135,7 @@ __device__ __forceinline__ Split kt_frag_at(const char *lds, int base, SLOT slot
   for (int half = 0; half < 2; ++half) {
     const int t = 32 * ks + 16 * half + 4 * g + k;
     const int idx = (t >> 4) * 4 + kc;
-    const int off = base + 2 * idx * 1024 + slot(idx, (t & 15) + 16 * a) * 16 + 2 * e0;
+    const int off = base + 2 * idx * 1024 + tb_pad * (idx >> 2) + slot(idx, (t & 15) + 16 * a) * 16 + 2 * e0;
     h[half] = lds_read_tr16(lds, off);
     l[half] = lds_read_tr16(lds, off + 1024);
   }
@@ -741,10 +743,15 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
 // the 16 lanes of a row: the decay products are scanned across the row with DPP.
 // A chunk in which some channel decays below 2^-96 is run token by token instead,
 // which is exact for any decay down to a = 0.
-constexpr int kAP = 0;                         // P  [tb 4][ks 4][plane 2]
-constexpr int kAQ = kAP + 32 * 1024;           // Q'
-constexpr int kAR = kAQ + 32 * 1024;           // R (a chunk run token by token: a, fp32 [64][128])
-constexpr int kAM = kAR + 32 * 1024;           // M  [pair 6][plane 2]
+// A plane's fragments [tb 4][ks 4][plane 2] of 1 KB; the fragments of token block tb
+// start 16 tb bytes later (kTbPad), so that the phase-1 writers, whose 16 lanes of a
+// channel group write into all four token blocks at once, reach different banks.
+constexpr int kTbPad = 16;
+constexpr int kAPlane = 32 * 1024 + 3 * kTbPad;
+constexpr int kAP = 0;                         // P
+constexpr int kAQ = kAP + kAPlane;             // Q'
+constexpr int kAR = kAQ + kAPlane;             // R (a chunk run token by token: a, fp32 [64][128])
+constexpr int kAM = kAR + kAPlane;             // M  [pair 6][plane 2]
 constexpr int kANF = kAM + 12 * 1024;          // -N_mk
 constexpr int kADF = kANF + 6 * 1024;          // D_m
 constexpr int kALD = kADF + 4 * 1024;          // diagonal blocks; in phase 1 the norm partial sums [8][64][2]
@@ -758,15 +765,17 @@ static_assert(8 * 64 * 2 * 4 <= 4 * 16 * kBP * 4, "norm partial sums fit the dia
 constexpr int kLbIq = 64, kLbIk = 128, kLbG = 192, kLbFlag = 320;  // float offsets in the kALB block
 constexpr float kPlaneFloor = 0x1p-96f;  // smallest g_63 the planes take
 
-// Lane-slot permutation of the fragments here.  The 16 lanes of a channel group
-// write 4 tokens into each of the 4 token-block fragments (tb = idx >> 2) at once,
-// and those fragments lie a multiple of the bank span apart: the XOR by tb gives
-// each of them its own bank positions (measured on gfx950 with in-bounds probes:
-// 512 -> 128 cycles per 8-byte write pair and wave with 8 waves writing).  The XOR
-// of bit 3 by bit 5 serves the transposing reads of the state update, as in the
-// kernel for a decay per head.
-__device__ __forceinline__ int ka_slot(int idx, int l) {
-  return l ^ (idx & 3) ^ (idx >> 2) ^ (8 * ((l >> 5) & 1));
+// Lane-slot permutation of the plane fragments: as for the decay per head (the XOR by
+// idx & 3 spreads writers; bit 3 XORed by bit 5 serves the transposing reads).  With
+// the token-block offset kTbPad, the 16 lanes of a channel group, which write 4 tokens
+// into each of the 4 token blocks at once, land on distinct bank pairs but for
+// pairs (measured on gfx950 with in-bounds probes: 512 -> 128 cycles per 8-byte write
+// pair and wave with 8 waves writing), and every read still adds a constant per
+// token block, which folds into the instruction's offset.
+__device__ __forceinline__ int ka_slot(int idx, int l) { return l ^ (idx & 3) ^ (8 * ((l >> 5) & 1)); }
+__device__ __forceinline__ int ka_frag(int idx) { return kTbPad * (idx >> 2); }  // token-block offset
+__device__ __forceinline__ Split ka_frag_lds(const char *lds, int plane, int idx, int lane) {
+  return frag_lds(lds, plane + ka_frag(idx), idx, ka_slot(idx, lane));
 }
 
 __device__ __forceinline__ int xv_off_at(int base, int row, int byte) {
@@ -1048,7 +1057,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
     // (t & 15) + 16 cg, slot e + 4 (w & 1) of fragment (t >> 4, w >> 1)
     auto put_item = [&](int off, int rr, const float *v) {
       const int t = 4 * tq + rr, idx = (t >> 4) * 4 + (w >> 1);
-      frag_put4(lds, off, idx, ka_slot(idx, (t & 15) + 16 * cg), 4 * (w & 1), v);
+      frag_put4(lds, off + ka_frag(idx), idx, ka_slot(idx, (t & 15) + 16 * cg), 4 * (w & 1), v);
     };
 
     // ================= P1: conv, planes, staged v rows, decays, norm sums =======
@@ -1211,7 +1220,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const int idx = m * 4 + ks;
-          c2[ks & 1] = mfma3(frag_lds(lds, kAP, idx, ka_slot(idx, lane)), frag_lds(lds, kAR, idx, ka_slot(idx, lane)),
+          c2[ks & 1] = mfma3(ka_frag_lds(lds, kAP, idx, lane), ka_frag_lds(lds, kAR, idx, lane),
                              c2[ks & 1]);
         }
         const f32x4 cc = c2[0] + c2[1];
@@ -1243,7 +1252,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const int idx = m * 4 + ks;
-          cm[ks & 1] = mfma3(frag_lds(lds, kAR, idx, ka_slot(idx, lane)), frag_lds(lds, kAQ, idx, ka_slot(idx, lane)),
+          cm[ks & 1] = mfma3(ka_frag_lds(lds, kAR, idx, lane), ka_frag_lds(lds, kAQ, idx, lane),
                              cm[ks & 1]);
         }
         put_m(m, m, cm[0] + cm[1]);
@@ -1267,8 +1276,8 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
               const int e = tile_entry(q);
               const int m = (e >> 2) & 3, k = e & 3;
               const int ia = k * 4 + ks, ib = m * 4 + ks;
-              cc[q] = mfma3(frag_lds(lds, kAR, ia, ka_slot(ia, lane)),
-                            frag_lds(lds, (e >> 4) ? kAP : kAQ, ib, ka_slot(ib, lane)), cc[q]);
+              cc[q] = mfma3(ka_frag_lds(lds, kAR, ia, lane),
+                            ka_frag_lds(lds, (e >> 4) ? kAP : kAQ, ib, lane), cc[q]);
             }
           }
 #pragma unroll
@@ -1298,15 +1307,15 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
           XQ[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         Split kf[2], qf[2], sop;
-        kf[0] = frag_lds(lds, kAP, 0, ka_slot(0, lane));
-        qf[0] = frag_lds(lds, kAQ, 0, ka_slot(0, lane));
+        kf[0] = ka_frag_lds(lds, kAP, 0, lane);
+        qf[0] = ka_frag_lds(lds, kAQ, 0, lane);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int ks = i >> 2, tb = i & 3;
           if (i + 1 < 16) {
             const int n = ((i + 1) & 3) * 4 + ((i + 1) >> 2);
-            kf[(i + 1) & 1] = frag_lds(lds, kAP, n, ka_slot(n, lane));
-            qf[(i + 1) & 1] = frag_lds(lds, kAQ, n, ka_slot(n, lane));
+            kf[(i + 1) & 1] = ka_frag_lds(lds, kAP, n, lane);
+            qf[(i + 1) & 1] = ka_frag_lds(lds, kAQ, n, lane);
           }
           if (tb == 0) sop = split44(S[2 * ks], S[2 * ks + 1]);
           X1[tb] = mfma3(kf[i & 1], sop, X1[tb]);
@@ -1350,7 +1359,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
         float u = 0.f, sq = 0.f, kq = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int fi = (t >> 4) * 4 + ks, fo = 2 * fi * 1024 + ka_slot(fi, fl) * 16;
+          const int fi = (t >> 4) * 4 + ks, fo = 2 * fi * 1024 + ka_frag(fi) + ka_slot(fi, fl) * 16;
           const u32x4 kh = *reinterpret_cast<const u32x4 *>(lds + kAP + fo);
           const u32x4 kl = *reinterpret_cast<const u32x4 *>(lds + kAP + fo + 1024);
           const u32x4 qh = *reinterpret_cast<const u32x4 *>(lds + kAQ + fo);
@@ -1383,7 +1392,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
         const float dk = bt * (vt - ki * u) * ki;  // d_t / |k_t|
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const int fi = (t >> 4) * 4 + ks, fo = 2 * fi * 1024 + ka_slot(fi, fl) * 16;
+          const int fi = (t >> 4) * 4 + ks, fo = 2 * fi * 1024 + ka_frag(fi) + ka_slot(fi, fl) * 16;
           const u32x4 kh = *reinterpret_cast<const u32x4 *>(lds + kAP + fo);
           const u32x4 kl = *reinterpret_cast<const u32x4 *>(lds + kAP + fo + 1024);
 #pragma unroll
@@ -1436,7 +1445,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kda_kernel(FArgs fa) 
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) S[kb] = mfma3(kt_frag_at(lds, kAR, slot_fn, kb, ks, lane), dgop[ks], S[kb]);
+        for (int ks = 0; ks < 2; ++ks) S[kb] = mfma3(kt_frag_at(lds, kAR, slot_fn, kb, ks, lane, kTbPad), dgop[ks], S[kb]);
         S[kb] *= *reinterpret_cast<const f32x4 *>(LB + kLbG + 16 * kb + 4 * g);
       }
     }
