@@ -768,10 +768,10 @@ constexpr float kPlaneFloor = 0x1p-96f;  // smallest g_63 the planes take
 // Lane-slot permutation of the plane fragments: as for the decay per head (the XOR by
 // idx & 3 spreads writers; bit 3 XORed by bit 5 serves the transposing reads).  With
 // the token-block offset kTbPad, the 16 lanes of a channel group, which write 4 tokens
-// into each of the 4 token blocks at once, land on distinct bank pairs but for
-// pairs (measured on gfx950 with in-bounds probes: 512 -> 128 cycles per 8-byte write
-// pair and wave with 8 waves writing), and every read still adds a constant per
-// token block, which folds into the instruction's offset.
+// into each of the 4 token blocks at once, put two lanes on a bank pair instead of
+// eight (measured on gfx950 with in-bounds probes: 512 -> 128 cycles per 8-byte
+// write pair and wave with 8 waves writing), and every read still adds a constant
+// per token block, which folds into the instruction's offset.
 __device__ __forceinline__ int ka_slot(int idx, int l) { return l ^ (idx & 3) ^ (8 * ((l >> 5) & 1)); }
 __device__ __forceinline__ int ka_frag(int idx) { return kTbPad * (idx >> 2); }  // token-block offset
 __device__ __forceinline__ Split ka_frag_lds(const char *lds, int plane, int idx, int lane) {
