@@ -440,7 +440,7 @@ GDN_API gdn_status gdn_accept_scatter(gdn_pool_t pool, int32_t layer, int32_t ba
 }
 
 namespace {
-gdn_status check_ring(gdn_pool_t pool, const gdn_replay_ring *r) {
+gdn_status check_ring(gdn_pool_t, const gdn_replay_ring *r) {
   if (!r) return fail(GDN_ERR_ARG, "ring is NULL");
   if (r->positions < 1 || r->positions > GDN_MAX_RING_POSITIONS)
     return fail(GDN_ERR_RANGE, "ring positions %d outside [1, %d]", r->positions, GDN_MAX_RING_POSITIONS);

@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
 
     // Y = Diag(b) (V - Diag(g) K S0^T) and Diag(g) Q S0^T for this wave's rows;
     // V comes from the staged raw rows
-    auto ks0_products = [&](int p0) {
+    auto ks0_products = [&]() {
       f32x4 X1[4], XQ[4];
   #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
@@ -640,7 +640,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_fused_kernel(FArgs fa) {
     // the previous chunk's outputs (the staged rows are rewritten only in phase 3):
     // here the stores meet no load issue on the vector-memory path
     if (c > 0) flush_out(tid_c, p0 - 64, std::integral_constant<int, kFThreads>());
-    ks0_products(p0);  // every wave, two per SIMD
+    ks0_products();  // every wave, two per SIMD
     lds_barrier();
 
     // ================= P3: Dl, O, state update ==================================

@@ -438,7 +438,7 @@ __global__ __launch_bounds__((MmaShape<D>::THREADS)) void replay_verify_mma_kern
     const TS *__restrict__ ssm, const uint16_t *__restrict__ conv, int32_t *err, int slots,
     int heads, ReplayArgs a) {
   using SH = MmaShape<D>;
-  constexpr int RBW = SH::RBW, KS = SH::KS, ROWS = SH::ROWS, CL = SH::CL, CPL = SH::CPL;
+  constexpr int RBW = SH::RBW, KS = SH::KS, ROWS = SH::ROWS;
   constexpr int NCOL = 2 * TMAX, NT = (NCOL + 15) / 16;  // columns: Gam.k of every token, then Gam.q
   constexpr int HALF = D / 2;                            // two-channel conv items per part (q, k, v)
   constexpr int ITEMS = 3 * HALF;
