@@ -227,3 +227,40 @@ def test_workspace_query():
         assert n.value > m.value > 0
     finally:
         B._lib.state_pool_destroy(h)
+
+
+def test_prefill_argument_checks_before_launch():
+    """Range, pointer, enum and alignment checks of conv_gdn_prefill_chunked, each
+    answered on the host with the status the header documents (nothing launches)."""
+    st, h = _create()
+    assert st == 0
+    fake, odd = ct.c_void_p(0x30000), ct.c_void_p(0x30008)  # 16-byte aligned / not
+
+    def call(**kw):
+        a = dict(layer=0, batch=1, total=64, maxlen=64, cu=fake, slots=fake, has=fake, start=fake,
+                 x=fake, w=fake, alpha=fake, amode=0, beta=fake, flags=1, out=fake, snap=0,
+                 track=None, nxt=None, ws=fake, wsb=1 << 30)
+        a.update(kw)
+        return B._lib.conv_gdn_prefill_chunked(
+            h, a["layer"], a["batch"], a["total"], a["maxlen"], a["cu"], a["slots"], a["has"],
+            a["start"], a["x"], a["w"], a["alpha"], a["amode"], a["beta"], 1.0, a["flags"], a["out"],
+            a["snap"], a["track"], a["nxt"], a["ws"], a["wsb"], None)
+
+    try:
+        assert call(batch=70000) == -2                 # batch outside [0, 65535]
+        assert call(total=-1) == -2                    # negative token count
+        assert call(batch=0, cu=None, x=None) == 0     # an empty batch launches nothing
+        assert call(cu=None) == -1                     # a required pointer is NULL
+        assert call(x=None) == -1                      # x is NULL with tokens to read
+        assert call(amode=7) == -1                     # unknown decay layout
+        assert call(w=odd) == -3                       # conv_w not 16-byte aligned
+        assert call(x=odd) == -3
+        assert call(out=odd) == -3
+        assert call(alpha=odd) == -3
+        assert "aligned" in B.last_error()
+        # the two-kernel path: a workspace that is not 256-byte aligned
+        assert call(ws=ct.c_void_p(0x30010)) == -3
+        assert "workspace" in B.last_error()
+        assert call(layer=5) == -2                     # layer outside the pool
+    finally:
+        B._lib.state_pool_destroy(h)
