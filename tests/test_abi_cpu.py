@@ -264,3 +264,30 @@ def test_prefill_argument_checks_before_launch():
         assert call(layer=5) == -2                     # layer outside the pool
     finally:
         B._lib.state_pool_destroy(h)
+
+
+def test_decode_argument_checks_before_launch():
+    """The decode entry's range, pointer, enum and alignment checks (nothing launches)."""
+    st, h = _create()
+    assert st == 0
+    fake, odd = ct.c_void_p(0x30000), ct.c_void_p(0x30008)
+
+    def call(**kw):
+        a = dict(batch=1, slots=fake, x=fake, w=fake, alpha=fake, amode=0, beta=fake, out=fake,
+                 ti=0)
+        a.update(kw)
+        return B._lib.gdn_decode_step(h, 0, a["batch"], a["slots"], a["x"], a["w"], a["alpha"],
+                                      a["amode"], a["beta"], 1.0, 1, a["out"], None, a["ti"], None,
+                                      None, None)
+
+    try:
+        assert call(batch=70000) == -2
+        assert call(batch=0, x=None) == 0
+        assert call(out=None) == -1
+        assert call(amode=7) == -1
+        assert call(ti=-1) == -1
+        assert call(w=odd) == -3
+        assert call(x=odd) == -3
+        assert call(alpha=odd) == -3
+    finally:
+        B._lib.state_pool_destroy(h)
