@@ -1081,12 +1081,14 @@ __global__ __launch_bounds__((128 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs
       }
     }
   };
-  auto load_m = [&](__amdgpu_buffer_rsrc_t r) {
+  // (KM: the k steps of M that hold nonzero tiles for this wave's token blocks)
+  auto load_m = [&](__amdgpu_buffer_rsrc_t r, auto km) {
+    constexpr int KM = decltype(km)::value;
 #pragma unroll
     for (int u = 0; u < TBW; ++u) {
       const int tb = tw + NW * u;
 #pragma unroll
-      for (int ksp = 0; ksp < 2; ++ksp) Mn[u][ksp] = frag_buf(r, voff, int(RC::MF) + (tb * 2 + ksp) * 2048);
+      for (int ksp = 0; ksp < KM; ++ksp) Mn[u][ksp] = frag_buf(r, voff, int(RC::MF) + (tb * 2 + ksp) * 2048);
     }
   };
   // the entry state's operand fragments (all channel slices) and Δ's (all tokens)
@@ -1196,6 +1198,10 @@ __global__ __launch_bounds__((128 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs
       if (warm) return *reinterpret_cast<const u32x4 *>(conv_live + int64_t(3 + q) * C + cp_ch);
       return u32x4{0u, 0u, 0u, 0u};
     };
+    // The tiles of M above the diagonal are zero: a wave whose only token block
+    // is 0 or 1 reads and multiplies its first k step of M alone.  The choice is made
+    // once, outside the chunk loop, so each loop has fixed loads.
+    auto run = [&](auto km) {
     int cdst;
     u32x4 cpiece;
     {
@@ -1204,7 +1210,7 @@ __global__ __launch_bounds__((128 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs
       __builtin_amdgcn_sched_barrier(0);
       cpiece = conv_fetch(ka.c0, cdst);
       __builtin_amdgcn_sched_barrier(0);
-      load_m(r0);
+      load_m(r0, km);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll 1
@@ -1241,7 +1247,7 @@ __global__ __launch_bounds__((128 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs
         const int tb = tw + NW * u;
         f32x4 o = Oq[u];
 #pragma unroll
-        for (int ksp = 0; ksp < 2; ++ksp) o = mfma3(Mn[u][ksp], Db[ksp], o);  // zero above the diagonal
+        for (int ksp = 0; ksp < decltype(km)::value; ++ksp) o = mfma3(Mn[u][ksp], Db[ksp], o);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int pos = 64 * c - rg.off + 16 * tb + 4 * g4 + j;
@@ -1249,7 +1255,7 @@ __global__ __launch_bounds__((128 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs
           __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(a.scale * o[j]), orsrc, offs, 0, 0);
         }
       }
-      load_m(rnext);
+      load_m(rnext, km);
 
       // conv rows of a snapshot at a boundary that ends this chunk
       if (cdst > 0 && cdst < ka.slots) {
@@ -1259,6 +1265,9 @@ __global__ __launch_bounds__((128 * Rec<D>::NKS)) void prefill_scan_kernel(KArgs
       cpiece = cpiece_next;
       cdst = cdst_next;
     }
+    };
+    if (TBW == 1 && tw < 2) run(std::integral_constant<int, 1>());
+    else run(std::integral_constant<int, 2>());
   }
 
   // ---- end of the window: live slot (request done) or the carry ----------------
