@@ -428,7 +428,8 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
         frag_store(rec + RC::QF, tb * NKS + ks, ln, sp);
       }
       // M fragments (tb 0 and 1, ks' 1) lie above the diagonal; the scan multiplies
-      // them anyway to keep its loop free of branches, so store zeros
+      // them where a wave holds several token blocks (head dims below 128), so store
+      // zeros
       for (int it = rel; it < 256; it += 384) {
         const int idx = (it >> 7) ? 3 : 1, plane = (it >> 6) & 1, ln = it & 63;
         *reinterpret_cast<u32x4 *>(rec + RC::MF + size_t(2 * idx + plane) * 1024 + ln * 16) = u32x4{0u, 0u, 0u, 0u};
@@ -744,7 +745,8 @@ __global__ __launch_bounds__(kPrepThreads) void prefill_prep_kernel(KArgs ka) {
       frag_store(rec + RC::KF, cb * 2 + ksp, ln, split8(v));
     }
     // M fragments (tb 0 and 1, ks' 1) lie above the diagonal; the scan multiplies
-    // them anyway to keep its loop free of branches, so store zeros
+    // them where a wave holds several token blocks (head dims below 128), so store
+    // zeros
     for (int it = rel; it < 256; it += 384) {
       const int idx = (it >> 7) ? 3 : 1, plane = (it >> 6) & 1, ln = it & 63;
       *reinterpret_cast<u32x4 *>(rec + RC::MF + size_t(2 * idx + plane) * 1024 + ln * 16) = u32x4{0u, 0u, 0u, 0u};
