@@ -269,6 +269,7 @@ def run_kda_batch_prefill(torch, gdn, wl, dev, reps=3, B=64, ws_cap=8 << 30):
                         "snapshot every 64, bf16 pool",
             "prefill_path": "one kernel (library default for 768 (request, head) units)",
             "tokens": T, "ms": t_one * 1e3, "tokens_per_s": T / t_one,
+            "snapshots_written": B * (Tr // 64), "snapshots_elided": 0,
             "hbm_frac": byts / t_one / 1e9 / HBM_PEAK_GBS,
             "mfma_util_vs_bf16_peak": flops / t_one / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "algorithmic_bytes": byts, "algorithmic_flops": flops,
