@@ -704,8 +704,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the hot path has no cross-GPU step and this build "
-              "runs on a single MI355X; rerun with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the hot path has no cross-GPU step (heads shard "
+              "with no exchange); rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

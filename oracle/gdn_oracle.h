@@ -82,7 +82,7 @@ typedef struct {
   int32_t restore_src_slot_id;
 } oracle_restore_op;
 
-/* Size of the arithmetic type this build uses: 4 or 8. */
+/* Size of the arithmetic type of this compiled variant of the oracle: 4 or 8. */
 int oracle_real_bytes(void);
 
 /* Threads the OpenMP loops use. */
